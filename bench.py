@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark one sparse decode step of the 128K batched-decode workload on one MI355X.
+
+A step is the whole hot path on one batch: append the current token (K, V and its
+projected scoring row), scoring prep, the full-context score scan, per-KV-head
+top-k, and gather-free attention with the split merge. Inputs are resident in HBM
+before timing starts. Each stage is bracketed by HIP events on the stream the
+kernels run on, so the scan kernel's own duration is measured in the timed region.
+
+Prints one JSON line. Default: --gpus 1 --steps 200 --warmup 20.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOAD = ("long-batched decode step: batch 16, 32 query / 8 KV heads (G=4), d=128, n=131072 cached tokens "
+            "per sequence, scoring rank r=32, budget k=4096; bf16 K/V with RoPE (base 500000) and 1% heavy "
+            "hitters (key x4), random orthonormal basis per KV head, 8 query sets cycled")
+PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_long_batched_pmc.json")
+SCAN_SOURCES = [os.path.join(ROOT, "token_level_sparse_kv_amd", "csrc", f) for f in ("score.hip", "sjsa_device.h")]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device-to-device copy of known size, for scaling rocprofv3 counters."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def traffic_from_profile(scan_bytes_per_launch):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
+    taken on the current scan kernel source; else None."""
+    try:
+        with open(PMC_FILE) as f:
+            p = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if p.get("source_sha256") != source_hash(SCAN_SOURCES):
+        return None
+    fetch = p["fetch_kib_per_launch"] * 1024.0 / p["copy_fetch_factor"]
+    write = p["write_kib_per_launch"] * 1024.0 / p["copy_write_factor"]
+    return fetch + write
+
+
+def cpu_baseline(host, units, k, scale, gpu_out, gpu_idx):
+    """The oracle, as it stands, on a sample of (sequence, KV head) units of the same
+    step, with a thread pool over units. Also checks the GPU results of those units."""
+    import numpy as np
+    from oracle import jssa
+    q, K, V, Kp, M, G = host["q"], host["K"], host["V"], host["Kp"], host["M"], host["G"]
+    n = K.shape[1]                      # K is [units, n, d]
+    workers = max(1, min(16, os.cpu_count() or 1))
+
+    def run(i):
+        b, h = units[i]
+        return jssa.decode_unit(q[b, h * G:(h + 1) * G], K[i], V[i], Kp[i], M[h], n, k, scale)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(run, range(len(units))))
+    dt = time.perf_counter() - t0
+    ok = True
+    worst = 0.0
+    for i, (b, h) in enumerate(units):
+        ref_out, ref_idx, s = res[i]
+        g = gpu_idx[i]
+        T = np.sort(s[ref_idx])[0]
+        diff = np.setxor1d(g, ref_idx)
+        ok &= bool(np.all(np.diff(g) > 0)) and bool(np.all(np.abs(s[diff] - T) <= 1e-3 * abs(T)))
+        mine = jssa.attend(q[b, h * G:(h + 1) * G], K[i], V[i], g, scale)
+        worst = max(worst, float(np.max(np.abs(gpu_out[i] - mine))))
+    return dt, workers, ok, worst
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-units", type=int, default=16, help="units sampled for the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this build measures the "
+              f"single-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(1 << 30, 5)
+        return
+
+    import numpy as np
+    import torch
+
+    import token_level_sparse_kv_amd as sj
+    import workloads
+    from token_level_sparse_kv_amd.perfmodel import MI355X_HBM_PEAK_GBS, step_bytes
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    wl = workloads.long_batched(device=dev, n_q_sets=8)
+    B, Hkv, G, d, r, n, k = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim, wl.rank, wl.capacity, wl.k
+    q_sets = wl.extra["q_sets"]
+    K, V, M, seq_len = wl.K, wl.V, wl.M, wl.seq_len
+    # projected scoring cache, built by the library's append over every cached token
+    Kp = torch.empty(B, Hkv, n, r, dtype=torch.bfloat16, device=dev)
+    T = 8192
+    for t0 in range(0, n, T):
+        pos = torch.full((B,), t0, dtype=torch.int32, device=dev)
+        sj.append_kv(K[:, :, t0:t0 + T].contiguous(), V[:, :, t0:t0 + T].contiguous(), M, pos, K, V, Kp)
+    k_new, v_new = workloads.new_token(wl, seed=99)
+    pos_new = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+    shape = sj.make_shape(B, Hkv, G, d, r, n)
+    ws = sj.alloc_workspace(shape, k, dev)
+    idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hkv * G, d, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    def step(i, ev=None):
+        q = q_sets[i % q_sets.shape[0]]
+        if ev is not None:
+            ev[0].record()
+        sj.append_kv(k_new, v_new, M, pos_new, K, V, Kp)
+        if ev is not None:
+            ev[1].record()
+        sj.prep(shape, q, M, ws)
+        if ev is not None:
+            ev[2].record()
+        sj.scan(shape, Kp, seq_len, ws)
+        if ev is not None:
+            ev[3].record()
+        sj.select(shape, seq_len, k, ws, idx=idx)
+        if ev is not None:
+            ev[4].record()
+        sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
+        if ev is not None:
+            ev[5].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    names = ["append", "prep", "scan", "select", "attend"]
+    stage_ms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, nm in enumerate(names)}
+    ms_per_step = total_ms / args.steps
+
+    tb = step_bytes(B, Hkv, G, d, r, n, k)
+    gbs = tb["total"] / (ms_per_step * 1e-3) / 1e9
+    scan_bytes = tb["scan_kproj"]
+    scan_gbs = scan_bytes / (stage_ms["scan"] * 1e-3) / 1e9
+    traffic = traffic_from_profile(scan_bytes)
+
+    line = {
+        "metric": "sparse decode steps/s + achieved HBM GB/s (% of peak) at 128K ctx",
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "n_q_heads": Hkv * G, "n_kv_heads": Hkv, "head_dim": d,
+                   "context": n, "rank": r, "k": k, "kproj_dtype": "bf16"},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / MI355X_HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": tb["total"],
+        "stage_us": {kk: round(v * 1000.0, 2) for kk, v in stage_ms.items()},
+        "roofline": {"kernel": "score scan (score_kernel<32,2>)", "bound": "hbm", "achieved": round(scan_gbs, 1),
+                     "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(scan_gbs / MI355X_HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic)},
+        "setup_s": round(t_setup, 2),
+    }
+
+    print(f"timed: {ms_per_step * 1000:.1f} us/step, stages (us) {line['stage_us']}", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(3)
+        all_units = [(b, h) for b in range(B) for h in range(Hkv)]
+        pick = sorted(rng.choice(len(all_units), size=min(args.cpu_units, len(all_units)), replace=False))
+        units = [all_units[i] for i in pick]
+        step(0)
+        torch.cuda.synchronize()
+        q0 = q_sets[0]
+
+        def bits(t):
+            return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+        host = {"q": bits(q0), "M": M.cpu().numpy(), "G": G,
+                "K": np.stack([bits(K[b, h]) for b, h in units]),
+                "V": np.stack([bits(V[b, h]) for b, h in units]),
+                "Kp": np.stack([bits(Kp[b, h]) for b, h in units])}
+        go = out.float().cpu().numpy()
+        gi = idx.cpu().numpy()
+        gpu_out = np.stack([go[b, h * G:(h + 1) * G] for b, h in units])
+        gpu_idx = np.stack([gi[b, h] for b, h in units])
+        dt, workers, ok, worst = cpu_baseline(host, units, k, 1.0 / np.sqrt(d), gpu_out, gpu_idx)
+        scale_up = len(all_units) / len(units)
+        line["cpu_baseline"] = {"value": round(1.0 / (dt * scale_up), 4), "unit": "steps/s", "cores": workers,
+                                "kind": "oracle",
+                                "sample": f"{len(units)} of {len(all_units)} (sequence, KV head) units of one "
+                                          f"step (scoring, top-k, exact attention), wall time scaled by "
+                                          f"{scale_up:g}; NumPy, thread pool over units"}
+        line["parity_sample"] = {"units": len(units), "idx_band_ok": bool(ok), "max_abs_out_err": worst}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * sjsa.h - C ABI of the MI355X (gfx950) JSSA sparse-decode library (libsjsa.so).
+ *
+ * One decode step of token-level top-k sparse attention for GQA, in the joint
+ * query-key subspace form of the JSSA article ("JSSA 完全拆解:联合 query-key
+ * 子空间打分与 gather-free 内核,训练无关的 token 级稀疏解码"). For every
+ * sequence b and KV head h:
+ *   q_bar = mean of the G query heads of KV head h        (section 打分误差的定义)
+ *   q_hat = M_h q_bar,  s_j = q_hat . Kproj[b,h,j]  for j < n_b
+ *   S     = the k positions with the largest s_j          (section JSSA 的整体结构)
+ *   out_g = softmax attention of query head g over S, reading the original bf16
+ *           K and V in place, with no gather              (section 原理详解(二))
+ * The G query heads of a KV head share its index set; each KV head has its own.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are row-major and contiguous. bf16 is passed as 16-bit patterns.
+ *       q      [B, H_q, d]        bf16, H_q = H_kv * G, query head hq -> KV head hq / G
+ *       K, V   [B, H_kv, cap, d]  bf16
+ *       Kproj  [B, H_kv, cap, r]  bf16 (projected scoring cache, K M^T)
+ *       M      [H_kv, r, d]       fp32, orthonormal rows (one basis per KV head)
+ *       seq_len[B]                int32: tokens valid in each sequence's cache
+ *       idx    [B, H_kv, k]       int32
+ *       out    [B, H_q, d]        bf16, or fp32 with SJSA_FLAG_OUT_F32
+ *   - Every tensor pointer is a DEVICE pointer except the sjsa_shape pointer,
+ *     which is host memory. The caller owns every buffer, including the
+ *     workspace; the library never allocates, frees or keeps device memory.
+ *   - d (head_dim) must be 128; r (rank) 16, 32 or 64; G (group) 1, 2, 4 or 8.
+ *   - All device pointers must be 16-byte aligned; the workspace 256-byte aligned.
+ *   - seq_len values are read on the device and clamped to [0, cap]; n_b below
+ *     means min(max(seq_len[b], 0), cap).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and runs asynchronously; no call synchronizes with the host.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns a negative status and enqueues nothing. A launch
+ *     failure reported by the HIP runtime returns SJSA_ERR_HIP.
+ *   - Calls that share a workspace must not overlap (use one stream or order
+ *     them); the library keeps no global mutable state.
+ *   - Results are deterministic: identical inputs give bit-identical outputs.
+ */
+#ifndef SJSA_H
+#define SJSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sjsa_status {
+  SJSA_OK = 0,
+  SJSA_ERR_NULL = -1,        /* a required pointer is NULL */
+  SJSA_ERR_DIMS = -2,        /* a size is out of range */
+  SJSA_ERR_UNSUPPORTED = -3, /* d, r, G or flags outside the supported set */
+  SJSA_ERR_K = -4,           /* k < 1 or above SJSA_MAX_K */
+  SJSA_ERR_WORKSPACE = -5,   /* workspace smaller than the size query returns */
+  SJSA_ERR_HIP = -6,         /* the HIP runtime reported a launch error */
+  SJSA_ERR_ALIGN = -7        /* a pointer is not aligned as required */
+} sjsa_status;
+
+/* Output dtype flag (sjsa_shape.flags): fp32 instead of bf16 for `out`. */
+#define SJSA_FLAG_OUT_F32 1
+/* Largest supported token budget per call. */
+#define SJSA_MAX_K (1 << 20)
+
+typedef struct sjsa_shape {
+  int32_t batch;      /* B >= 1 */
+  int32_t n_kv_heads; /* H_kv >= 1 */
+  int32_t group;      /* G: query heads per KV head (1, 2, 4, 8) */
+  int32_t head_dim;   /* d: must be 128 */
+  int32_t rank;       /* r: 16, 32 or 64 */
+  int32_t flags;      /* 0 or SJSA_FLAG_OUT_F32 */
+  int64_t capacity;   /* cap: token slots per (b, h) in K, V, Kproj; 1 .. 2^31-1 */
+} sjsa_shape;
+
+/*
+ * Append n_new tokens per (sequence, KV head) to the caches.
+ * Source: JSSA article, section 投影打分缓存与校准成本 (the auxiliary scoring
+ * cache Kproj = K M^T sits next to the original KV cache) and section 组件级拆解
+ * (projecting each new key is the pipeline's cheapest stage).
+ *   k_new, v_new [B, H_kv, n_new, d] bf16 (device)
+ *   M            [H_kv, r, d] fp32 (device)
+ *   pos          [B] int32 (device): first slot written for sequence b
+ * Writes K[b,h,pos_b+t] = k_new[b,h,t], V likewise, and
+ * Kproj[b,h,pos_b+t,i] = bf16_rne(sum_c M[h,i,c] * k_new[b,h,t,c]) (fp32 dot).
+ * Rows whose slot falls outside [0, cap) are skipped (nothing is written).
+ * Errors: SJSA_ERR_NULL, _DIMS (n_new < 1), _UNSUPPORTED, _ALIGN, _HIP.
+ */
+int sjsa_append_kv(const sjsa_shape* shape, const void* k_new, const void* v_new,
+                   int32_t n_new, const float* M, const int32_t* pos,
+                   void* K, void* V, void* Kproj, void* stream);
+
+/*
+ * Bytes of device workspace that sjsa_decode_step / the stage calls need for
+ * this shape and budget k. Returns 0 if the shape or k is invalid.
+ */
+size_t sjsa_decode_workspace_size(const sjsa_shape* shape, int32_t k);
+
+/*
+ * One sparse decode step: the whole pipeline of the JSSA article's section
+ * 组件级拆解 (scoring prep, candidate scoring, top-k selection, sparse
+ * attention) on one stream. Equivalent to sjsa_score, then sjsa_select, then
+ * sjsa_attend on the same workspace.
+ *   q [B, H_q, d] bf16; K, V [B, H_kv, cap, d] bf16; Kproj [B, H_kv, cap, r] bf16
+ *   M [H_kv, r, d] fp32; seq_len [B] int32; k >= 1 (token budget per KV head)
+ *   sm_scale: softmax scale of the final attention; 0 selects 1/sqrt(d)
+ *   out [B, H_q, d] (bf16, or fp32 with SJSA_FLAG_OUT_F32); idx [B, H_kv, k]
+ * idx[b,h] holds the min(k, n_b) selected positions in ascending order, then -1.
+ * Ranking: larger score first, equal scores by lower position, -0 == +0, NaN
+ * last. out is zero where n_b = 0.
+ * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _K, _WORKSPACE, _ALIGN, _HIP.
+ */
+int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, const void* V,
+                     const void* Kproj, const float* M, const int32_t* seq_len,
+                     int32_t k, float sm_scale, void* out, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 1+2 of the step: scoring prep (q_bar, q_hat; section 打分误差的定义)
+ * and the full-context score scan over Kproj (section 原理详解(二): scoring
+ * still scans every candidate). Leaves the fp32 scores and a first-digit
+ * histogram of them in the workspace. The score of (b, h, j) can be read back
+ * at float offset sjsa_workspace_scores_offset(shape)/4 + (b*H_kv + h)*stride + j,
+ * stride = sjsa_workspace_score_stride(shape). The workspace may be the one
+ * sized for decode, or at least sjsa_workspace_scores_offset + 4*B*H_kv*stride.
+ * Errors: as sjsa_decode_step.
+ */
+int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const float* M,
+               const int32_t* seq_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/* sjsa_score in two launches, for callers that time the stages separately:
+ * sjsa_prep (q_bar, q_hat; clears the unit's score histogram) then
+ * sjsa_scan (the score scan over Kproj). Same workspace rules as sjsa_score. */
+int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, void* workspace,
+              size_t workspace_bytes, void* stream);
+int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Stage 3: top-k of the scores sjsa_score left in the workspace -> idx [B, H_kv, k].
+ * Source: JSSA article, section JSSA 的整体结构 (per-KV-head top-k). */
+int sjsa_select(const sjsa_shape* shape, const int32_t* seq_len, int32_t k, int32_t* idx,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 4: gather-free indexed attention (JSSA article, section 原理详解(二):
+ * one launch per layer, per-KV-head index sets resolved inside the kernel, K and
+ * V read in place). idx [B, H_kv, k] may come from any source: entries < 0 or
+ * >= n_b are skipped, and duplicates count as often as they appear.
+ */
+int sjsa_attend(const sjsa_shape* shape, const void* q, const void* K, const void* V,
+                const int32_t* idx, int32_t k, const int32_t* seq_len, float sm_scale,
+                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Top-k of caller-provided fp32 scores: scores [B, H_kv, score_stride], the first
+ * n_b entries of each row valid; score_stride >= cap, a multiple of 4. Same
+ * ranking and output as sjsa_select. Uses the same workspace as decode.
+ */
+int sjsa_topk(const sjsa_shape* shape, const float* scores, int64_t score_stride,
+              const int32_t* seq_len, int32_t k, int32_t* idx,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace layout helpers for reading the scores back (host only). */
+size_t sjsa_workspace_scores_offset(const sjsa_shape* shape);
+int64_t sjsa_workspace_score_stride(const sjsa_shape* shape);
+
+/* Static message for a status code. */
+const char* sjsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SJSA_H */

@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI: every declared symbol is exported, the workspace
+layout is consistent, and invalid arguments are rejected before any launch.
+No call here reaches the GPU (every call fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_sparse_kv_amd as sj
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "sjsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sjsa_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert "sjsa_decode_step" in names and "sjsa_append_kv" in names
+    lib = ctypes.CDLL(sj.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _shape(**kw):
+    base = dict(batch=2, n_kv_heads=8, group=4, head_dim=128, rank=32, capacity=1000)
+    base.update(kw)
+    return sj.make_shape(base["batch"], base["n_kv_heads"], base["group"], base["head_dim"], base["rank"],
+                         base["capacity"])
+
+
+def test_workspace_size_and_layout():
+    L = sj.lib()
+    s = _shape()
+    ws = sj.workspace_size(s, 256)
+    off = L.sjsa_workspace_scores_offset(ctypes.byref(s))
+    stride = L.sjsa_workspace_score_stride(ctypes.byref(s))
+    assert stride >= 1000 and stride % 64 == 0
+    assert off % 256 == 0
+    assert ws >= off + 2 * 8 * stride * 4
+    assert ws % 256 == 0
+    # bigger budgets never need less workspace
+    assert sj.workspace_size(s, 4096) >= ws
+    # invalid shapes or k give 0
+    assert L.sjsa_decode_workspace_size(ctypes.byref(_shape(head_dim=64)), 256) == 0
+    assert L.sjsa_decode_workspace_size(ctypes.byref(s), 0) == 0
+    assert L.sjsa_decode_workspace_size(None, 16) == 0
+
+
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation
+
+
+def _step(shape, k=16, ws_bytes=1 << 30, ptrs=None, sm_scale=0.0):
+    L = sj.lib()
+    p = [ctypes.c_void_p(FAKE)] * 9 if ptrs is None else ptrs
+    return L.sjsa_decode_step(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], p[5], k, sm_scale, p[6], p[7],
+                              p[8], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), -3), (dict(rank=24), -3), (dict(group=3), -3), (dict(group=16), -3),
+    (dict(batch=0), -2), (dict(capacity=0), -2), (dict(capacity=1 << 31), -2),
+    (dict(batch=1000, n_kv_heads=100), -2),
+])
+def test_bad_shapes(kw, status):
+    assert _step(_shape(**kw)) == status
+
+
+def test_bad_k_null_workspace_alignment():
+    s = _shape()
+    assert _step(s, k=0) == -4
+    assert _step(s, k=(1 << 20) + 1) == -4
+    ptrs = [ctypes.c_void_p(FAKE)] * 9
+    ptrs[3] = None
+    assert _step(s, ptrs=ptrs) == -1
+    assert _step(s, ws_bytes=1024) == -5
+    ptrs = [ctypes.c_void_p(FAKE)] * 9
+    ptrs[0] = ctypes.c_void_p(FAKE + 2)
+    assert _step(s, ptrs=ptrs) == -7
+    ptrs = [ctypes.c_void_p(FAKE)] * 9
+    ptrs[8] = ctypes.c_void_p(FAKE + 64)            # workspace needs 256-byte alignment
+    assert _step(s, ptrs=ptrs) == -7
+    assert _step(s, sm_scale=float("nan")) == -2
+    L = sj.lib()
+    assert L.sjsa_decode_step(None, *([None] * 6), 16, 0.0, None, None, None, 0, None) == -1
+
+
+def test_stage_validation():
+    L = sj.lib()
+    s = _shape()
+    f = ctypes.c_void_p(FAKE)
+    assert L.sjsa_score(ctypes.byref(s), f, f, f, f, f, 16, None) == -5
+    assert L.sjsa_select(ctypes.byref(s), f, 0, f, f, 1 << 30, None) == -4
+    assert L.sjsa_topk(ctypes.byref(s), f, 999, f, 8, f, f, 1 << 30, None) == -2      # stride < cap
+    assert L.sjsa_topk(ctypes.byref(s), f, 1002, f, 8, f, f, 1 << 30, None) == -2     # stride % 4
+    assert L.sjsa_attend(ctypes.byref(s), f, f, f, f, 8, f, 0.0, f, f, 100, None) == -5
+    assert L.sjsa_append_kv(ctypes.byref(s), f, f, 0, f, f, f, f, f, None) == -2
+    assert L.sjsa_append_kv(ctypes.byref(s), f, None, 1, f, f, f, f, f, None) == -1
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, 5):
+        assert isinstance(L.sjsa_status_string(st), bytes)
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 128, dtype=torch.bfloat16)
+    K = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    M = torch.zeros(1, 16, 128)
+    with pytest.raises(ValueError):
+        sj.decode_step(q, K, K, torch.zeros(1, 1, 64, 16, dtype=torch.bfloat16), M,
+                       torch.zeros(1, dtype=torch.int32), 8)

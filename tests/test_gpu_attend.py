@@ -1,0 +1,81 @@
+"""GPU gather-free attention (sjsa_attend) against the oracle's exact attention over
+the same index sets: every group size, split counts from 1 to many, -1 padding,
+out-of-range and duplicate entries, bf16 and fp32 outputs."""
+import numpy as np
+import pytest
+import torch
+
+import token_level_sparse_kv_amd as sj
+import workloads
+from oracle import jssa
+from tests.gpu_helpers import OUT_TOL_BF16, OUT_TOL_F32, bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref(q, K, V, idx, seq_len, G, scale):
+    B, Hq, d = q.shape
+    H = K.shape[1]
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        n = min(max(int(seq_len[b]), 0), K.shape[2])
+        for h in range(H):
+            sel = idx[b, h]
+            sel = sel[(sel >= 0) & (sel < n)]
+            out[b, h * G:(h + 1) * G] = jssa.attend(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], sel, scale)
+    return out
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("k", [1, 63, 64, 65, 1000, 4096])
+def test_attend_matches_oracle(G, k):
+    say(f"attend G={G} k={k}")
+    B, H, n = 2, 2, 5000
+    wl = workloads.gaussian(B, H, G, 128, 16, n, k, seed=G * 1000 + k, device="cuda", seq_len=[n, 4321])
+    rng = np.random.default_rng(k)
+    idx = np.stack([np.stack([np.sort(rng.choice(n, size=min(k, n), replace=False)) for _ in range(H)])
+                    for _ in range(B)]).astype(np.int32)
+    idx_t = torch.from_numpy(idx).cuda()
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    scale = jssa.default_sm_scale(128)
+    ref = _ref(q, K, V, idx, wl.seq_len.cpu().numpy(), G, scale)
+    for out_f32, tol in ((True, OUT_TOL_F32), (False, OUT_TOL_BF16)):
+        out = sj.attend(wl.q, wl.K, wl.V, idx_t, wl.seq_len, out_f32=out_f32)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = np.max(np.abs(got - ref))
+        assert err <= tol, (out_f32, err)
+
+
+def test_attend_padding_duplicates_out_of_range_and_scale():
+    say("attend padding/duplicates")
+    B, H, G, n = 2, 1, 4, 300
+    wl = workloads.gaussian(B, H, G, 128, 16, n, 64, seed=9, device="cuda", seq_len=[300, 0])
+    idx = np.full((B, H, 200), -1, dtype=np.int32)
+    idx[0, 0, :50] = np.arange(0, 100, 2)
+    idx[0, 0, 50:60] = 10                     # duplicates count as often as they appear
+    idx[0, 0, 60:70] = 5000                   # beyond n: skipped
+    idx[1, 0, :20] = np.arange(20)            # sequence 1 is empty: everything skipped
+    idx_t = torch.from_numpy(idx).cuda()
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    for scale in (0.0, 0.37):
+        s = scale if scale else jssa.default_sm_scale(128)
+        ref = _ref(q, K, V, idx, [300, 0], G, s)
+        out = sj.attend(wl.q, wl.K, wl.V, idx_t, wl.seq_len, sm_scale=scale, out_f32=True)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.max(np.abs(got - ref)) <= OUT_TOL_F32
+        assert np.all(got[1] == 0)
+
+
+def test_single_selected_row_reproduces_v():
+    say("attend k=1 -> V row")
+    wl = workloads.gaussian(1, 2, 4, 128, 16, 100, 1, seed=10, device="cuda")
+    idx_t = torch.tensor([[[17], [93]]], dtype=torch.int32, device="cuda")
+    out = sj.attend(wl.q, wl.K, wl.V, idx_t, wl.seq_len)
+    torch.cuda.synchronize()
+    o = bits(out)
+    V = bits(wl.V)
+    for g in range(4):
+        assert np.array_equal(o[0, g], V[0, 0, 17])
+        assert np.array_equal(o[0, 4 + g], V[0, 1, 93])

@@ -1,0 +1,144 @@
+"""End-to-end GPU parity of sjsa_decode_step (and the stage calls) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import token_level_sparse_kv_amd as sj
+import workloads
+from oracle import calib, jssa
+from oracle.numerics import bf16_to_f32
+from tests import golden_toy
+from tests.gpu_helpers import (OUT_TOL_BF16, OUT_TOL_F32, bits, check_unit, from_bits, kproj_oracle, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(wl, kproj_bits, k, out_f32=True, tag=""):
+    Kp = from_bits(kproj_bits).cuda()
+    out, idx = sj.decode_step(wl.q, wl.K, wl.V, Kp, wl.M, wl.seq_len, k, out_f32=out_f32)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    ix = idx.cpu().numpy()
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    M = wl.M.cpu().numpy()
+    scale = jssa.default_sm_scale(128)
+    G = wl.group
+    tol = OUT_TOL_F32 if out_f32 else OUT_TOL_BF16
+    msgs = []
+    for b in range(wl.batch):
+        n = min(max(int(wl.seq_len[b]), 0), wl.capacity)
+        for h in range(wl.n_kv_heads):
+            msgs.append(check_unit(o[b, h * G:(h + 1) * G], ix[b, h], q, K, V, kproj_bits, M, b, h, G, n, k,
+                                   scale, tol, tag))
+    return o, ix, msgs
+
+
+def test_tiny_single_head_calibrated():
+    say("step tiny single head, calibrated basis")
+    wl = workloads.tiny_single_head()
+    M = calib.calibrate(wl.calib_q.numpy(), wl.calib_k.numpy(), wl.rank).astype(np.float32)
+    wl.M = torch.from_numpy(M)[None].contiguous()
+    wl = wl.to("cuda")
+    kp = kproj_oracle(bits(wl.K), M[None])
+    for out_f32 in (True, False):
+        _run_and_check(wl, kp, wl.k, out_f32=out_f32, tag="tiny")
+
+
+def test_llama8b_layer():
+    say("step llama8b-shaped layer n=32768 k=2048")
+    wl = workloads.llama8b_layer(device="cuda")
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    _run_and_check(wl, kp, wl.k, out_f32=False, tag="llama8b")
+
+
+@pytest.mark.parametrize("r,G", [(16, 1), (32, 2), (64, 4), (32, 8)])
+def test_ragged_batches(r, G):
+    say(f"step ragged r={r} G={G}")
+    seq = [7000, 1, 0, 4099, 6999]
+    wl = workloads.gaussian(5, 2, G, 128, r, 7000, 300, seed=r * 10 + G, device="cuda", seq_len=seq,
+                            capacity=7003)
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    for k in (300, 1, 7000):
+        _run_and_check(wl, kp, k, tag=f"ragged r{r} G{G} k{k}")
+
+
+def test_budget_at_least_context_is_dense():
+    say("step k >= n")
+    wl = workloads.gaussian(2, 2, 4, 128, 32, 900, 1000, seed=21, device="cuda", seq_len=[900, 333])
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    o, ix, _ = _run_and_check(wl, kp, 1000, tag="dense")
+    assert np.array_equal(ix[0, 0, :900], np.arange(900)) and np.all(ix[0, 0, 900:] == -1)
+    assert np.array_equal(ix[1, 1, :333], np.arange(333)) and np.all(ix[1, 1, 333:] == -1)
+
+
+def test_duplicated_kproj_rows_tie_to_lower_position():
+    say("step exact ties from duplicated rows")
+    wl = workloads.gaussian(1, 1, 4, 128, 32, 8192, 512, seed=22, device="cuda")
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    kp[0, 0, 4096:] = kp[0, 0, :4096]          # every projected row appears twice
+    o, ix, msgs = _run_and_check(wl, kp, 512, tag="dup")
+    # bit-equal scores on both sides: the sets must be identical (no band needed)
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    _, ref_idx, _ = jssa.decode_unit(q[0], K[0, 0], V[0, 0], kp[0, 0], wl.M.cpu().numpy()[0], 8192, 512,
+                                     jssa.default_sm_scale(128))
+    assert np.array_equal(ix[0, 0], ref_idx)
+
+
+def test_zero_query_all_scores_tie():
+    say("step zero query")
+    wl = workloads.gaussian(1, 2, 4, 128, 16, 3000, 100, seed=23, device="cuda")
+    wl.q.zero_()
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    o, ix, _ = _run_and_check(wl, kp, 100, tag="zero-q")
+    assert np.array_equal(ix[0, 0], np.arange(100))       # all scores are +-0: lowest positions
+
+
+def test_stage_calls_equal_fused_step_and_are_deterministic():
+    say("stages vs fused step, determinism")
+    wl = workloads.gaussian(3, 2, 4, 128, 32, 20000, 700, seed=24, device="cuda", seq_len=[20000, 15000, 9])
+    Kp = from_bits(kproj_oracle(bits(wl.K), wl.M.cpu().numpy())).cuda()
+    shape = sj.shape_of(wl.q, wl.K, wl.M)
+    ws = sj.alloc_workspace(shape, 700)
+    o1, i1 = sj.decode_step(wl.q, wl.K, wl.V, Kp, wl.M, wl.seq_len, 700, workspace=ws)
+    o2, i2 = sj.decode_step(wl.q, wl.K, wl.V, Kp, wl.M, wl.seq_len, 700, workspace=ws)
+    sc = sj.score(wl.q, Kp, wl.M, wl.seq_len, ws)
+    i3 = sj.select(shape, wl.seq_len, 700, ws)
+    o3 = sj.attend(wl.q, wl.K, wl.V, i3, wl.seq_len, workspace=ws, rank=32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(i1, i3)
+    # scores from the stage call against the oracle's scores, within the fp32 error bound
+    q = bits(wl.q)
+    M = wl.M.cpu().numpy()
+    kp = bits(Kp)
+    s_gpu = sc.cpu().numpy()
+    for b, n in ((0, 20000), (1, 15000), (2, 9)):
+        for h in range(2):
+            qbar = jssa.mean_query(q[b, 4 * h:4 * h + 4])
+            qhat = jssa.project_query(qbar, M[h])
+            s_ref = jssa.score_positions(qhat, kp[b, h, :n]).astype(np.float64)
+            kf = np.abs(bf16_to_f32(kp[b, h, :n]).astype(np.float64))
+            a = np.abs(M[h]).astype(np.float64) @ np.abs(qbar.astype(np.float64))
+            bound = 1e-5 * (kf @ np.abs(qhat.astype(np.float64)) + kf @ a) + 1e-30
+            assert np.all(np.abs(s_gpu[b, h, :n] - s_ref) <= bound)
+
+
+def test_golden_toy_hand_worked_on_gpu():
+    say("step golden toy")
+    g = golden_toy.load()
+    q, K, V, M = golden_toy.padded(g)
+    kp = jssa.project_keys(K, M)
+    qt = from_bits(q[None]).cuda()
+    Kt = from_bits(K[None, None]).cuda()
+    Vt = from_bits(V[None, None]).cuda()
+    Kpt = from_bits(kp[None, None]).cuda()
+    Mt = torch.from_numpy(M[None]).cuda()
+    sl = torch.tensor([5], dtype=torch.int32, device="cuda")
+    for c in g["cases"]:
+        out, idx = sj.decode_step(qt, Kt, Vt, Kpt, Mt, sl, c["k"], sm_scale=g["sm_scale"], out_f32=True)
+        torch.cuda.synchronize()
+        assert list(idx.cpu().numpy()[0, 0]) == c["idx"]
+        if c["out"] is not None:
+            o = out.cpu().numpy()[0]
+            assert np.max(np.abs(o[:, :4] - c["out"])) <= 1e-6
+            assert np.all(o[:, 4:] == 0)

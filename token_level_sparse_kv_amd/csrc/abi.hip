@@ -1,0 +1,229 @@
+// C ABI of libsjsa: host-side argument validation, workspace layout and launch
+// sequencing on the caller's stream. Nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include "sjsa_internal.h"
+
+namespace sjsa {
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+constexpr int ATT_TARGET_WGS = 2048;   // aim for >= 8 workgroups per CU in the attention launch
+constexpr int ATT_MIN_CHUNK = 64;
+constexpr int ATT_MAX_CHUNK = 1024;    // the attention kernel stages one chunk of indices in LDS
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const sjsa_shape* s) {
+  if (!s) return SJSA_ERR_NULL;
+  if (s->batch < 1 || s->n_kv_heads < 1 || s->capacity < 1 || s->capacity > INT32_MAX) return SJSA_ERR_DIMS;
+  if ((int64_t)s->batch * s->n_kv_heads > 65535) return SJSA_ERR_DIMS;     // grid.y limit
+  if (s->head_dim != HEAD_DIM) return SJSA_ERR_UNSUPPORTED;
+  if (s->rank != 16 && s->rank != 32 && s->rank != 64) return SJSA_ERR_UNSUPPORTED;
+  if (s->group != 1 && s->group != 2 && s->group != 4 && s->group != 8) return SJSA_ERR_UNSUPPORTED;
+  if (s->flags & ~SJSA_FLAG_OUT_F32) return SJSA_ERR_UNSUPPORTED;
+  return SJSA_OK;
+}
+
+int check_k(int32_t k) { return (k < 1 || k > SJSA_MAX_K) ? SJSA_ERR_K : SJSA_OK; }
+
+float resolve_scale(float sm_scale) {
+  return sm_scale != 0.f ? sm_scale : (float)(1.0 / sqrt((double)HEAD_DIM));
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SJSA_OK : SJSA_ERR_HIP; }
+
+}  // namespace
+
+Layout make_layout(const sjsa_shape& s, int k) {
+  Layout L;
+  L.units = (int64_t)s.batch * s.n_kv_heads;
+  L.score_stride = (int64_t)align_up((size_t)s.capacity, 64);
+  const int64_t max_split = (k + ATT_MIN_CHUNK - 1) / ATT_MIN_CHUNK;
+  int64_t want = (ATT_TARGET_WGS + L.units - 1) / L.units;
+  want = want < 1 ? 1 : (want > max_split ? max_split : want);
+  int64_t chunk = (k + want - 1) / want;
+  chunk = (int64_t)align_up((size_t)chunk, ATT_MIN_CHUNK);
+  if (chunk > ATT_MAX_CHUNK) chunk = ATT_MAX_CHUNK;
+  L.chunk = (int)chunk;
+  L.nsplit = (int)((k + chunk - 1) / chunk);
+  size_t off = 0;
+  L.off_qhat = off;
+  off = align_up(off + (size_t)L.units * QHAT_STRIDE * sizeof(float), WS_ALIGN);
+  L.off_hist = off;
+  off = align_up(off + (size_t)L.units * HIST_BINS * sizeof(uint32_t), WS_ALIGN);
+  L.off_scores = off;
+  off = align_up(off + (size_t)L.units * L.score_stride * sizeof(float), WS_ALIGN);
+  L.scores_end = off;
+  L.off_partials = off;
+  const size_t part = L.nsplit > 1 ? (size_t)L.units * L.nsplit * s.group * PART_STRIDE * sizeof(float) : 0;
+  off = align_up(off + part, WS_ALIGN);
+  L.total = off;
+  return L;
+}
+
+}  // namespace sjsa
+
+using namespace sjsa;
+
+extern "C" {
+
+const char* sjsa_status_string(int status) {
+  switch (status) {
+    case SJSA_OK: return "ok";
+    case SJSA_ERR_NULL: return "a required pointer is NULL";
+    case SJSA_ERR_DIMS: return "a size is out of range";
+    case SJSA_ERR_UNSUPPORTED: return "head_dim, rank, group or flags outside the supported set";
+    case SJSA_ERR_K: return "k is below 1 or above SJSA_MAX_K";
+    case SJSA_ERR_WORKSPACE: return "workspace is smaller than required";
+    case SJSA_ERR_HIP: return "the HIP runtime reported a launch error";
+    case SJSA_ERR_ALIGN: return "a pointer is not aligned as required";
+    default: return "unknown status";
+  }
+}
+
+size_t sjsa_decode_workspace_size(const sjsa_shape* shape, int32_t k) {
+  if (check_shape(shape) != SJSA_OK || check_k(k) != SJSA_OK) return 0;
+  return make_layout(*shape, k).total;
+}
+
+size_t sjsa_workspace_scores_offset(const sjsa_shape* shape) {
+  if (check_shape(shape) != SJSA_OK) return 0;
+  return make_layout(*shape, 1).off_scores;
+}
+
+int64_t sjsa_workspace_score_stride(const sjsa_shape* shape) {
+  if (check_shape(shape) != SJSA_OK) return 0;
+  return make_layout(*shape, 1).score_stride;
+}
+
+int sjsa_append_kv(const sjsa_shape* shape, const void* k_new, const void* v_new, int32_t n_new,
+                   const float* M, const int32_t* pos, void* K, void* V, void* Kproj, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!k_new || !v_new || !M || !pos || !K || !V || !Kproj) return SJSA_ERR_NULL;
+  if (n_new < 1) return SJSA_ERR_DIMS;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(K, 16) || !aligned(V, 16) ||
+      !aligned(Kproj, 16) || !aligned(M, 16) || !aligned(pos, 4))
+    return SJSA_ERR_ALIGN;
+  if ((n_new + 63) / 64 > 2147483647) return SJSA_ERR_DIMS;
+  return status_of(launch_append(*shape, (const uint16_t*)k_new, (const uint16_t*)v_new, n_new, M, pos,
+                                 (uint16_t*)K, (uint16_t*)V, (uint16_t*)Kproj, (hipStream_t)stream));
+}
+
+int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const float* M,
+               const int32_t* seq_len, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!q || !Kproj || !M || !seq_len || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(Kproj, 16) || !aligned(M, 16) || !aligned(seq_len, 4) ||
+      !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, 1);
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, ws, s);
+  if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
+  return status_of(e);
+}
+
+int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!q || !M || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(M, 16) || !aligned(workspace, WS_ALIGN)) return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, 1);
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (unsigned char*)workspace, (hipStream_t)stream));
+}
+
+int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!Kproj || !seq_len || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(Kproj, 16) || !aligned(seq_len, 4) || !aligned(workspace, WS_ALIGN)) return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, 1);
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  return status_of(launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, (unsigned char*)workspace,
+                                (hipStream_t)stream));
+}
+
+int sjsa_select(const sjsa_shape* shape, const int32_t* seq_len, int32_t k, int32_t* idx,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (!seq_len || !idx || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(workspace, WS_ALIGN)) return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  return status_of(launch_select(*shape, L, nullptr, 0, seq_len, k, idx, (unsigned char*)workspace,
+                                 (hipStream_t)stream));
+}
+
+int sjsa_topk(const sjsa_shape* shape, const float* scores, int64_t score_stride, const int32_t* seq_len,
+              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (!scores || !seq_len || !idx || !workspace) return SJSA_ERR_NULL;
+  if (score_stride < shape->capacity || (score_stride % 4) != 0) return SJSA_ERR_DIMS;
+  if (!aligned(scores, 16) || !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.off_scores) return SJSA_ERR_WORKSPACE;
+  return status_of(launch_select(*shape, L, scores, score_stride, seq_len, k, idx, (unsigned char*)workspace,
+                                 (hipStream_t)stream));
+}
+
+int sjsa_attend(const sjsa_shape* shape, const void* q, const void* K, const void* V, const int32_t* idx,
+                int32_t k, const int32_t* seq_len, float sm_scale, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (!q || !K || !V || !idx || !seq_len || !out || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(idx, 4) || !aligned(seq_len, 4) ||
+      !aligned(out, 16) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  if (!isfinite(sm_scale)) return SJSA_ERR_DIMS;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
+                      resolve_scale(sm_scale), out, ws, s);
+  return status_of(e);
+}
+
+int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, const void* V, const void* Kproj,
+                     const float* M, const int32_t* seq_len, int32_t k, float sm_scale, void* out, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (!q || !K || !V || !Kproj || !M || !seq_len || !out || !idx || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Kproj, 16) || !aligned(M, 16) ||
+      !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(out, 16) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  if (!isfinite(sm_scale)) return SJSA_ERR_DIMS;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, ws, s);
+  if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
+  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, seq_len, k, idx, ws, s);
+  if (e == hipSuccess)
+    e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
+                      resolve_scale(sm_scale), out, ws, s);
+  return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,217 @@
+// Gather-free indexed attention over each KV head's selected positions.
+//
+// Source: JSSA article, section 原理详解(二) (gather-free indexed attention): one
+// launch per layer; the kernel resolves every KV head's own index set and maps
+// each query head to its KV head's set; K and V are read in place, never copied
+// to a staging buffer. One token's K (or V) row is contiguous along head_dim, so
+// each indexed read is a full burst (section 不规则索引本身不是障碍): here a
+// 256-byte row is read by 16 lanes with 16 bytes each.
+//
+// grid = (nsplit, B * H_kv), 256 threads = 16 row slots of 16 lanes. A workgroup
+// handles `chunk` consecutive entries of its unit's index list; each slot walks
+// its share of rows, U rows at a time, computing the G logits per row (lane t
+// holds head dims 8t..8t+7; a DPP row reduction finishes each dot), and keeps an
+// online softmax (running max m, sum l, accumulator acc) per query head, in the
+// exp2 domain with q pre-scaled by sm_scale*log2(e). Slots are combined in LDS;
+// with one split the workgroup writes the output directly, otherwise it writes its
+// (m, l, acc) partial and merge_kernel (one workgroup per unit, launched next on the
+// same stream) combines the partials in split order with a log-sum-exp merge.
+#include "sjsa_device.h"
+#include "sjsa_internal.h"
+
+namespace sjsa {
+namespace {
+
+constexpr int ATT_THREADS = 256;
+constexpr int SLOTS = ATT_THREADS / 16;
+constexpr int U = 4;                 // rows in flight per slot
+constexpr float LOG2E = 1.4426950408889634f;
+
+template <int G>
+__global__ __launch_bounds__(ATT_THREADS) void attend_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ seq_len, int n_kv_heads, int64_t cap,
+    int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
+    void* __restrict__ out, int out_f32) {
+  __shared__ int32_t sidx[1024];
+  __shared__ float sm_m[SLOTS][G];
+  __shared__ float sm_l[SLOTS][G];
+  __shared__ float sm_acc[SLOTS][G][HEAD_DIM];
+
+  const int unit = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = unit / n_kv_heads;
+  const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
+  const int tid = threadIdx.x;
+  const int slot = tid >> 4;
+  const int t = tid & 15;
+
+  const int first = split * chunk;
+  const int cnt = max(0, min(chunk, k - first));
+  const int32_t* ids = idx + (size_t)unit * k + first;
+  for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
+
+  float qv[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const u32x4 w = ld16(q + ((size_t)unit * G + g) * HEAD_DIM + t * 8);
+    qv[g][0] = bf_lo(w.x) * qscale; qv[g][1] = bf_hi(w.x) * qscale;
+    qv[g][2] = bf_lo(w.y) * qscale; qv[g][3] = bf_hi(w.y) * qscale;
+    qv[g][4] = bf_lo(w.z) * qscale; qv[g][5] = bf_hi(w.z) * qscale;
+    qv[g][6] = bf_lo(w.w) * qscale; qv[g][7] = bf_hi(w.w) * qscale;
+  }
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+  __syncthreads();
+
+  const uint16_t* Kb = K + (size_t)unit * cap * HEAD_DIM + t * 8;
+  const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + t * 8;
+
+  for (int base = slot * U; base < cnt; base += SLOTS * U) {
+    int64_t j[U];
+    bool ok[U];
+    u32x4 kw[U], vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u;
+      j[u] = i < cnt ? (int64_t)sidx[i] : -1;
+      ok[u] = j[u] >= 0 && j[u] < n;
+    }
+    // loads are unconditional (an invalid entry reads row 0, which always exists, and
+    // gets zero weight), so the compiler can keep every load of the batch in flight
+#pragma unroll
+    for (int u = 0; u < U; ++u) kw[u] = ld16(Kb + (ok[u] ? j[u] : 0) * HEAD_DIM);
+#pragma unroll
+    for (int u = 0; u < U; ++u) vw[u] = ld16(Vb + (ok[u] ? j[u] : 0) * HEAD_DIM);
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float z[U];
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        z[u] = row16_sum(dot8_bf16(qv[g], kw[u]));
+        z[u] = ok[u] ? z[u] : -INFINITY;
+        mx = fmaxf(mx, z[u]);
+      }
+      if (mx == -INFINITY) continue;          // nothing valid yet for this head
+      const float sc = exp2f(m[g] - mx);     // 0 when m was -inf
+      float p[U];
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) { p[u] = exp2f(z[u] - mx); ps += p[u]; }
+      l[g] = l[g] * sc + ps;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = acc[g][e] * sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t word = (e >> 1) == 0 ? vw[u].x : (e >> 1) == 1 ? vw[u].y : (e >> 1) == 2 ? vw[u].z : vw[u].w;
+          a = fmaf(p[u], (e & 1) ? bf_hi(word) : bf_lo(word), a);
+        }
+        acc[g][e] = a;
+      }
+      m[g] = mx;
+    }
+  }
+
+  // ---- combine the 16 slots of this workgroup
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (t == 0) { sm_m[slot][g] = m[g]; sm_l[slot][g] = l[g]; }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_acc[slot][g][t * 8 + e] = acc[g][e];
+  }
+  __syncthreads();
+
+  const bool direct = nsplit == 1;
+  float* part = partials + ((size_t)unit * nsplit + split) * G * PART_STRIDE;
+  for (int o = tid; o < G * HEAD_DIM; o += ATT_THREADS) {
+    const int g = o / HEAD_DIM, dim = o - g * HEAD_DIM;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) M = fmaxf(M, sm_m[s][g]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const float ms = sm_m[s][g];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f(ms - M);
+        L = fmaf(sm_l[s][g], w, L);
+        A = fmaf(sm_acc[s][g][dim], w, A);
+      }
+    }
+    if (direct) {
+      const float r = L > 0.f ? A / L : 0.f;
+      const size_t oi = ((size_t)unit * G + g) * HEAD_DIM + dim;
+      if (out_f32) reinterpret_cast<float*>(out)[oi] = r;
+      else reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
+    } else {
+      part[g * PART_STRIDE + dim] = A;
+      if (dim == 0) { part[g * PART_STRIDE + HEAD_DIM] = M; part[g * PART_STRIDE + HEAD_DIM + 1] = L; }
+    }
+  }
+}
+
+// One workgroup per unit: combine the nsplit partials of every query head in split
+// order. m_s are running maxima in the exp2 domain; l_s the sums; acc_s the
+// unnormalized outputs: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+template <int G>
+__global__ __launch_bounds__(ATT_THREADS) void merge_kernel(const float* __restrict__ partials, int nsplit,
+                                                            void* __restrict__ out, int out_f32) {
+  const int unit = blockIdx.x;
+  const float* pu = partials + (size_t)unit * nsplit * G * PART_STRIDE;
+  for (int o = threadIdx.x; o < G * HEAD_DIM; o += ATT_THREADS) {
+    const int g = o / HEAD_DIM, dim = o - g * HEAD_DIM;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pu[((size_t)s * G + g) * PART_STRIDE + HEAD_DIM]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < nsplit; ++s) {
+        const float* ps = pu + ((size_t)s * G + g) * PART_STRIDE;
+        const float ms = ps[HEAD_DIM];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f(ms - M);
+        L = fmaf(ps[HEAD_DIM + 1], w, L);
+        A = fmaf(ps[dim], w, A);
+      }
+    }
+    const float r = L > 0.f ? A / L : 0.f;
+    const size_t oi = ((size_t)unit * G + g) * HEAD_DIM + dim;
+    if (out_f32) reinterpret_cast<float*>(out)[oi] = r;
+    else reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
+                         const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
+                         float sm_scale, void* out, unsigned char* ws, hipStream_t st) {
+  float* partials = reinterpret_cast<float*>(ws + L.off_partials);
+  const float qscale = sm_scale * LOG2E;
+  const int out_f32 = (s.flags & SJSA_FLAG_OUT_F32) ? 1 : 0;
+  const dim3 grid((unsigned)L.nsplit, (unsigned)L.units), block(ATT_THREADS);
+#define SJSA_ATT(GG)                                                                              \
+  attend_kernel<GG><<<grid, block, 0, st>>>(q, K, V, idx, seq_len, s.n_kv_heads, s.capacity, k,   \
+                                            L.chunk, L.nsplit, qscale, partials, out, out_f32);   \
+  if (L.nsplit > 1) merge_kernel<GG><<<dim3((unsigned)L.units), block, 0, st>>>(partials, L.nsplit, out, out_f32)
+  switch (s.group) {
+    case 1: SJSA_ATT(1); break;
+    case 2: SJSA_ATT(2); break;
+    case 4: SJSA_ATT(4); break;
+    case 8: SJSA_ATT(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SJSA_ATT
+  return hipGetLastError();
+}
+
+}  // namespace sjsa

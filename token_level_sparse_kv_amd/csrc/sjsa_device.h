@@ -1,0 +1,104 @@
+// Device-side helpers shared by the gfx950 kernels of libsjsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sjsa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 halves of a 32-bit word (little endian: element 2i in the low half).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bit pattern, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving map of an fp32 score to a u32 key: a larger score gives a
+// larger key; -0 and +0 share one key; every NaN maps to 0, below -inf (0x007fffff).
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  const uint32_t mag = u & 0x7fffffffu;
+  if (mag > 0x7f800000u) return 0u;
+  if (mag == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Cross-lane moves with DPP (within rows of 16 lanes). quad_perm [a,b,c,d] is
+// encoded as a | b<<2 | c<<4 | d<<6; row_ror:n is 0x120 + n.
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // [2,3,0,1]
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Lane xor 4 inside groups of 32 (ds_swizzle bitmask mode: and 0x1f, or 0, xor 4).
+__device__ __forceinline__ float swz_xor4(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same value.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<DPP_ROW_ROR8>(v);
+  v += dpp<DPP_ROW_ROR4>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  v += dpp<DPP_QUAD_XOR1>(v);
+  return v;
+}
+
+// Max over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<DPP_ROW_ROR8>(v));
+  v = fmaxf(v, dpp<DPP_ROW_ROR4>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_XOR1>(v));
+  return v;
+}
+
+// 128-bit global loads; the nontemporal form streams data that is read once.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Dot of 8 fp32 values with the 8 bf16 values packed in a 128-bit word.
+__device__ __forceinline__ float dot8_bf16(const float* q, u32x4 w) {
+  float a = q[0] * bf_lo(w.x);
+  a = fmaf(q[1], bf_hi(w.x), a);
+  a = fmaf(q[2], bf_lo(w.y), a);
+  a = fmaf(q[3], bf_hi(w.y), a);
+  a = fmaf(q[4], bf_lo(w.z), a);
+  a = fmaf(q[5], bf_hi(w.z), a);
+  a = fmaf(q[6], bf_lo(w.w), a);
+  a = fmaf(q[7], bf_hi(w.w), a);
+  return a;
+}
+
+// Wave-wide (64 lanes) inclusive prefix sum of a u32.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace sjsa

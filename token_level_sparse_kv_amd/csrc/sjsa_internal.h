@@ -1,0 +1,45 @@
+// Internal host-side declarations of libsjsa: workspace layout and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sjsa.h"
+
+namespace sjsa {
+
+constexpr int HEAD_DIM = 128;
+constexpr int HIST_BINS = 4096;      // first radix digit: top 12 bits of the score key
+constexpr int HIST_SHIFT = 20;
+constexpr int QHAT_STRIDE = 64;      // floats reserved per unit for q_hat (r <= 64)
+constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
+
+struct Layout {
+  int64_t units = 0;          // B * H_kv
+  int64_t score_stride = 0;   // floats per unit row of the score buffer
+  int nsplit = 1;             // attention splits per unit
+  int chunk = 0;              // selected indices per split
+  size_t off_qhat = 0, off_hist = 0, off_scores = 0, off_partials = 0;
+  size_t scores_end = 0, total = 0;
+};
+
+Layout make_layout(const sjsa_shape& s, int k);
+
+// Kernel launchers (device pointers; host-validated arguments).
+hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
+                         const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, uint16_t* Kproj,
+                         hipStream_t st);
+hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
+                       unsigned char* ws, hipStream_t st);
+hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kproj, const int32_t* seq_len,
+                        unsigned char* ws, hipStream_t st);
+hipError_t launch_hist(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
+                       const int32_t* seq_len, unsigned char* ws, hipStream_t st);
+hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
+                         const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws, hipStream_t st);
+hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
+                         const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
+                         float sm_scale, void* out, unsigned char* ws, hipStream_t st);
+
+}  // namespace sjsa

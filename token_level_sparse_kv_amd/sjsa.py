@@ -1,0 +1,265 @@
+"""ctypes binding of libsjsa (the MI355X JSSA sparse-decode library).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, turned into pointers, and the work is enqueued on torch's current
+stream. Every computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and a missing library raises at load time.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libsjsa.so")
+
+SJSA_FLAG_OUT_F32 = 1
+SJSA_MAX_K = 1 << 20
+
+
+class SjsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sjsa error {status}: {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "sjsa_append_kv": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "sjsa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "sjsa_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                        ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_score": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_prep": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_scan": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_attend": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_float,
+                                   _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_topk": (ctypes.c_int, [ctypes.POINTER(Shape), _P, ctypes.c_int64, _P, ctypes.c_int32, _P, _P,
+                                 ctypes.c_size_t, _P]),
+    "sjsa_workspace_scores_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "sjsa_workspace_score_stride": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
+    "sjsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def lib():
+    """Load libsjsa.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m token_level_sparse_kv_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SjsaError(status, lib().sjsa_status_string(status).decode())
+
+
+def make_shape(batch, n_kv_heads, group, head_dim, rank, capacity, out_f32=False) -> Shape:
+    return Shape(batch, n_kv_heads, group, head_dim, rank, SJSA_FLAG_OUT_F32 if out_f32 else 0, capacity)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def shape_of(q: torch.Tensor, K: torch.Tensor, M: torch.Tensor, out_f32=False) -> Shape:
+    B, Hkv, cap, d = K.shape
+    Hq = q.shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    return make_shape(B, Hkv, Hq // Hkv, d, M.shape[1], cap, out_f32)
+
+
+def workspace_size(shape: Shape, k: int) -> int:
+    n = lib().sjsa_decode_workspace_size(ctypes.byref(shape), int(k))
+    if n == 0:
+        raise SjsaError(-2, "invalid shape or k for the workspace query")
+    return int(n)
+
+
+def alloc_workspace(shape: Shape, k: int, device=None) -> torch.Tensor:
+    return torch.empty(workspace_size(shape, k), dtype=torch.uint8, device=device or "cuda")
+
+
+def scores_view(shape: Shape, workspace: torch.Tensor) -> torch.Tensor:
+    """The fp32 score buffer inside a workspace, viewed as [B, H_kv, stride]."""
+    off = lib().sjsa_workspace_scores_offset(ctypes.byref(shape))
+    stride = lib().sjsa_workspace_score_stride(ctypes.byref(shape))
+    n = shape.batch * shape.n_kv_heads * stride * 4
+    return workspace[off:off + n].view(torch.float32).view(shape.batch, shape.n_kv_heads, stride)
+
+
+def append_kv(k_new, v_new, M, pos, K, V, Kproj, stream=None):
+    """Write n_new tokens per (b, h) at slots pos[b].. into K, V and Kproj (in place)."""
+    B, Hkv, cap, d = K.shape
+    r = M.shape[1]
+    T = k_new.shape[2]
+    _need(K, "K", torch.bfloat16)
+    _need(V, "V", torch.bfloat16, K.shape)
+    _need(Kproj, "Kproj", torch.bfloat16, (B, Hkv, cap, r))
+    _need(k_new, "k_new", torch.bfloat16, (B, Hkv, T, d))
+    _need(v_new, "v_new", torch.bfloat16, (B, Hkv, T, d))
+    _need(M, "M", torch.float32, (Hkv, r, d))
+    _need(pos, "pos", torch.int32, (B,))
+    shape = make_shape(B, Hkv, 1, d, r, cap)
+    _check(lib().sjsa_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), T, _ptr(M), _ptr(pos),
+                                _ptr(K), _ptr(V), _ptr(Kproj), _stream(stream)))
+
+
+def _step_checks(q, K, V, Kproj, M, seq_len):
+    B, Hkv, cap, d = K.shape
+    r = M.shape[1]
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != d:
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected [B={B}, H_q, d={d}]")
+    _need(K, "K", torch.bfloat16)
+    _need(V, "V", torch.bfloat16, K.shape)
+    if Kproj is not None:
+        _need(Kproj, "Kproj", torch.bfloat16, (B, Hkv, cap, r))
+    _need(M, "M", torch.float32, (Hkv, r, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+
+
+def decode_step(q, K, V, Kproj, M, seq_len, k, sm_scale=0.0, out=None, idx=None, workspace=None,
+                out_f32=False, stream=None):
+    """One sparse decode step. Returns (out [B, H_q, d], idx [B, H_kv, k])."""
+    _step_checks(q, K, V, Kproj, M, seq_len)
+    shape = shape_of(q, K, M, out_f32)
+    B, Hkv = shape.batch, shape.n_kv_heads
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hkv, int(k)), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, q.shape)
+    _need(idx, "idx", torch.int32, (B, Hkv, int(k)))
+    if workspace is None:
+        workspace = alloc_workspace(shape, k, q.device)
+    _check(lib().sjsa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(Kproj), _ptr(M),
+                                  _ptr(seq_len), int(k), float(sm_scale), _ptr(out), _ptr(idx),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, idx
+
+
+def score(q, Kproj, M, seq_len, workspace, capacity=None, stream=None):
+    """Scoring prep + score scan into the workspace; returns the [B, H_kv, stride] fp32 view."""
+    B, Hkv, cap, r = Kproj.shape
+    d = M.shape[2]
+    shape = make_shape(B, Hkv, q.shape[1] // Hkv, d, r, cap)
+    _need(q, "q", torch.bfloat16, (B, shape.group * Hkv, d))
+    _need(Kproj, "Kproj", torch.bfloat16)
+    _need(M, "M", torch.float32, (Hkv, r, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    _check(lib().sjsa_score(ctypes.byref(shape), _ptr(q), _ptr(Kproj), _ptr(M), _ptr(seq_len),
+                            _ptr(workspace), workspace.numel(), _stream(stream)))
+    return scores_view(shape, workspace)
+
+
+def prep(shape: Shape, q, M, workspace, stream=None):
+    """Scoring prep only (mean query, projection; clears the histogram and counters)."""
+    _need(q, "q", torch.bfloat16, (shape.batch, shape.n_kv_heads * shape.group, shape.head_dim))
+    _need(M, "M", torch.float32, (shape.n_kv_heads, shape.rank, shape.head_dim))
+    _check(lib().sjsa_prep(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(workspace), workspace.numel(),
+                           _stream(stream)))
+
+
+def scan(shape: Shape, Kproj, seq_len, workspace, stream=None):
+    """Score scan only (after prep)."""
+    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need(seq_len, "seq_len", torch.int32, (shape.batch,))
+    _check(lib().sjsa_scan(ctypes.byref(shape), _ptr(Kproj), _ptr(seq_len), _ptr(workspace), workspace.numel(),
+                           _stream(stream)))
+
+
+def select(shape: Shape, seq_len, k, workspace, idx=None, stream=None):
+    """Top-k over the scores left in the workspace by score()."""
+    if idx is None:
+        idx = torch.empty((shape.batch, shape.n_kv_heads, int(k)), dtype=torch.int32, device=workspace.device)
+    _need(idx, "idx", torch.int32, (shape.batch, shape.n_kv_heads, int(k)))
+    _check(lib().sjsa_select(ctypes.byref(shape), _ptr(seq_len), int(k), _ptr(idx), _ptr(workspace),
+                             workspace.numel(), _stream(stream)))
+    return idx
+
+
+def topk(scores, seq_len, k, workspace=None, idx=None, group=1, rank=16, stream=None):
+    """Top-k of caller fp32 scores [B, H_kv, stride] (the first seq_len[b] entries valid)."""
+    B, Hkv, stride = scores.shape
+    _need(scores, "scores", torch.float32)
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    shape = make_shape(B, Hkv, group, 128, rank, stride)
+    if workspace is None:
+        workspace = alloc_workspace(shape, k, scores.device)
+    if idx is None:
+        idx = torch.empty((B, Hkv, int(k)), dtype=torch.int32, device=scores.device)
+    _check(lib().sjsa_topk(ctypes.byref(shape), _ptr(scores), stride, _ptr(seq_len), int(k), _ptr(idx),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
+    return idx
+
+
+def attend(q, K, V, idx, seq_len, sm_scale=0.0, out=None, workspace=None, out_f32=False, rank=16,
+           stream=None):
+    """Gather-free attention of every query head over its KV head's idx [B, H_kv, k]."""
+    B, Hkv, cap, d = K.shape
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16)
+    _need(V, "V", torch.bfloat16, K.shape)
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    k = idx.shape[2]
+    _need(idx, "idx", torch.int32, (B, Hkv, k))
+    shape = make_shape(B, Hkv, q.shape[1] // Hkv, d, rank, cap, out_f32)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, q.shape)
+    if workspace is None:
+        workspace = alloc_workspace(shape, k, q.device)
+    _check(lib().sjsa_attend(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(idx), int(k), _ptr(seq_len),
+                             float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def default_sm_scale(head_dim: int = 128) -> float:
+    return 1.0 / math.sqrt(head_dim)
