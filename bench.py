@@ -148,13 +148,13 @@ def main():
         sj.append_kv(k_new, v_new, M, pos_new, K, V, Kp)
         if ev is not None:
             ev[1].record()
-        sj.prep(shape, q, M, ws)
+        sj.prep(shape, q, M, Kp, seq_len, k, ws)
         if ev is not None:
             ev[2].record()
         sj.scan(shape, Kp, seq_len, ws)
         if ev is not None:
             ev[3].record()
-        sj.select(shape, seq_len, k, ws, idx=idx)
+        sj.select(shape, Kp, seq_len, k, ws, idx=idx)
         if ev is not None:
             ev[4].record()
         sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)

@@ -58,10 +58,15 @@ typedef enum sjsa_status {
   SJSA_ERR_ALIGN = -7        /* a pointer is not aligned as required */
 } sjsa_status;
 
-/* Output dtype flag (sjsa_shape.flags): fp32 instead of bf16 for `out`. */
+/* sjsa_shape.flags bits.
+ * SJSA_FLAG_OUT_F32: `out` is fp32 instead of bf16.
+ * SJSA_FLAG_WRITE_SCORES: the score scan also stores every fp32 score in the
+ *   workspace (for inspection; see sjsa_score). Results do not change. */
 #define SJSA_FLAG_OUT_F32 1
-/* Largest supported token budget per call. */
+#define SJSA_FLAG_WRITE_SCORES 2
+/* Largest supported token budget per call, and largest cache capacity. */
 #define SJSA_MAX_K (1 << 20)
+#define SJSA_MAX_CAPACITY ((int64_t)1 << 30)
 
 typedef struct sjsa_shape {
   int32_t batch;      /* B >= 1 */
@@ -69,8 +74,8 @@ typedef struct sjsa_shape {
   int32_t group;      /* G: query heads per KV head (1, 2, 4, 8) */
   int32_t head_dim;   /* d: must be 128 */
   int32_t rank;       /* r: 16, 32 or 64 */
-  int32_t flags;      /* 0 or SJSA_FLAG_OUT_F32 */
-  int64_t capacity;   /* cap: token slots per (b, h) in K, V, Kproj; 1 .. 2^31-1 */
+  int32_t flags;      /* 0 or SJSA_FLAG_* bits */
+  int64_t capacity;   /* cap: token slots per (b, h) in K, V, Kproj; 1 .. SJSA_MAX_CAPACITY */
 } sjsa_shape;
 
 /*
@@ -118,28 +123,33 @@ int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, cons
 /*
  * Stage 1+2 of the step: scoring prep (q_bar, q_hat; section 打分误差的定义)
  * and the full-context score scan over Kproj (section 原理详解(二): scoring
- * still scans every candidate). Leaves the fp32 scores and a first-digit
- * histogram of them in the workspace. The score of (b, h, j) can be read back
- * at float offset sjsa_workspace_scores_offset(shape)/4 + (b*H_kv + h)*stride + j,
- * stride = sjsa_workspace_score_stride(shape). The workspace may be the one
- * sized for decode, or at least sjsa_workspace_scores_offset + 4*B*H_kv*stride.
+ * still scans every candidate position). The scan keeps, per (b, h), only the
+ * positions whose score reaches a threshold placed by the prep stage from a
+ * sample of 2048 evenly spaced rows, low enough that the exact top k is among
+ * them in all but misjudged cases (which sjsa_select detects and resolves
+ * exactly); hence the budget k is an argument. With SJSA_FLAG_WRITE_SCORES the
+ * scan also stores every fp32 score: that of (b, h, j) is at float offset
+ * sjsa_workspace_scores_offset(shape)/4 + (b*H_kv + h)*stride + j, stride =
+ * sjsa_workspace_score_stride(shape).
  * Errors: as sjsa_decode_step.
  */
 int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const float* M,
-               const int32_t* seq_len, void* workspace, size_t workspace_bytes, void* stream);
+               const int32_t* seq_len, int32_t k, void* workspace, size_t workspace_bytes, void* stream);
 
 /* sjsa_score in two launches, for callers that time the stages separately:
- * sjsa_prep (q_bar, q_hat; clears the unit's score histogram) then
- * sjsa_scan (the score scan over Kproj). Same workspace rules as sjsa_score. */
-int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, void* workspace,
-              size_t workspace_bytes, void* stream);
+ * sjsa_prep (q_bar, q_hat, the candidate threshold) then sjsa_scan (the score
+ * scan over Kproj). Same workspace rules as sjsa_score. */
+int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, const void* Kproj,
+              const int32_t* seq_len, int32_t k, void* workspace, size_t workspace_bytes, void* stream);
 int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* Stage 3: top-k of the scores sjsa_score left in the workspace -> idx [B, H_kv, k].
- * Source: JSSA article, section JSSA 的整体结构 (per-KV-head top-k). */
-int sjsa_select(const sjsa_shape* shape, const int32_t* seq_len, int32_t k, int32_t* idx,
-                void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 3: top-k per (b, h) from what sjsa_score left in the workspace -> idx
+ * [B, H_kv, k] (Kproj is read again only for a unit whose sampled threshold
+ * misjudged the scores). Source: JSSA article, section JSSA 的整体结构
+ * (per-KV-head top-k shared by the group's query heads). */
+int sjsa_select(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, int32_t k,
+                int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Stage 4: gather-free indexed attention (JSSA article, section 原理详解(二):
@@ -160,7 +170,8 @@ int sjsa_topk(const sjsa_shape* shape, const float* scores, int64_t score_stride
               const int32_t* seq_len, int32_t k, int32_t* idx,
               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace layout helpers for reading the scores back (host only). */
+/* Workspace layout helpers for reading scores stored with SJSA_FLAG_WRITE_SCORES
+ * (host only). */
 size_t sjsa_workspace_scores_offset(const sjsa_shape* shape);
 int64_t sjsa_workspace_score_stride(const sjsa_shape* shape);
 

@@ -27,10 +27,12 @@ def test_every_declared_symbol_is_exported():
 
 
 def _shape(**kw):
-    base = dict(batch=2, n_kv_heads=8, group=4, head_dim=128, rank=32, capacity=1000)
+    base = dict(batch=2, n_kv_heads=8, group=4, head_dim=128, rank=32, capacity=1000, flags=0)
     base.update(kw)
-    return sj.make_shape(base["batch"], base["n_kv_heads"], base["group"], base["head_dim"], base["rank"],
-                         base["capacity"])
+    s = sj.make_shape(base["batch"], base["n_kv_heads"], base["group"], base["head_dim"], base["rank"],
+                      base["capacity"])
+    s.flags = base["flags"]
+    return s
 
 
 def test_workspace_size_and_layout():
@@ -63,7 +65,8 @@ def _step(shape, k=16, ws_bytes=1 << 30, ptrs=None, sm_scale=0.0):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), -3), (dict(rank=24), -3), (dict(group=3), -3), (dict(group=16), -3),
-    (dict(batch=0), -2), (dict(capacity=0), -2), (dict(capacity=1 << 31), -2),
+    (dict(flags=4), -3),
+    (dict(batch=0), -2), (dict(capacity=0), -2), (dict(capacity=(1 << 30) + 1), -2),
     (dict(batch=1000, n_kv_heads=100), -2),
 ])
 def test_bad_shapes(kw, status):
@@ -93,8 +96,12 @@ def test_stage_validation():
     L = sj.lib()
     s = _shape()
     f = ctypes.c_void_p(FAKE)
-    assert L.sjsa_score(ctypes.byref(s), f, f, f, f, f, 16, None) == -5
-    assert L.sjsa_select(ctypes.byref(s), f, 0, f, f, 1 << 30, None) == -4
+    assert L.sjsa_score(ctypes.byref(s), f, f, f, f, 16, f, 16, None) == -5
+    assert L.sjsa_score(ctypes.byref(s), f, f, f, f, 0, f, 1 << 30, None) == -4
+    assert L.sjsa_prep(ctypes.byref(s), f, f, None, f, 16, f, 1 << 30, None) == -1
+    assert L.sjsa_scan(ctypes.byref(s), f, f, f, 16, None) == -5
+    assert L.sjsa_select(ctypes.byref(s), f, f, 0, f, f, 1 << 30, None) == -4
+    assert L.sjsa_select(ctypes.byref(s), None, f, 8, f, f, 1 << 30, None) == -1
     assert L.sjsa_topk(ctypes.byref(s), f, 999, f, 8, f, f, 1 << 30, None) == -2      # stride < cap
     assert L.sjsa_topk(ctypes.byref(s), f, 1002, f, 8, f, f, 1 << 30, None) == -2     # stride % 4
     assert L.sjsa_attend(ctypes.byref(s), f, f, f, f, 8, f, 0.0, f, f, 100, None) == -5

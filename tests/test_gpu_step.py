@@ -101,13 +101,13 @@ def test_stage_calls_equal_fused_step_and_are_deterministic():
     ws = sj.alloc_workspace(shape, 700)
     o1, i1 = sj.decode_step(wl.q, wl.K, wl.V, Kp, wl.M, wl.seq_len, 700, workspace=ws)
     o2, i2 = sj.decode_step(wl.q, wl.K, wl.V, Kp, wl.M, wl.seq_len, 700, workspace=ws)
-    sc = sj.score(wl.q, Kp, wl.M, wl.seq_len, ws)
-    i3 = sj.select(shape, wl.seq_len, 700, ws)
+    sc = sj.score(wl.q, Kp, wl.M, wl.seq_len, 700, ws, write_scores=True)
+    i3 = sj.select(shape, Kp, wl.seq_len, 700, ws)
     o3 = sj.attend(wl.q, wl.K, wl.V, i3, wl.seq_len, workspace=ws, rank=32)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(i1, i2)
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(i1, i3)
-    # scores from the stage call against the oracle's scores, within the fp32 error bound
+    # stored scores against the oracle's scores, within the fp32 error bound
     q = bits(wl.q)
     M = wl.M.cpu().numpy()
     kp = bits(Kp)
@@ -142,3 +142,45 @@ def test_golden_toy_hand_worked_on_gpu():
             o = out.cpu().numpy()[0]
             assert np.max(np.abs(o[:, :4] - c["out"])) <= 1e-6
             assert np.all(o[:, 4:] == 0)
+
+
+def _ties_check(wl, kp, k, tag):
+    """Exact index-set equality (scores tie bit-for-bit on both sides) plus output parity."""
+    o, ix, _ = _run_and_check(wl, kp, k, tag=tag)
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    M = wl.M.cpu().numpy()
+    for b in range(wl.batch):
+        n = int(wl.seq_len[b])
+        for h in range(wl.n_kv_heads):
+            _, ref_idx, _ = jssa.decode_unit(q[b, 4 * h:4 * h + 4], K[b, h], V[b, h], kp[b, h], M[h], n, k,
+                                             jssa.default_sm_scale(128))
+            assert np.array_equal(ix[b, h], ref_idx), (tag, b, h)
+
+
+def test_candidate_overflow_falls_back_exactly():
+    # every projected row identical: all scores tie, every row reaches the threshold,
+    # and 40000 candidates exceed what the selection keeps in LDS
+    say("step candidate overflow -> exact fallback")
+    wl = workloads.gaussian(1, 2, 4, 128, 16, 40000, 1500, seed=25, device="cuda")
+    kp = kproj_oracle(bits(wl.K[:, :, :1].contiguous()), wl.M.cpu().numpy())
+    kp = np.ascontiguousarray(np.repeat(kp, 40000, axis=2))
+    _ties_check(wl, kp, 1500, "overflow")
+
+
+def test_candidate_underflow_falls_back_exactly():
+    # the rows the prep stage samples (positions s*n/2048) score high, all others low:
+    # the sampled threshold lands above the true k-th score, too few rows qualify
+    say("step candidate underflow -> exact fallback")
+    n, k = 40000, 2000
+    wl = workloads.gaussian(1, 1, 4, 128, 16, n, k, seed=26, device="cuda")
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    qhat = jssa.project_query(jssa.mean_query(q[0, 0:4]), M[0]).astype(np.float64)
+    low = jssa.project_keys(bits(wl.K[0, 0, :1].contiguous()), M[0])[0]
+    high = (np.sign(qhat) * 4.0)
+    from oracle.numerics import round_to_bf16
+    high = round_to_bf16(high)
+    kp = np.tile(low, (1, 1, n, 1)).astype(np.uint16)
+    sampled = (np.arange(2048, dtype=np.int64) * n) // 2048
+    kp[0, 0, sampled] = high
+    _ties_check(wl, kp, k, "underflow")

@@ -9,7 +9,7 @@ namespace sjsa {
 namespace {
 
 constexpr size_t WS_ALIGN = 256;
-constexpr int ATT_TARGET_WGS = 2048;   // aim for >= 8 workgroups per CU in the attention launch
+constexpr int ATT_TARGET_WGS = 1024;   // attention workgroups to aim for (4 per CU)
 constexpr int ATT_MIN_CHUNK = 64;
 constexpr int ATT_MAX_CHUNK = 1024;    // the attention kernel stages one chunk of indices in LDS
 
@@ -19,12 +19,12 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int check_shape(const sjsa_shape* s) {
   if (!s) return SJSA_ERR_NULL;
-  if (s->batch < 1 || s->n_kv_heads < 1 || s->capacity < 1 || s->capacity > INT32_MAX) return SJSA_ERR_DIMS;
+  if (s->batch < 1 || s->n_kv_heads < 1 || s->capacity < 1 || s->capacity > SJSA_MAX_CAPACITY) return SJSA_ERR_DIMS;
   if ((int64_t)s->batch * s->n_kv_heads > 65535) return SJSA_ERR_DIMS;     // grid.y limit
   if (s->head_dim != HEAD_DIM) return SJSA_ERR_UNSUPPORTED;
   if (s->rank != 16 && s->rank != 32 && s->rank != 64) return SJSA_ERR_UNSUPPORTED;
   if (s->group != 1 && s->group != 2 && s->group != 4 && s->group != 8) return SJSA_ERR_UNSUPPORTED;
-  if (s->flags & ~SJSA_FLAG_OUT_F32) return SJSA_ERR_UNSUPPORTED;
+  if (s->flags & ~(SJSA_FLAG_OUT_F32 | SJSA_FLAG_WRITE_SCORES)) return SJSA_ERR_UNSUPPORTED;
   return SJSA_OK;
 }
 
@@ -50,11 +50,17 @@ Layout make_layout(const sjsa_shape& s, int k) {
   if (chunk > ATT_MAX_CHUNK) chunk = ATT_MAX_CHUNK;
   L.chunk = (int)chunk;
   L.nsplit = (int)((k + chunk - 1) / chunk);
+  L.nseg_cap = (s.capacity + SEG_ROWS - 1) / SEG_ROWS;
+  L.cand_stride = (s.capacity + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
   size_t off = 0;
   L.off_qhat = off;
   off = align_up(off + (size_t)L.units * QHAT_STRIDE * sizeof(float), WS_ALIGN);
-  L.off_hist = off;
-  off = align_up(off + (size_t)L.units * HIST_BINS * sizeof(uint32_t), WS_ALIGN);
+  L.off_tlow = off;
+  off = align_up(off + (size_t)L.units * 2 * sizeof(uint32_t), WS_ALIGN);
+  L.off_counts = off;
+  off = align_up(off + (size_t)L.units * L.nseg_cap * sizeof(uint32_t), WS_ALIGN);
+  L.off_cand = off;
+  off = align_up(off + (size_t)L.units * L.cand_stride * sizeof(uint64_t), WS_ALIGN);
   L.off_scores = off;
   off = align_up(off + (size_t)L.units * L.score_stride * sizeof(float), WS_ALIGN);
   L.scores_end = off;
@@ -115,31 +121,36 @@ int sjsa_append_kv(const sjsa_shape* shape, const void* k_new, const void* v_new
 }
 
 int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const float* M,
-               const int32_t* seq_len, void* workspace, size_t workspace_bytes, void* stream) {
+               const int32_t* seq_len, int32_t k, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st) return st;
+  if ((st = check_k(k))) return st;
   if (!q || !Kproj || !M || !seq_len || !workspace) return SJSA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(Kproj, 16) || !aligned(M, 16) || !aligned(seq_len, 4) ||
       !aligned(workspace, WS_ALIGN))
     return SJSA_ERR_ALIGN;
-  const Layout L = make_layout(*shape, 1);
+  const Layout L = make_layout(*shape, k);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, ws, s);
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s);
   if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
   return status_of(e);
 }
 
-int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, void* workspace, size_t workspace_bytes,
-              void* stream) {
+int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, const void* Kproj, const int32_t* seq_len,
+              int32_t k, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st) return st;
-  if (!q || !M || !workspace) return SJSA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(M, 16) || !aligned(workspace, WS_ALIGN)) return SJSA_ERR_ALIGN;
-  const Layout L = make_layout(*shape, 1);
+  if ((st = check_k(k))) return st;
+  if (!q || !M || !Kproj || !seq_len || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(M, 16) || !aligned(Kproj, 16) || !aligned(seq_len, 4) ||
+      !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, k);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
-  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (unsigned char*)workspace, (hipStream_t)stream));
+  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k,
+                               (unsigned char*)workspace, (hipStream_t)stream));
 }
 
 int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
@@ -154,17 +165,18 @@ int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len
                                 (hipStream_t)stream));
 }
 
-int sjsa_select(const sjsa_shape* shape, const int32_t* seq_len, int32_t k, int32_t* idx,
+int sjsa_select(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, int32_t k, int32_t* idx,
                 void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st) return st;
   if ((st = check_k(k))) return st;
-  if (!seq_len || !idx || !workspace) return SJSA_ERR_NULL;
-  if (!aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(workspace, WS_ALIGN)) return SJSA_ERR_ALIGN;
+  if (!Kproj || !seq_len || !idx || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(Kproj, 16) || !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
   const Layout L = make_layout(*shape, k);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
-  return status_of(launch_select(*shape, L, nullptr, 0, seq_len, k, idx, (unsigned char*)workspace,
-                                 (hipStream_t)stream));
+  return status_of(launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx,
+                                 (unsigned char*)workspace, (hipStream_t)stream));
 }
 
 int sjsa_topk(const sjsa_shape* shape, const float* scores, int64_t score_stride, const int32_t* seq_len,
@@ -177,9 +189,9 @@ int sjsa_topk(const sjsa_shape* shape, const float* scores, int64_t score_stride
   if (!aligned(scores, 16) || !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(workspace, WS_ALIGN))
     return SJSA_ERR_ALIGN;
   const Layout L = make_layout(*shape, k);
-  if (workspace_bytes < L.off_scores) return SJSA_ERR_WORKSPACE;
-  return status_of(launch_select(*shape, L, scores, score_stride, seq_len, k, idx, (unsigned char*)workspace,
-                                 (hipStream_t)stream));
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  return status_of(launch_select(*shape, L, scores, score_stride, nullptr, seq_len, k, idx,
+                                 (unsigned char*)workspace, (hipStream_t)stream));
 }
 
 int sjsa_attend(const sjsa_shape* shape, const void* q, const void* K, const void* V, const int32_t* idx,
@@ -217,9 +229,9 @@ int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, cons
   if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, ws, s);
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s);
   if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
-  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, seq_len, k, idx, ws, s);
+  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx, ws, s);
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
                       resolve_scale(sm_scale), out, ws, s);

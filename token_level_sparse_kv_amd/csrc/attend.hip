@@ -14,8 +14,9 @@
 // online softmax (running max m, sum l, accumulator acc) per query head, in the
 // exp2 domain with q pre-scaled by sm_scale*log2(e). Slots are combined in LDS;
 // with one split the workgroup writes the output directly, otherwise it writes its
-// (m, l, acc) partial and merge_kernel (one workgroup per unit, launched next on the
-// same stream) combines the partials in split order with a log-sum-exp merge.
+// (m, l, acc) partial and merge_kernel (one workgroup per (unit, query head),
+// launched next on the same stream) combines the partials in split order with a
+// log-sum-exp merge.
 #include "sjsa_device.h"
 #include "sjsa_internal.h"
 
@@ -24,16 +25,17 @@ namespace {
 
 constexpr int ATT_THREADS = 256;
 constexpr int SLOTS = ATT_THREADS / 16;
-constexpr int U = 4;                 // rows in flight per slot
+constexpr int ATT_U = 4;             // rows in flight per slot
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <int G>
-__global__ __launch_bounds__(ATT_THREADS) void attend_kernel(
+template <int G, int U>
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ seq_len, int n_kv_heads, int64_t cap,
     int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
     void* __restrict__ out, int out_f32) {
   __shared__ int32_t sidx[1024];
+  __shared__ float sq[G][HEAD_DIM];
   __shared__ float sm_m[SLOTS][G];
   __shared__ float sm_l[SLOTS][G];
   __shared__ float sm_acc[SLOTS][G][HEAD_DIM];
@@ -51,15 +53,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(
   const int32_t* ids = idx + (size_t)unit * k + first;
   for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
 
-  float qv[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const u32x4 w = ld16(q + ((size_t)unit * G + g) * HEAD_DIM + t * 8);
-    qv[g][0] = bf_lo(w.x) * qscale; qv[g][1] = bf_hi(w.x) * qscale;
-    qv[g][2] = bf_lo(w.y) * qscale; qv[g][3] = bf_hi(w.y) * qscale;
-    qv[g][4] = bf_lo(w.z) * qscale; qv[g][5] = bf_hi(w.z) * qscale;
-    qv[g][6] = bf_lo(w.w) * qscale; qv[g][7] = bf_hi(w.w) * qscale;
-  }
+  // query heads, pre-scaled into the exp2 domain, kept in LDS (read per use: fewer
+  // registers, more waves in flight)
+  for (int i = tid; i < G * HEAD_DIM; i += ATT_THREADS)
+    sq[i / HEAD_DIM][i % HEAD_DIM] = __uint_as_float((uint32_t)q[(size_t)unit * G * HEAD_DIM + i] << 16) * qscale;
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -74,50 +71,66 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(
   const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + t * 8;
 
   for (int base = slot * U; base < cnt; base += SLOTS * U) {
-    int64_t j[U];
+    int32_t j[U];
     bool ok[U];
     u32x4 kw[U], vw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = base + u;
-      j[u] = i < cnt ? (int64_t)sidx[i] : -1;
-      ok[u] = j[u] >= 0 && j[u] < n;
+      j[u] = i < cnt ? sidx[i] : -1;
+      ok[u] = j[u] >= 0 && (int64_t)j[u] < n;
     }
     // loads are unconditional (an invalid entry reads row 0, which always exists, and
     // gets zero weight), so the compiler can keep every load of the batch in flight
 #pragma unroll
-    for (int u = 0; u < U; ++u) kw[u] = ld16(Kb + (ok[u] ? j[u] : 0) * HEAD_DIM);
+    for (int u = 0; u < U; ++u) kw[u] = ld16(Kb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
 #pragma unroll
-    for (int u = 0; u < U; ++u) vw[u] = ld16(Vb + (ok[u] ? j[u] : 0) * HEAD_DIM);
+    for (int u = 0; u < U; ++u) vw[u] = ld16(Vb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
 
+    // logits: per query head, its q slice is read from LDS once and dotted with the U
+    // packed K rows (bf16 unpacked on the fly: a shift or a mask); the reduction runs
+    // for every row (a DPP row is one slot) and invalid rows are masked afterwards
+    float z[U][G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float z[U];
-      float mx = m[g];
+      float qv[8];
+      *reinterpret_cast<f32x4*>(&qv[0]) = *reinterpret_cast<const f32x4*>(&sq[g][t * 8]);
+      *reinterpret_cast<f32x4*>(&qv[4]) = *reinterpret_cast<const f32x4*>(&sq[g][t * 8 + 4]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        z[u] = row16_sum(dot8_bf16(qv[g], kw[u]));
-        z[u] = ok[u] ? z[u] : -INFINITY;
-        mx = fmaxf(mx, z[u]);
+        const float a = row16_sum(dot8_bf16(qv, kw[u]));
+        z[u][g] = ok[u] ? a : -INFINITY;
       }
-      if (mx == -INFINITY) continue;          // nothing valid yet for this head
-      const float sc = exp2f(m[g] - mx);     // 0 when m was -inf
-      float p[U];
+    }
+    // online softmax update, branch free: with no valid logit yet (mx = -inf) the
+    // reference point is 0, so every weight and the rescale factor come out 0
+    float p[U][G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, z[u][g]);
+      const float ref = mx == -INFINITY ? 0.f : mx;
+      const float sc = exp2f(m[g] - ref);
       float ps = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) { p[u] = exp2f(z[u] - mx); ps += p[u]; }
-      l[g] = l[g] * sc + ps;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = acc[g][e] * sc;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t word = (e >> 1) == 0 ? vw[u].x : (e >> 1) == 1 ? vw[u].y : (e >> 1) == 2 ? vw[u].z : vw[u].w;
-          a = fmaf(p[u], (e & 1) ? bf_hi(word) : bf_lo(word), a);
-        }
-        acc[g][e] = a;
-      }
+      for (int u = 0; u < U; ++u) { p[u][g] = exp2f(z[u][g] - ref); ps += p[u][g]; }
+      l[g] = fmaf(l[g], sc, ps);
       m[g] = mx;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] *= sc;
+    }
+    // weighted V rows: each V row is unpacked once and added into the G accumulators
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      vf[0] = bf_lo(vw[u].x); vf[1] = bf_hi(vw[u].x); vf[2] = bf_lo(vw[u].y); vf[3] = bf_hi(vw[u].y);
+      vf[4] = bf_lo(vw[u].z); vf[5] = bf_hi(vw[u].z); vf[6] = bf_lo(vw[u].w); vf[7] = bf_hi(vw[u].w);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
+      }
     }
   }
 
@@ -160,34 +173,45 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(
   }
 }
 
-// One workgroup per unit: combine the nsplit partials of every query head in split
-// order. m_s are running maxima in the exp2 domain; l_s the sums; acc_s the
-// unnormalized outputs: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Combine the nsplit partials of one (unit, query head) in split order; one thread
+// per output dim. Partial s holds the running maximum m_s (exp2 domain), the sum
+// l_s and the unnormalized output acc_s; the merge keeps a running (m, l, acc)
+// and rescales by 2^(m_old - m_new) as each partial comes in (log-sum-exp merge),
+// then out = acc / l.
 template <int G>
-__global__ __launch_bounds__(ATT_THREADS) void merge_kernel(const float* __restrict__ partials, int nsplit,
-                                                            void* __restrict__ out, int out_f32) {
-  const int unit = blockIdx.x;
-  const float* pu = partials + (size_t)unit * nsplit * G * PART_STRIDE;
-  for (int o = threadIdx.x; o < G * HEAD_DIM; o += ATT_THREADS) {
-    const int g = o / HEAD_DIM, dim = o - g * HEAD_DIM;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pu[((size_t)s * G + g) * PART_STRIDE + HEAD_DIM]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* ps = pu + ((size_t)s * G + g) * PART_STRIDE;
-        const float ms = ps[HEAD_DIM];
-        if (ms == -INFINITY) continue;
-        const float w = exp2f(ms - M);
-        L = fmaf(ps[HEAD_DIM + 1], w, L);
-        A = fmaf(ps[dim], w, A);
-      }
+__global__ __launch_bounds__(HEAD_DIM) void merge_kernel(const float* __restrict__ partials, int nsplit,
+                                                         void* __restrict__ out, int out_f32) {
+  constexpr int MU = 8;
+  const int unit = blockIdx.x / G;
+  const int g = blockIdx.x - unit * G;
+  const int dim = threadIdx.x;
+  const float* pu = partials + ((size_t)unit * nsplit * G + g) * PART_STRIDE;
+  const size_t sstride = (size_t)G * PART_STRIDE;
+  float m = -INFINITY, l = 0.f, a = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += MU) {
+    float ms[MU], ls[MU], as[MU];
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int s = min(s0 + u, nsplit - 1);
+      const float* ps = pu + (size_t)s * sstride;
+      ms[u] = s0 + u < nsplit ? ps[HEAD_DIM] : -INFINITY;
+      ls[u] = ps[HEAD_DIM + 1];
+      as[u] = ps[dim];
     }
-    const float r = L > 0.f ? A / L : 0.f;
-    const size_t oi = ((size_t)unit * G + g) * HEAD_DIM + dim;
-    if (out_f32) reinterpret_cast<float*>(out)[oi] = r;
-    else reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const float mn = fmaxf(m, ms[u]);
+      const float ref = mn == -INFINITY ? 0.f : mn;
+      const float so = exp2f(m - ref), sn = exp2f(ms[u] - ref);
+      l = fmaf(l, so, ls[u] * sn);
+      a = fmaf(a, so, as[u] * sn);
+      m = mn;
+    }
   }
+  const float r = l > 0.f ? a / l : 0.f;
+  const size_t oi = ((size_t)unit * G + g) * HEAD_DIM + dim;
+  if (out_f32) reinterpret_cast<float*>(out)[oi] = r;
+  else reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
 }
 
 }  // namespace
@@ -200,9 +224,9 @@ hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q
   const int out_f32 = (s.flags & SJSA_FLAG_OUT_F32) ? 1 : 0;
   const dim3 grid((unsigned)L.nsplit, (unsigned)L.units), block(ATT_THREADS);
 #define SJSA_ATT(GG)                                                                              \
-  attend_kernel<GG><<<grid, block, 0, st>>>(q, K, V, idx, seq_len, s.n_kv_heads, s.capacity, k,   \
+  attend_kernel<GG, ATT_U><<<grid, block, 0, st>>>(q, K, V, idx, seq_len, s.n_kv_heads, s.capacity, k,   \
                                             L.chunk, L.nsplit, qscale, partials, out, out_f32);   \
-  if (L.nsplit > 1) merge_kernel<GG><<<dim3((unsigned)L.units), block, 0, st>>>(partials, L.nsplit, out, out_f32)
+  if (L.nsplit > 1) merge_kernel<GG><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32)
   switch (s.group) {
     case 1: SJSA_ATT(1); break;
     case 2: SJSA_ATT(2); break;

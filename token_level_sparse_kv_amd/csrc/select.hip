@@ -1,4 +1,4 @@
-// Per-(sequence, KV head) top-k selection over the fp32 scores.
+// Per-(sequence, KV head) top-k selection.
 //
 // Source: JSSA article, section JSSA 的整体结构 (top-k token positions per KV head,
 // shared by its query heads) and section 组件级拆解 (top-k selection is the stage
@@ -6,19 +6,25 @@
 // the lower position; -0 equals +0; NaN ranks below everything. Output: the
 // min(k, n) selected positions in ascending order, then -1.
 //
-// One 1024-thread workgroup per unit, working on order-preserving u32 keys:
-//  1. First radix digit (top 12 key bits): the histogram comes from the score
-//     kernel (or is built here in one pass). A block scan finds the bin b1 that
-//     holds the k-th largest key: cntA keys lie in higher bins, cntC in b1.
-//  2. Fast path (cntA <= A_CAP, cntC <= C_CAP): one ordered pass over the scores
-//     compacts the positions above b1 (list A) and the (key, position) pairs in b1
-//     (list C) into LDS, in position order, with wavefront ballots. The rest is
-//     LDS-only: two 10-bit radix rounds over C give the exact threshold key T and
-//     how many keys equal to T are taken (the lowest positions first); C is
-//     compacted to the selected positions, and A and C are merged by rank.
-//  3. Fallback (large k or a degenerate score distribution): the remaining two
-//     digits are resolved by histogram passes over the scores, then one ordered
-//     ballot-compaction pass writes the result directly.
+// Scores are compared as order-preserving u32 keys. One 1024-thread workgroup per
+// unit, three paths:
+//  * take-all: k >= n, positions 0..n-1.
+//  * candidates (the usual case): the scan kept, per 1024-row segment and in
+//    position order, every row whose key reached the unit's sampled threshold.
+//    If their count c satisfies k <= c <= CAND_CAP, the exact top k is among
+//    them: the segments are gathered into LDS in order, three radix rounds
+//    (12 + 10 + 10 bits) find the exact k-th key T and how many keys equal to T
+//    are taken (lowest positions first), and one ordered ballot compaction writes
+//    the ascending result.
+//  * dense: exact selection over a full score row. Used for caller-provided
+//    scores, and when the sampled threshold misjudged the distribution (fewer than
+//    k candidates, or more than fit in LDS); the unit's scores are then recomputed
+//    first with arithmetic bit-identical to the scan's. The first radix digit's
+//    histogram locates the bin b1 of the k-th key; one ordered pass compacts the
+//    positions above b1 (list A) and the (key, position) pairs in b1 (list C) into
+//    LDS; C is resolved exactly and merged with A by rank. If A or C would not fit,
+//    the remaining digits are resolved by passes over the row and a final ordered
+//    pass writes the result.
 #include "sjsa_device.h"
 #include "sjsa_internal.h"
 
@@ -29,17 +35,19 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int EPT = 4;                          // consecutive positions per thread (one float4)
 constexpr int SUB = SEL_THREADS * EPT;          // positions per sub-chunk
-constexpr int SUPER = 4;                        // sub-chunks loaded ahead together
-constexpr int A_CAP = 8192;
+constexpr int STEPS = 4;                        // float4 loads per lane per super-chunk
+constexpr int WAVE_SPAN = STEPS * 64 * EPT;     // contiguous positions per wave per super-chunk
+constexpr int SUPER_SPAN = SEL_WAVES * WAVE_SPAN;
+constexpr int LDS_WORDS = 32768;                // list storage (128 KB)
+constexpr int A_CAP = 8192;                     // dense path: listA | ckey | cpos
 constexpr int C_CAP = 12288;
+constexpr int CAND_CAP = LDS_WORDS / 2;         // candidate path: ckey | cpos
+static_assert(A_CAP + 2 * C_CAP == LDS_WORDS, "dense lists fill the list storage");
 
 struct SelShared {
   uint32_t hist[HIST_BINS];
-  int32_t listA[A_CAP];
-  uint32_t ckey[C_CAP];
-  int32_t cpos[C_CAP];
-  uint32_t wtot[2][SEL_WAVES];
-  uint32_t wcnt[2][2][SUPER][SEL_WAVES];   // [buffer][list A/C][sub-chunk][wave]
+  uint32_t buf[LDS_WORDS];
+  uint32_t wtot[2][2 * SEL_WAVES];   // [buffer][A totals of waves | C totals of waves]
   uint32_t scan[SEL_WAVES];
   int32_t misc[8];
 };
@@ -63,9 +71,9 @@ __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
   return inc + before;
 }
 
-// Given a histogram of `nbins` bins (LDS) and need >= 1, find the bin b with
-// count(bins > b) < need <= count(bins >= b). Results go to misc[0] (bin) and
-// misc[1] (count above the bin), misc[2] (count in the bin). All threads call.
+// Given a histogram of `nbins` bins (LDS) and 1 <= need <= total count, find the bin
+// b with count(bins > b) < need <= count(bins >= b). Results: misc[0] = b,
+// misc[1] = count above b, misc[2] = count in b. All threads call.
 __device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, SelShared& sh) {
   const int per = nbins / SEL_THREADS;         // 4 or 1 bins per thread
   const int lo = threadIdx.x * per;
@@ -73,8 +81,7 @@ __device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, SelS
   for (int i = 0; i < per; ++i) local += hist[lo + i];
   uint32_t total;
   const uint32_t inc = block_incl_scan(local, sh.scan, &total);
-  // keys in bins above this thread's range
-  uint32_t above = total - inc;
+  uint32_t above = total - inc;                // keys in bins above this thread's range
   if (above < need && need <= above + local) {
     for (int i = per - 1; i >= 0; --i) {
       const uint32_t c = hist[lo + i];
@@ -91,17 +98,17 @@ __device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, SelS
 }
 
 // Unconditional float4 load of positions pos..pos+3 of a score row: positions at or
-// past n are clamped to the last float4 that starts inside the row (the row is
-// allocated up to a multiple of 4), and callers mask them out. Keeping every load
-// unconditional lets the compiler overlap a whole batch of them.
+// past n are clamped to the last float4 that starts inside the row (rows are
+// allocated up to a multiple of 4) and are masked by the callers. Keeping every
+// load unconditional lets the compiler overlap a whole batch of them.
 __device__ __forceinline__ f32x4 load4(const float* row, int64_t pos, int64_t last4) {
   return *reinterpret_cast<const f32x4*>(row + min(pos, last4));
 }
 
 // Ordered compaction helper: ranks of the flagged elements of one sub-chunk (each
 // thread holds EPT consecutive positions; lanes, then waves, are in position order).
-// Returns this thread's first output slot relative to the sub-chunk start for the
-// flag vector `f`, and the sub-chunk total through wave totals in wtot[which].
+// Returns this thread's first output slot relative to the sub-chunk start and the
+// sub-chunk total (through per-wave totals in wtot_row). One barrier.
 __device__ __forceinline__ uint32_t ballot_rank(const bool (&f)[EPT], uint32_t* wtot_row, uint32_t* total) {
   const int wave = threadIdx.x >> 6;
   const uint64_t lt = lanemask_lt();
@@ -125,36 +132,98 @@ __device__ __forceinline__ uint32_t ballot_rank(const bool (&f)[EPT], uint32_t* 
   return before + below;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(
-    const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
-    int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx,
-    uint32_t* __restrict__ ghist, int have_hist) {
-  __shared__ SelShared sh;
-  const int unit = blockIdx.x;
-  const int b = unit / n_kv_heads;
+// Exact resolution of the threshold inside an LDS key list: the keys all share the
+// bits selected by `mask` (value `prefix`); `need` of them are to be taken. The
+// remaining bits are resolved 10 at a time (after an optional 12-bit first round).
+// Returns T; *needT receives how many keys equal to T are taken.
+__device__ uint32_t lds_threshold(const uint32_t* keys, int cnt, uint32_t prefix, uint32_t mask, uint32_t need,
+                                  bool first12, SelShared& sh, uint32_t* needT) {
   const int tid = threadIdx.x;
-  const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
-  const int kk = (int)min((int64_t)k, n);
-  int32_t* out = idx + (size_t)unit * k;
-  const float* row = scores + (size_t)unit * stride;
-
-  for (int i = kk + tid; i < k; i += SEL_THREADS) out[i] = -1;
-  if (kk == 0) return;
-  const int64_t last4 = ((n - 1) >> 2) << 2;     // last float4 start inside the row
-
-  // ---- first digit: histogram of the top 12 key bits
-  if (have_hist) {
-    const uint32_t* gh = ghist + (size_t)unit * HIST_BINS;
-    for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = gh[i];
-  } else {
-    for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
+  const int nrounds = first12 ? 3 : 2;
+  for (int round = 0; round < nrounds; ++round) {
+    const bool big = first12 && round == 0;
+    const int shift = big ? 20 : (round == nrounds - 1 ? 0 : 10);
+    const int nb = big ? HIST_BINS : 1024;
+    for (int i = tid; i < nb; i += SEL_THREADS) sh.hist[i] = 0u;
     __syncthreads();
-    for (int64_t c = (int64_t)tid * EPT; c < n; c += SUB) {
-      const f32x4 v = load4(row, c, last4);
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if (c + e < n) atomicAdd(&sh.hist[score_key(v[e]) >> HIST_SHIFT], 1u);
+    for (int i = tid; i < cnt; i += SEL_THREADS) {
+      const uint32_t key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
     }
+    __syncthreads();
+    find_bucket(sh.hist, nb, need, sh);
+    need -= (uint32_t)sh.misc[1];
+    prefix |= (uint32_t)sh.misc[0] << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+  }
+  *needT = need;
+  return prefix;
+}
+
+// Ordered compaction of an LDS (key, position) list in position order: keep keys
+// above T, and the first needT keys equal to T. With to_lds the kept positions are
+// written back into pos_l[] (in place); otherwise to out[]. Returns the kept count.
+__device__ uint32_t compact_list(const uint32_t* key_l, int32_t* pos_l, int cnt, uint32_t T, uint32_t needT,
+                                 bool take_all, bool to_lds, int32_t* out, SelShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t baseS = 0, baseEq = 0;
+  for (int c0 = 0; c0 < cnt; c0 += SUB) {
+    const int i0 = c0 + tid * EPT;
+    bool sel[EPT], eq[EPT];
+    int32_t pos[EPT];
+    uint32_t key[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool valid = i0 + e < cnt;
+      key[e] = valid ? key_l[i0 + e] : 0u;
+      pos[e] = valid ? pos_l[i0 + e] : 0;
+      eq[e] = valid && !take_all && key[e] == T;
+    }
+    uint32_t totEq;
+    const uint32_t req = ballot_rank(eq, sh.wtot[0], &totEq);
+    uint32_t r = baseEq + req;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool valid = i0 + e < cnt;
+      if (take_all) sel[e] = valid;
+      else if (eq[e]) { sel[e] = r < needT; ++r; }
+      else sel[e] = valid && key[e] > T;
+    }
+    uint32_t totS;
+    const uint32_t rs = ballot_rank(sel, sh.wtot[1], &totS);
+    __syncthreads();     // every thread has read its entries before any is overwritten
+    uint32_t o = baseS + rs;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (sel[e]) {
+        if (to_lds) pos_l[o] = pos[e];
+        else out[o] = pos[e];
+        ++o;
+      }
+    }
+    baseS += totS;
+    baseEq += totEq;
+    __syncthreads();
+  }
+  return baseS;
+}
+
+// Exact top-kk of a dense score row of n >= kk >= 1 entries -> out[0..kk).
+__device__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, SelShared& sh) {
+  const int tid = threadIdx.x;
+  const int64_t last4 = ((n - 1) >> 2) << 2;     // last float4 start inside the row
+  int32_t* listA = reinterpret_cast<int32_t*>(sh.buf);
+  uint32_t* ckey = sh.buf + A_CAP;
+  int32_t* cpos = reinterpret_cast<int32_t*>(sh.buf + A_CAP + C_CAP);
+
+  // first digit: histogram of the top 12 key bits
+  for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
+  __syncthreads();
+  for (int64_t c = (int64_t)tid * EPT; c < n; c += SUB) {
+    const f32x4 v = load4(row, c, last4);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (c + e < n) atomicAdd(&sh.hist[score_key(v[e]) >> HIST_SHIFT], 1u);
   }
   __syncthreads();
   find_bucket(sh.hist, HIST_BINS, (uint32_t)kk, sh);
@@ -164,159 +233,110 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   uint32_t need = (uint32_t)(kk - cntA);          // 1 <= need <= cntC
 
   if (cntA <= A_CAP && cntC <= C_CAP) {
-    // ---- fast path, pass A: ordered compaction of lists A and C into LDS.
-    // A super-chunk is SUPER sub-chunks of SUB positions; in sub-chunk s thread t holds
-    // positions c0 + s*SUB + 4t .. +3, so position order is (s, wave, lane, e). Each
-    // wave publishes its A and C counts per sub-chunk (double-buffered, one barrier
-    // per super-chunk); every thread then derives its output slots. The next
+    // Pass A: ordered compaction of lists A and C into LDS. A super-chunk is
+    // SEL_WAVES * WAVE_SPAN positions; wave w owns the contiguous range
+    // c0 + w*WAVE_SPAN .. +WAVE_SPAN, read as STEPS coalesced float4 loads per lane
+    // (step i, lane l: positions +i*256 + 4l .. +3). Inside a wave, ballots give each
+    // flagged element its rank in position order (step, lane, e); across waves the
+    // per-wave totals are published once per super-chunk (double-buffered, one
+    // barrier) and scanned by a DPP row scan read back with readlane. The next
     // super-chunk's loads are in flight while the current one is classified.
     uint32_t baseA = 0, baseC = 0;
     const int lane = tid & 63, wave = tid >> 6;
     const uint64_t lt = lanemask_lt();
-    f32x4 cur[SUPER];
+    f32x4 cur[STEPS];
 #pragma unroll
-    for (int s = 0; s < SUPER; ++s) cur[s] = load4(row, (int64_t)s * SUB + tid * EPT, last4);
+    for (int i = 0; i < STEPS; ++i) cur[i] = load4(row, (int64_t)wave * WAVE_SPAN + i * 256 + lane * EPT, last4);
     int it = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)SUPER * SUB, ++it) {
-      f32x4 nxt[SUPER];
+    for (int64_t c0 = 0; c0 < n; c0 += SUPER_SPAN, ++it) {
+      const int64_t wbase = c0 + (int64_t)wave * WAVE_SPAN;
+      f32x4 nxt[STEPS];
 #pragma unroll
-      for (int s = 0; s < SUPER; ++s) nxt[s] = load4(row, c0 + (int64_t)(SUPER + s) * SUB + tid * EPT, last4);
+      for (int i = 0; i < STEPS; ++i) nxt[i] = load4(row, wbase + SUPER_SPAN + i * 256 + lane * EPT, last4);
       const int buf = it & 1;
-      uint32_t key[SUPER][EPT];
-      uint32_t fa[SUPER], fc[SUPER];                 // flag bits per element e
-      uint32_t ra[SUPER], rc[SUPER];                 // flagged elements in lower lanes
+      uint32_t key[STEPS][EPT];
+      uint32_t fa[STEPS], fc[STEPS];      // flag bits per element e
+      uint32_t ra[STEPS], rc[STEPS];      // rank of this lane's first flagged element within the wave
+      uint32_t wa = 0u, wc = 0u;          // wave totals so far
 #pragma unroll
-      for (int s = 0; s < SUPER; ++s) {
-        const int64_t p0 = c0 + (int64_t)s * SUB + tid * EPT;
-        fa[s] = 0u;
-        fc[s] = 0u;
-        ra[s] = 0u;
-        rc[s] = 0u;
-        uint32_t wa = 0u, wc = 0u;
+      for (int i = 0; i < STEPS; ++i) {
+        const int64_t p0 = wbase + i * 256 + lane * EPT;
+        fa[i] = 0u;
+        fc[i] = 0u;
+        uint32_t la = 0u, lc = 0u, sa = 0u, sc = 0u;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-          key[s][e] = score_key(cur[s][e]);
-          const uint32_t bin = key[s][e] >> HIST_SHIFT;
+          key[i][e] = score_key(cur[i][e]);
+          const uint32_t bin = key[i][e] >> HIST_SHIFT;
           const bool valid = p0 + e < n;
           const bool a = valid && bin > b1;
           const bool c = valid && bin == b1;
-          fa[s] |= (uint32_t)a << e;
-          fc[s] |= (uint32_t)c << e;
+          fa[i] |= (uint32_t)a << e;
+          fc[i] |= (uint32_t)c << e;
           const uint64_t ma = __ballot(a), mc = __ballot(c);
-          ra[s] += __popcll(ma & lt);
-          rc[s] += __popcll(mc & lt);
-          wa += __popcll(ma);
-          wc += __popcll(mc);
+          la += __popcll(ma & lt);
+          lc += __popcll(mc & lt);
+          sa += __popcll(ma);
+          sc += __popcll(mc);
         }
-        if (lane == 0) { sh.wcnt[buf][0][s][wave] = wa; sh.wcnt[buf][1][s][wave] = wc; }
+        ra[i] = wa + la;
+        rc[i] = wc + lc;
+        wa += sa;
+        wc += sc;
       }
+      if (lane == 0) { sh.wtot[buf][wave] = wa; sh.wtot[buf][SEL_WAVES + wave] = wc; }
       __syncthreads();
+      // lanes 0..15 scan the A totals of waves 0..15, lanes 16..31 the C totals
+      const uint32_t scan = row16_incl_scan(lane < 32 ? sh.wtot[buf][lane] : 0u);
+      const uint32_t totA = __builtin_amdgcn_readlane(scan, 15);
+      const uint32_t totC = __builtin_amdgcn_readlane(scan, 31);
+      const uint32_t beforeA = wave == 0 ? 0u : __builtin_amdgcn_readlane(scan, wave - 1);
+      const uint32_t beforeC = wave == 0 ? 0u : __builtin_amdgcn_readlane(scan, 16 + wave - 1);
 #pragma unroll
-      for (int s = 0; s < SUPER; ++s) {
-        uint32_t beforeA = 0, beforeC = 0, totA = 0, totC = 0;
-#pragma unroll
-        for (int w = 0; w < SEL_WAVES; ++w) {
-          const uint32_t xa = sh.wcnt[buf][0][s][w], xc = sh.wcnt[buf][1][s][w];
-          beforeA += (w < wave) ? xa : 0u;
-          beforeC += (w < wave) ? xc : 0u;
-          totA += xa;
-          totC += xc;
-        }
-        uint32_t oa = baseA + beforeA + ra[s], oc = baseC + beforeC + rc[s];
-        const int64_t p0 = c0 + (int64_t)s * SUB + tid * EPT;
+      for (int i = 0; i < STEPS; ++i) {
+        uint32_t oa = baseA + beforeA + ra[i], oc = baseC + beforeC + rc[i];
+        const int64_t p0 = wbase + i * 256 + lane * EPT;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-          if ((fa[s] >> e) & 1u) { if (oa < A_CAP) sh.listA[oa] = (int32_t)(p0 + e); ++oa; }
-          if ((fc[s] >> e) & 1u) {
-            if (oc < C_CAP) { sh.ckey[oc] = key[s][e]; sh.cpos[oc] = (int32_t)(p0 + e); }
+          if ((fa[i] >> e) & 1u) { if (oa < A_CAP) listA[oa] = (int32_t)(p0 + e); ++oa; }
+          if ((fc[i] >> e) & 1u) {
+            if (oc < C_CAP) { ckey[oc] = key[i][e]; cpos[oc] = (int32_t)(p0 + e); }
             ++oc;
           }
         }
-        baseA += totA;
-        baseC += totC;
       }
+      baseA += totA;
+      baseC += totC;
 #pragma unroll
-      for (int s = 0; s < SUPER; ++s) cur[s] = nxt[s];
+      for (int i = 0; i < STEPS; ++i) cur[i] = nxt[i];
     }
     __syncthreads();
 
-    // ---- resolve the threshold inside list C (LDS only)
-    uint32_t T = 0;
-    uint32_t needT = need;                 // keys equal to T to take (lowest positions)
-    const bool take_all_c = (need == (uint32_t)cntC);
-    if (!take_all_c) {
-      uint32_t prefix = 0;                 // resolved bits 19..10 (as a 10-bit digit)
-      for (int round = 0; round < 2; ++round) {
-        const int shift = round == 0 ? 10 : 0;
-        for (int i = tid; i < 1024; i += SEL_THREADS) sh.hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < cntC; i += SEL_THREADS) {
-          const uint32_t key = sh.ckey[i];
-          if (round == 0 || ((key >> 10) & 1023u) == prefix) atomicAdd(&sh.hist[(key >> shift) & 1023u], 1u);
-        }
-        __syncthreads();
-        find_bucket(sh.hist, 1024, needT, sh);
-        const uint32_t d = (uint32_t)sh.misc[0];
-        needT -= (uint32_t)sh.misc[1];
-        if (round == 0) prefix = d;
-        else T = (b1 << HIST_SHIFT) | (prefix << 10) | d;
-      }
-    }
-
-    // ---- compact C in place to the selected positions (position order kept)
-    uint32_t baseS = 0, baseEq = 0;
-    for (int c0 = 0; c0 < cntC; c0 += SUB) {
-      const int i0 = c0 + tid * EPT;
-      bool sel[EPT], eq[EPT];
-      int32_t pos[EPT];
-      uint32_t key[EPT];
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const bool valid = i0 + e < cntC;
-        key[e] = valid ? sh.ckey[i0 + e] : 0u;
-        pos[e] = valid ? sh.cpos[i0 + e] : 0;
-        eq[e] = valid && !take_all_c && key[e] == T;
-      }
-      uint32_t totEq;
-      const uint32_t req = ballot_rank(eq, sh.wtot[0], &totEq);
-      uint32_t r = baseEq + req;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const bool valid = i0 + e < cntC;
-        if (take_all_c) sel[e] = valid;
-        else if (eq[e]) { sel[e] = r < needT; ++r; }
-        else sel[e] = valid && key[e] > T;
-      }
-      uint32_t totS;
-      const uint32_t rs = ballot_rank(sel, sh.wtot[1], &totS);
-      __syncthreads();     // every thread has read its C entries before any is overwritten
-      uint32_t o = baseS + rs;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if (sel[e]) { if (o < C_CAP) sh.cpos[o] = pos[e]; ++o; }
-      baseS += totS;
-      baseEq += totEq;
-      __syncthreads();
-    }
+    // resolve the threshold inside list C (LDS only) and keep the selected C entries
+    const bool take_all_c = need == (uint32_t)cntC;
+    uint32_t T = 0, needT = need;
+    if (!take_all_c)
+      T = lds_threshold(ckey, cntC, b1 << HIST_SHIFT, 0xfff00000u, need, false, sh, &needT);
+    compact_list(ckey, cpos, cntC, T, needT, take_all_c, true, nullptr, sh);
     const int nS = kk - cntA;
 
-    // ---- merge lists A (cntA) and C-selected (nS), both ascending, by rank
+    // merge lists A (cntA) and C-selected (nS), both ascending, by rank
     for (int i = tid; i < cntA; i += SEL_THREADS) {
-      const int32_t x = sh.listA[i];
+      const int32_t x = listA[i];
       int lo = 0, hi = nS;
-      while (lo < hi) { const int mid = (lo + hi) >> 1; if (sh.cpos[mid] < x) lo = mid + 1; else hi = mid; }
+      while (lo < hi) { const int mid = (lo + hi) >> 1; if (cpos[mid] < x) lo = mid + 1; else hi = mid; }
       if (i + lo < kk) out[i + lo] = x;
     }
     for (int i = tid; i < nS; i += SEL_THREADS) {
-      const int32_t x = sh.cpos[i];
+      const int32_t x = cpos[i];
       int lo = 0, hi = cntA;
-      while (lo < hi) { const int mid = (lo + hi) >> 1; if (sh.listA[mid] < x) lo = mid + 1; else hi = mid; }
+      while (lo < hi) { const int mid = (lo + hi) >> 1; if (listA[mid] < x) lo = mid + 1; else hi = mid; }
       if (i + lo < kk) out[i + lo] = x;
     }
     return;
   }
 
-  // ---- fallback: resolve the lower 20 bits with passes over the scores
+  // the lists would not fit: resolve the lower 20 bits with passes over the row
   uint32_t prefix = b1 << HIST_SHIFT;
   uint32_t mask = 0xfff00000u;
   for (int round = 0; round < 2; ++round) {
@@ -362,24 +382,150 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint32_t rs = ballot_rank(sel, sh.wtot[1], &totS);
     uint32_t o = baseS + rs;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
+    for (int e = 0; e < EPT; ++e) {
       if (sel[e]) { if (o < (uint32_t)kk) out[o] = (int32_t)(p0 + e); ++o; }
+    }
     baseS += totS;
     baseEq += totEq;
     __syncthreads();
   }
 }
 
+// Recompute a unit's dense scores (bit-identical to the scan) into row[0..n).
+template <int R>
+__device__ void recompute_scores(const uint16_t* kproj_unit, const float* qhat_unit, int64_t n, float* row) {
+  float q[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) q[i] = qhat_unit[i];
+  for (int64_t j = threadIdx.x; j < n; j += SEL_THREADS) row[j] = row_score<R>(q, kproj_unit + j * R);
+  __syncthreads();
+}
+
+// grid = B * H_kv. scores != nullptr: dense selection over caller scores (stride
+// `stride`). Otherwise: take-all, candidate path, or recompute + dense selection.
+template <int R>
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(
+    const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
+    int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const uint16_t* __restrict__ kproj,
+    const float* __restrict__ qhat, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ counts,
+    float* __restrict__ dense, int64_t dense_stride, int64_t nseg_cap, int64_t cand_stride) {
+  __shared__ SelShared sh;
+  const int unit = blockIdx.x;
+  const int b = unit / n_kv_heads;
+  const int tid = threadIdx.x;
+  const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
+  const int kk = (int)min((int64_t)k, n);
+  int32_t* out = idx + (size_t)unit * k;
+
+  for (int i = kk + tid; i < k; i += SEL_THREADS) out[i] = -1;
+  if (kk == 0) return;
+  if (scores != nullptr) {
+    select_dense(scores + (size_t)unit * stride, n, kk, out, sh);
+    return;
+  }
+  if ((int64_t)kk == n) {
+    for (int i = tid; i < kk; i += SEL_THREADS) out[i] = i;
+    return;
+  }
+
+  // Gather the candidates into LDS in position order. The scan packed them per
+  // (tile, wave): segment s (tile t = s / SEGS_PER_TILE, j = s % SEGS_PER_TILE, wave
+  // j % 4, i-th segment of that wave for i = j / 4) starts at entry
+  // t*TILE_ROWS + (j % 4)*TILE_ROWS/4 + (counts of that wave's earlier segments).
+  // Per chunk of SEL_THREADS segments (whole tiles): a block scan of the counts gives
+  // each segment's output offset, a short sum its offset inside its wave's region
+  // (both kept in LDS, reusing the histogram words), then every thread copies
+  // entries of the chunk's flat range, finding the owning segment by binary search.
+  // The loads are unconditional (clamped into the range), so a batch stays in flight.
+  constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
+  constexpr int SCAN_WAVES = 4;
+  static_assert(SEL_THREADS % SEGS_PER_TILE == 0, "chunks hold whole tiles");
+  uint32_t* ckey = sh.buf;
+  int32_t* cpos = reinterpret_cast<int32_t*>(sh.buf + CAND_CAP);
+  uint32_t* segoff = sh.hist;                     // SEL_THREADS + 1 output offsets
+  uint32_t* segcnt = sh.hist + 2048;              // SEL_THREADS counts, then region offsets
+  const int64_t nseg = (n + SEG_ROWS - 1) / SEG_ROWS;
+  const uint32_t* cnt_u = counts + (size_t)unit * nseg_cap;
+  const uint64_t* cand_u = cand + (size_t)unit * cand_stride;
+  uint32_t total = 0;
+  for (int64_t s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
+    const int64_t sg = s0 + tid;
+    const int nchunk = (int)min((int64_t)SEL_THREADS, nseg - s0);
+    const uint32_t c = sg < nseg ? cnt_u[sg] : 0u;
+    uint32_t chunk_total;
+    const uint32_t incl = block_incl_scan(c, sh.scan, &chunk_total);
+    segoff[tid + 1] = incl;
+    if (tid == 0) segoff[0] = 0u;
+    segcnt[tid] = c;
+    __syncthreads();
+    // offset of this segment inside its wave's region, and the region's start
+    const int j = tid % SEGS_PER_TILE;
+    uint32_t roff = 0;
+    for (int jj = j % SCAN_WAVES; jj < j; jj += SCAN_WAVES) roff += segcnt[tid - j + jj];
+    const uint32_t src0 = (uint32_t)((s0 + tid) / SEGS_PER_TILE) * TILE_ROWS +
+                          (uint32_t)(j % SCAN_WAVES) * (TILE_ROWS / SCAN_WAVES) + roff;
+    __syncthreads();
+    segcnt[tid] = src0;
+    __syncthreads();
+    const uint32_t room = total < (uint32_t)CAND_CAP ? (uint32_t)CAND_CAP - total : 0u;
+    const uint32_t ncopy = min(chunk_total, room);
+    constexpr int GU = 4;
+    for (uint32_t f0 = 0; f0 < ncopy; f0 += SEL_THREADS * GU) {
+      uint64_t v[GU];
+      uint32_t dst[GU];
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const uint32_t f = min(f0 + (uint32_t)(u * SEL_THREADS + tid), ncopy - 1);
+        int lo = 0, hi = nchunk;                    // last segment with offset <= f
+        while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (segoff[mid] <= f) lo = mid; else hi = mid; }
+        v[u] = cand_u[segcnt[lo] + (f - segoff[lo])];
+        dst[u] = total + f;
+      }
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        if (f0 + (uint32_t)(u * SEL_THREADS + tid) < ncopy) {
+          ckey[dst[u]] = (uint32_t)(v[u] >> 32);
+          cpos[dst[u]] = (int32_t)(uint32_t)v[u];
+        }
+      }
+    }
+    total += chunk_total;
+    __syncthreads();
+  }
+
+  if (total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
+    uint32_t needT;
+    const uint32_t T = lds_threshold(ckey, (int)total, 0u, 0u, (uint32_t)kk, true, sh, &needT);
+    compact_list(ckey, cpos, (int)total, T, needT, false, false, out, sh);
+    return;
+  }
+  // the sampled threshold misjudged this unit: exact selection over recomputed scores
+  float* row = dense + (size_t)unit * dense_stride;
+  recompute_scores<R>(kproj + (size_t)unit * cap * R, qhat + (size_t)unit * QHAT_STRIDE, n, row);
+  select_dense(row, n, kk, out, sh);
+}
+
 }  // namespace
 
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
-                         const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws, hipStream_t st) {
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.off_hist);
-  const int have_hist = scores == nullptr ? 1 : 0;
-  const float* src = scores ? scores : reinterpret_cast<const float*>(ws + L.off_scores);
-  const int64_t sstride = scores ? stride : L.score_stride;
-  select_kernel<<<dim3((unsigned)L.units), dim3(SEL_THREADS), 0, st>>>(
-      src, sstride, seq_len, s.n_kv_heads, s.capacity, k, idx, hist, have_hist);
+                         const uint16_t* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
+                         hipStream_t st) {
+  const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
+  const uint64_t* cand = reinterpret_cast<const uint64_t*>(ws + L.off_cand);
+  const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + L.off_counts);
+  float* dense = reinterpret_cast<float*>(ws + L.off_scores);
+  const dim3 grid((unsigned)L.units), block(SEL_THREADS);
+#define SJSA_SEL(RR)                                                                                   \
+  select_kernel<RR><<<grid, block, 0, st>>>(scores, stride, seq_len, s.n_kv_heads, s.capacity, k, idx, \
+                                            kproj, qhat, cand, counts, dense, L.score_stride, L.nseg_cap,  \
+                                            L.cand_stride)
+  switch (s.rank) {
+    case 16: SJSA_SEL(16); break;
+    case 32: SJSA_SEL(32); break;
+    case 64: SJSA_SEL(64); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SJSA_SEL
   return hipGetLastError();
 }
 

@@ -66,6 +66,26 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+constexpr int DPP_ROW_SHR1 = 0x111;
+constexpr int DPP_ROW_SHR2 = 0x112;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_SHR8 = 0x118;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Inclusive prefix sum inside each DPP row of 16 lanes (lanes shifted in from
+// outside the row read 0).
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
+  v += dpp_u32<DPP_ROW_SHR1>(v);
+  v += dpp_u32<DPP_ROW_SHR2>(v);
+  v += dpp_u32<DPP_ROW_SHR4>(v);
+  v += dpp_u32<DPP_ROW_SHR8>(v);
+  return v;
+}
+
 // 128-bit global loads; the nontemporal form streams data that is read once.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
@@ -99,6 +119,61 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Wave-level transposed reduction: lanes p = lane % LPR of a row hold partial sums
+// a[i] for LPR consecutive loads i; afterwards lane p holds the full sum of load
+// index p. At the stage with lane distance 2^j a lane keeps the loads whose index
+// has bit j equal to its own and adds its partner's copy (quad DPP moves for
+// distances 1 and 2, a swizzle for 4).
+template <int LPR>
+__device__ __forceinline__ float transpose_reduce(float (&a)[LPR], int p) {
+  float b[LPR / 2];
+  const bool odd = p & 1;
+#pragma unroll
+  for (int t = 0; t < LPR / 2; ++t) {
+    const float keep = odd ? a[2 * t + 1] : a[2 * t];
+    const float send = odd ? a[2 * t] : a[2 * t + 1];
+    b[t] = keep + dpp<DPP_QUAD_XOR1>(send);
+  }
+  if constexpr (LPR == 2) {
+    return b[0];
+  } else {
+    float c[LPR / 4];
+    const bool b1 = (p >> 1) & 1;
+#pragma unroll
+    for (int t = 0; t < LPR / 4; ++t) {
+      const float keep = b1 ? b[2 * t + 1] : b[2 * t];
+      const float send = b1 ? b[2 * t] : b[2 * t + 1];
+      c[t] = keep + dpp<DPP_QUAD_XOR2>(send);
+    }
+    if constexpr (LPR == 4) {
+      return c[0];
+    } else {
+      const bool b2 = (p >> 2) & 1;
+      const float keep = b2 ? c[1] : c[0];
+      const float send = b2 ? c[0] : c[1];
+      return keep + swz_xor4(send);
+    }
+  }
+}
+
+// Score of one projected row by one lane: the r/8 partial dots are summed in the
+// balanced tree the transposed wave reduction uses, so identical rows get
+// bit-identical scores whichever code path computes them. q holds q_hat (r fp32).
+template <int R>
+__device__ __forceinline__ float row_score(const float* q, const uint16_t* rowp) {
+  constexpr int LPR = R / 8;
+  float a[LPR];
+#pragma unroll
+  for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(q + 8 * i, ld16(rowp + 8 * i));
+  if constexpr (LPR == 2) {
+    return a[0] + a[1];
+  } else if constexpr (LPR == 4) {
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  } else {
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  }
 }
 
 }  // namespace sjsa

@@ -13,6 +13,9 @@ constexpr int HEAD_DIM = 128;
 constexpr int HIST_BINS = 4096;      // first radix digit: top 12 bits of the score key
 constexpr int HIST_SHIFT = 20;
 constexpr int QHAT_STRIDE = 64;      // floats reserved per unit for q_hat (r <= 64)
+constexpr int SEG_ROWS = 128;        // rows per scan segment (one wave iteration)
+constexpr int TILE_ROWS = 4096;      // rows per scan workgroup; candidate region of a workgroup
+constexpr int CAND_STAGE = 256;      // candidates a scan wave stages in LDS before writing
 constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
 
 struct Layout {
@@ -20,7 +23,9 @@ struct Layout {
   int64_t score_stride = 0;   // floats per unit row of the score buffer
   int nsplit = 1;             // attention splits per unit
   int chunk = 0;              // selected indices per split
-  size_t off_qhat = 0, off_hist = 0, off_scores = 0, off_partials = 0;
+  int64_t nseg_cap = 0;       // scan segments per unit row (capacity / SEG_ROWS, rounded up)
+  int64_t cand_stride = 0;    // candidate entries per unit (capacity rounded up to TILE_ROWS)
+  size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
   size_t scores_end = 0, total = 0;
 };
 
@@ -31,13 +36,14 @@ hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint1
                          const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, uint16_t* Kproj,
                          hipStream_t st);
 hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
-                       unsigned char* ws, hipStream_t st);
+                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st);
 hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kproj, const int32_t* seq_len,
                         unsigned char* ws, hipStream_t st);
-hipError_t launch_hist(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
-                       const int32_t* seq_len, unsigned char* ws, hipStream_t st);
+// scores == nullptr: select from the scan's candidates in the workspace (recomputing a
+// unit's scores from kproj/qhat when needed); else exact top-k of the given dense scores.
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
-                         const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws, hipStream_t st);
+                         const uint16_t* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
+                         hipStream_t st);
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
                          float sm_scale, void* out, unsigned char* ws, hipStream_t st);

@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libsjsa.so")
 
 SJSA_FLAG_OUT_F32 = 1
+SJSA_FLAG_WRITE_SCORES = 2
 SJSA_MAX_K = 1 << 20
 
 
@@ -47,10 +48,11 @@ _SIGS = {
     "sjsa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
     "sjsa_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
-    "sjsa_score": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "sjsa_prep": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_score": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t,
+                                  _P]),
+    "sjsa_prep": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
     "sjsa_scan": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_size_t, _P]),
-    "sjsa_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
     "sjsa_attend": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_float,
                                    _P, _P, ctypes.c_size_t, _P]),
     "sjsa_topk": (ctypes.c_int, [ctypes.POINTER(Shape), _P, ctypes.c_int64, _P, ctypes.c_int32, _P, _P,
@@ -81,8 +83,9 @@ def _check(status: int):
         raise SjsaError(status, lib().sjsa_status_string(status).decode())
 
 
-def make_shape(batch, n_kv_heads, group, head_dim, rank, capacity, out_f32=False) -> Shape:
-    return Shape(batch, n_kv_heads, group, head_dim, rank, SJSA_FLAG_OUT_F32 if out_f32 else 0, capacity)
+def make_shape(batch, n_kv_heads, group, head_dim, rank, capacity, out_f32=False, write_scores=False) -> Shape:
+    flags = (SJSA_FLAG_OUT_F32 if out_f32 else 0) | (SJSA_FLAG_WRITE_SCORES if write_scores else 0)
+    return Shape(batch, n_kv_heads, group, head_dim, rank, flags, capacity)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -127,7 +130,8 @@ def alloc_workspace(shape: Shape, k: int, device=None) -> torch.Tensor:
 
 
 def scores_view(shape: Shape, workspace: torch.Tensor) -> torch.Tensor:
-    """The fp32 score buffer inside a workspace, viewed as [B, H_kv, stride]."""
+    """The fp32 score buffer inside a workspace, viewed as [B, H_kv, stride]; filled by a
+    score() call made with write_scores=True."""
     off = lib().sjsa_workspace_scores_offset(ctypes.byref(shape))
     stride = lib().sjsa_workspace_score_stride(ctypes.byref(shape))
     n = shape.batch * shape.n_kv_heads * stride * 4
@@ -185,26 +189,30 @@ def decode_step(q, K, V, Kproj, M, seq_len, k, sm_scale=0.0, out=None, idx=None,
     return out, idx
 
 
-def score(q, Kproj, M, seq_len, workspace, capacity=None, stream=None):
-    """Scoring prep + score scan into the workspace; returns the [B, H_kv, stride] fp32 view."""
+def score(q, Kproj, M, seq_len, k, workspace, write_scores=False, stream=None):
+    """Scoring prep + score scan into the workspace (candidates for budget k). With
+    write_scores the dense fp32 scores are stored too and returned as a
+    [B, H_kv, stride] view; otherwise returns None."""
     B, Hkv, cap, r = Kproj.shape
     d = M.shape[2]
-    shape = make_shape(B, Hkv, q.shape[1] // Hkv, d, r, cap)
+    shape = make_shape(B, Hkv, q.shape[1] // Hkv, d, r, cap, write_scores=write_scores)
     _need(q, "q", torch.bfloat16, (B, shape.group * Hkv, d))
     _need(Kproj, "Kproj", torch.bfloat16)
     _need(M, "M", torch.float32, (Hkv, r, d))
     _need(seq_len, "seq_len", torch.int32, (B,))
-    _check(lib().sjsa_score(ctypes.byref(shape), _ptr(q), _ptr(Kproj), _ptr(M), _ptr(seq_len),
+    _check(lib().sjsa_score(ctypes.byref(shape), _ptr(q), _ptr(Kproj), _ptr(M), _ptr(seq_len), int(k),
                             _ptr(workspace), workspace.numel(), _stream(stream)))
-    return scores_view(shape, workspace)
+    return scores_view(shape, workspace) if write_scores else None
 
 
-def prep(shape: Shape, q, M, workspace, stream=None):
-    """Scoring prep only (mean query, projection; clears the histogram and counters)."""
+def prep(shape: Shape, q, M, Kproj, seq_len, k, workspace, stream=None):
+    """Scoring prep only (mean query, projection, candidate threshold for budget k)."""
     _need(q, "q", torch.bfloat16, (shape.batch, shape.n_kv_heads * shape.group, shape.head_dim))
     _need(M, "M", torch.float32, (shape.n_kv_heads, shape.rank, shape.head_dim))
-    _check(lib().sjsa_prep(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(workspace), workspace.numel(),
-                           _stream(stream)))
+    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need(seq_len, "seq_len", torch.int32, (shape.batch,))
+    _check(lib().sjsa_prep(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(Kproj), _ptr(seq_len), int(k),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def scan(shape: Shape, Kproj, seq_len, workspace, stream=None):
@@ -215,12 +223,13 @@ def scan(shape: Shape, Kproj, seq_len, workspace, stream=None):
                            _stream(stream)))
 
 
-def select(shape: Shape, seq_len, k, workspace, idx=None, stream=None):
-    """Top-k over the scores left in the workspace by score()."""
+def select(shape: Shape, Kproj, seq_len, k, workspace, idx=None, stream=None):
+    """Top-k from what score() left in the workspace."""
     if idx is None:
         idx = torch.empty((shape.batch, shape.n_kv_heads, int(k)), dtype=torch.int32, device=workspace.device)
     _need(idx, "idx", torch.int32, (shape.batch, shape.n_kv_heads, int(k)))
-    _check(lib().sjsa_select(ctypes.byref(shape), _ptr(seq_len), int(k), _ptr(idx), _ptr(workspace),
+    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _check(lib().sjsa_select(ctypes.byref(shape), _ptr(Kproj), _ptr(seq_len), int(k), _ptr(idx), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
     return idx
 
