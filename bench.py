@@ -164,18 +164,29 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # throughput: K whole steps back to back, bracketed by one pair of events (an event
+    # between two kernels delays the second by several microseconds, so the steps
+    # themselves carry none)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    # stage durations: the same K steps again with an event between consecutive
+    # stages, all on the stream the kernels run on (torch's current stream); each
+    # interval also holds the launch latency of its first kernel, so these figures
+    # slightly overstate the kernels' own durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     names = ["append", "prep", "scan", "select", "attend"]
     stage_ms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, nm in enumerate(names)}
-    ms_per_step = total_ms / args.steps
 
     tb = step_bytes(B, Hkv, G, d, r, n, k)
     gbs = tb["total"] / (ms_per_step * 1e-3) / 1e9

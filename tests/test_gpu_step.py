@@ -168,8 +168,9 @@ def test_candidate_overflow_falls_back_exactly():
 
 
 def test_candidate_underflow_falls_back_exactly():
-    # the rows the prep stage samples (positions s*n/2048) score high, all others low:
-    # the sampled threshold lands above the true k-th score, too few rows qualify
+    # every other row the prep stage samples (positions s*n/2048, s even) scores high,
+    # all others low: the sampled threshold lands on the high score, and only 1024
+    # rows (fewer than k) reach it
     say("step candidate underflow -> exact fallback")
     n, k = 40000, 2000
     wl = workloads.gaussian(1, 1, 4, 128, 16, n, k, seed=26, device="cuda")
@@ -182,5 +183,23 @@ def test_candidate_underflow_falls_back_exactly():
     high = round_to_bf16(high)
     kp = np.tile(low, (1, 1, n, 1)).astype(np.uint16)
     sampled = (np.arange(2048, dtype=np.int64) * n) // 2048
-    kp[0, 0, sampled] = high
+    kp[0, 0, sampled[::2]] = high
     _ties_check(wl, kp, k, "underflow")
+
+
+def test_scan_stage_overflow_falls_back_exactly():
+    # the first 4096 rows (one scan tile) all score high, the rest low: every wave of
+    # that tile finds 1024 candidates, more than it can stage; the total (4096) would
+    # fit the selection, so only the overflow flag keeps the result exact
+    say("step scan stage overflow -> exact fallback")
+    n, k = 40000, 1500
+    wl = workloads.gaussian(1, 1, 4, 128, 16, n, k, seed=27, device="cuda")
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    qhat = jssa.project_query(jssa.mean_query(q[0, 0:4]), M[0]).astype(np.float64)
+    low = jssa.project_keys(bits(wl.K[0, 0, :1].contiguous()), M[0])[0]
+    from oracle.numerics import round_to_bf16
+    high = round_to_bf16(np.sign(qhat) * 4.0)
+    kp = np.tile(low, (1, 1, n, 1)).astype(np.uint16)
+    kp[0, 0, :4096] = high
+    _ties_check(wl, kp, k, "stage overflow")

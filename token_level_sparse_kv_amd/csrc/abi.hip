@@ -50,7 +50,7 @@ Layout make_layout(const sjsa_shape& s, int k) {
   if (chunk > ATT_MAX_CHUNK) chunk = ATT_MAX_CHUNK;
   L.chunk = (int)chunk;
   L.nsplit = (int)((k + chunk - 1) / chunk);
-  L.nseg_cap = (s.capacity + SEG_ROWS - 1) / SEG_ROWS;
+  L.ntile_cap = (s.capacity + TILE_ROWS - 1) / TILE_ROWS;
   L.cand_stride = (s.capacity + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
   size_t off = 0;
   L.off_qhat = off;
@@ -58,7 +58,7 @@ Layout make_layout(const sjsa_shape& s, int k) {
   L.off_tlow = off;
   off = align_up(off + (size_t)L.units * 2 * sizeof(uint32_t), WS_ALIGN);
   L.off_counts = off;
-  off = align_up(off + (size_t)L.units * L.nseg_cap * sizeof(uint32_t), WS_ALIGN);
+  off = align_up(off + (size_t)L.units * L.ntile_cap * sizeof(uint64_t), WS_ALIGN);
   L.off_cand = off;
   off = align_up(off + (size_t)L.units * L.cand_stride * sizeof(uint64_t), WS_ALIGN);
   L.off_scores = off;

@@ -11,18 +11,21 @@ namespace {
 
 constexpr int APPEND_THREADS = 256;
 constexpr int APPEND_ROWS = 64;                 // token rows per workgroup
-constexpr int LDS_ROW = HEAD_DIM + 1;           // padded LDS row (no bank conflicts)
 
-// grid = (ceil(n_new / APPEND_ROWS), B * H_kv)
+// grid = (ceil(n_new / APPEND_ROWS), B * H_kv). Threads copy the workgroup's K and
+// V rows (16 bytes each), then project them: output i of a projected row is split
+// over TPO = 256 / R lanes, lane `part` owning channels part*CH .. part*CH + CH - 1
+// of basis row i, which it holds in registers for all the workgroup's rows. The
+// TPO partial dots (each in channel order) are combined with DPP lane moves, so a
+// projected row's bits do not depend on how many tokens one call appends.
 template <int R>
 __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n_new,
     const float* __restrict__ M, const int32_t* __restrict__ pos,
     uint16_t* __restrict__ K, uint16_t* __restrict__ V, uint16_t* __restrict__ Kproj,
     int n_kv_heads, int64_t cap) {
-  __shared__ float sM[R * LDS_ROW];
-  __shared__ float sk[APPEND_ROWS * LDS_ROW];
-
+  constexpr int TPO = APPEND_THREADS / R;      // lanes per output (16, 8 or 4)
+  constexpr int CH = HEAD_DIM / TPO;           // channels per lane (8, 16 or 32)
   const int unit = blockIdx.y;
   const int b = unit / n_kv_heads;
   const int h = unit - b * n_kv_heads;
@@ -30,47 +33,51 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
   const int rows = min(APPEND_ROWS, n_new - t0);
   const int64_t p0 = (int64_t)pos[b] + t0;
   const int tid = threadIdx.x;
+  const size_t src0 = ((size_t)unit * n_new + t0) * HEAD_DIM;
 
-  const float* Mh = M + (size_t)h * R * HEAD_DIM;
-  for (int i = tid; i < R * HEAD_DIM; i += APPEND_THREADS) {
-    const int j = i / HEAD_DIM, c = i - j * HEAD_DIM;
-    sM[j * LDS_ROW + c] = Mh[i];
-  }
-
-  // K / V rows: 16 lanes x 16 bytes per 256-byte row.
-  const size_t src_base = ((size_t)unit * n_new + t0) * HEAD_DIM;
-  for (int i = tid; i < APPEND_ROWS * 16; i += APPEND_THREADS) {
-    const int r = i >> 4, part = i & 15;
-    if (r < rows) {
-      const u32x4 kw = ld16(k_new + src_base + (size_t)r * HEAD_DIM + part * 8);
-      const u32x4 vw = ld16(v_new + src_base + (size_t)r * HEAD_DIM + part * 8);
-      const int64_t p = p0 + r;
-      if (p >= 0 && p < cap) {
-        const size_t dst = ((size_t)unit * cap + p) * HEAD_DIM + part * 8;
-        *reinterpret_cast<u32x4*>(K + dst) = kw;
-        *reinterpret_cast<u32x4*>(V + dst) = vw;
-      }
-      float* dstk = sk + r * LDS_ROW + part * 8;
-      dstk[0] = bf_lo(kw.x); dstk[1] = bf_hi(kw.x);
-      dstk[2] = bf_lo(kw.y); dstk[3] = bf_hi(kw.y);
-      dstk[4] = bf_lo(kw.z); dstk[5] = bf_hi(kw.z);
-      dstk[6] = bf_lo(kw.w); dstk[7] = bf_hi(kw.w);
-    }
-  }
-  __syncthreads();
-
-  // Kproj rows: one (row, output) pair per thread iteration, fp32 dot in channel order.
-  for (int o = tid; o < APPEND_ROWS * R; o += APPEND_THREADS) {
-    const int r = o / R, j = o - r * R;
-    if (r >= rows) continue;
+  for (int w = tid; w < rows * 32; w += APPEND_THREADS) {
+    const int r = w >> 5, part = w & 15;
     const int64_t p = p0 + r;
     if (p < 0 || p >= cap) continue;
-    const float* mr = sM + j * LDS_ROW;
-    const float* kr = sk + r * LDS_ROW;
+    const bool is_v = (w >> 4) & 1;
+    const size_t off = (size_t)r * HEAD_DIM + part * 8;
+    const u32x4 x = ld16((is_v ? v_new : k_new) + src0 + off);
+    *reinterpret_cast<u32x4*>((is_v ? V : K) + ((size_t)unit * cap + p) * HEAD_DIM + part * 8) = x;
+  }
+
+  const int i = tid / TPO, part = tid % TPO;
+  const f32x4* m4 = reinterpret_cast<const f32x4*>(M + ((size_t)h * R + i) * HEAD_DIM + part * CH);
+  f32x4 mv[CH / 4];
+#pragma unroll
+  for (int c = 0; c < CH / 4; ++c) mv[c] = m4[c];
+  const uint16_t* kbase = k_new + src0 + part * CH;
+  for (int r = 0; r < rows; ++r) {
+    u32x4 kv[CH / 8];
+#pragma unroll
+    for (int c = 0; c < CH / 8; ++c) kv[c] = ld16(kbase + (size_t)r * HEAD_DIM + c * 8);
     float acc = 0.f;
-#pragma unroll 16
-    for (int c = 0; c < HEAD_DIM; ++c) acc = fmaf(mr[c], kr[c], acc);
-    Kproj[((size_t)unit * cap + p) * R + j] = (uint16_t)f32_to_bf16_rne(acc);
+#pragma unroll
+    for (int c = 0; c < CH / 8; ++c) {
+      const f32x4 m0 = mv[2 * c], m1 = mv[2 * c + 1];
+      acc = fmaf(m0.x, bf_lo(kv[c].x), acc);
+      acc = fmaf(m0.y, bf_hi(kv[c].x), acc);
+      acc = fmaf(m0.z, bf_lo(kv[c].y), acc);
+      acc = fmaf(m0.w, bf_hi(kv[c].y), acc);
+      acc = fmaf(m1.x, bf_lo(kv[c].z), acc);
+      acc = fmaf(m1.y, bf_hi(kv[c].z), acc);
+      acc = fmaf(m1.z, bf_lo(kv[c].w), acc);
+      acc = fmaf(m1.w, bf_hi(kv[c].w), acc);
+    }
+    if constexpr (TPO == 16) {
+      acc = row16_sum(acc);
+    } else {
+      acc += dpp<DPP_QUAD_XOR1>(acc);
+      acc += dpp<DPP_QUAD_XOR2>(acc);
+      if constexpr (TPO == 8) acc += swz_xor4(acc);
+    }
+    const int64_t p = p0 + r;
+    if (part == 0 && p >= 0 && p < cap)
+      Kproj[((size_t)unit * cap + p) * R + i] = (uint16_t)f32_to_bf16_rne(acc);
   }
 }
 
@@ -79,8 +86,8 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
 hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
                          const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, uint16_t* Kproj,
                          hipStream_t st) {
-  const dim3 grid((n_new + APPEND_ROWS - 1) / APPEND_ROWS, s.batch * s.n_kv_heads);
   const dim3 block(APPEND_THREADS);
+  const dim3 grid((n_new + APPEND_ROWS - 1) / APPEND_ROWS, s.batch * s.n_kv_heads);
   switch (s.rank) {
     case 16: append_kernel<16><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads, s.capacity); break;
     case 32: append_kernel<32><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads, s.capacity); break;

@@ -8,162 +8,193 @@
 // scoring, top-k selection, sparse attention.
 //
 // prep_kernel  (one workgroup per (b, h)): q_bar in fp32 (sum in head order, then
-//              divide by G), q_hat = M_h q_bar (fp32), and clears this unit's
-//              first-digit histogram for the scan.
+//              divide by G), q_hat = M_h q_bar (fp32), and the unit's candidate
+//              threshold, placed from the scores of evenly spaced sample rows.
 // score_kernel (grid = tiles x units): streams Kproj rows with 128-bit coalesced
 //              loads, each lane holding 8 of a row's r values; the partial dots of
 //              the r/8 lanes of a row are reduced with DPP lane moves in a
 //              transposed pattern, so that after the reduction each lane owns the
-//              full score of one row. Scores are written as fp32, and a histogram
-//              of their top 12 key bits is accumulated for the top-k stage.
+//              full score of one row. Rows whose score key reaches the threshold
+//              are kept as candidates for the top-k stage (and, on request, every
+//              score is stored).
 #include "sjsa_device.h"
 #include "sjsa_internal.h"
 
 namespace sjsa {
 namespace {
 
-constexpr int PREP_THREADS = 256;
+constexpr int PREP_THREADS = 512;
+constexpr int PREP_WAVES = PREP_THREADS / 64;
 constexpr int SCORE_THREADS = 256;
 constexpr int SCORE_WAVES = SCORE_THREADS / 64;
 constexpr int GROUP_ROWS = 64;       // rows covered by r/8 wave-wide 16-byte loads
 constexpr int SAMPLES = 2048;        // rows scored by the prep kernel to place the threshold
+constexpr int PREP_BINS = 4096;      // linear score bins of the threshold histogram
 
-// Radix select over `cnt` u32 keys in LDS with PREP_THREADS threads: the key of
-// rank m (1 = largest). Three rounds of 11, 11 and 10 bits; in each round a
-// histogram of the keys that match the bits resolved so far is built, and the bin
-// holding rank m is found with a block scan. hist needs 2048 words, scratch 8.
-__device__ uint32_t lds_kth_largest(const uint32_t* keys, int cnt, uint32_t m, uint32_t* hist,
-                                    uint32_t* scratch) {
-  constexpr int NW = PREP_THREADS / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t prefix = 0, mask = 0;
-  for (int round = 0; round < 3; ++round) {
-    const int sh = round == 0 ? 21 : (round == 1 ? 10 : 0);
-    const int nb = round == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += PREP_THREADS) hist[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < cnt; i += PREP_THREADS) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    const int per = nb / PREP_THREADS;
-    const int lo = tid * per;
-    uint32_t local = 0;
-    for (int i = 0; i < per; ++i) local += hist[lo + i];
-    const uint32_t inc = wave_incl_scan(local);
-    if (lane == 63) scratch[2 + wave] = inc;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
+// Block-wide (PREP_THREADS) inclusive scan of one u32 per thread; the block total
+// goes to *total. Two barriers.
+__device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) scan_lds[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t t = scratch[2 + w];
-      before += w < wave ? t : 0u;
-      total += t;
-    }
-    uint32_t above = total - (inc + before);      // keys in bins above this thread's range
-    if (above < m && m <= above + local) {
-      for (int i = per - 1; i >= 0; --i) {
-        const uint32_t c = hist[lo + i];
-        if (above + c >= m) { scratch[0] = (uint32_t)(lo + i); scratch[1] = above; break; }
-        above += c;
-      }
-    }
-    __syncthreads();
-    const uint32_t bsel = scratch[0];
-    m -= scratch[1];
-    prefix |= bsel << sh;
-    mask |= (uint32_t)(nb - 1) << sh;
-    __syncthreads();
+  for (int w = 0; w < PREP_WAVES; ++w) {
+    const uint32_t t = scan_lds[w];
+    before += w < wave ? t : 0u;
+    tot += t;
   }
-  return prefix;
+  __syncthreads();
+  *total = tot;
+  return inc + before;
 }
 
 // One workgroup per (b, h).
-//  * q_bar in fp32 (sum in head order, then divide by G) and q_hat = M_h q_bar.
+//  * q_bar in fp32 (sum in head order, then divide by G) and q_hat = M_h q_bar: output
+//    i is split over 16 lanes of 8 channels each (fp32 partial dots, DPP row sum).
 //  * Threshold for the scan: the scores of SAMPLES evenly spaced rows (all rows when
-//    n <= SAMPLES) are ranked, and the key of rank m (see below) becomes the unit's
-//    candidate threshold. The exact top k is among the rows that reach it unless the
-//    sample misjudges the distribution, a case the select stage detects and handles
-//    exactly.
+//    n <= SAMPLES) are binned linearly between their least and greatest finite value
+//    (+inf in the top bin, -inf and NaN left out); the bin that holds the sample of
+//    rank m (see below) is found, and the least key in it becomes the unit's
+//    candidate threshold, so at least m samples reach it. The exact top k is among
+//    the rows that reach it unless the sample misjudges the distribution, a case the
+//    select stage detects and handles exactly: the threshold only decides how much
+//    work the select stage does, never its result.
 //  * mode: 1 when k >= n (every position is selected and the scan has no work).
+// The sample rows are loaded first, so their latency overlaps the q_hat work.
 template <int R>
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ M, const uint16_t* __restrict__ kproj,
     const int32_t* __restrict__ seq_len, int k, float* __restrict__ qhat, uint32_t* __restrict__ tlow,
     int n_kv_heads, int group, int64_t cap) {
-  __shared__ float sq[HEAD_DIM];
-  __shared__ float sM[R * (HEAD_DIM + 1)];
+  constexpr int LPR = R / 8;                          // 16-byte words per Kproj row
+  constexpr int RPL = 64 / LPR;                       // samples per wave-wide load
+  constexpr int BATCHES = SAMPLES / PREP_THREADS;     // 64-sample batches per wave (= samples per lane)
+  constexpr int OUTS = (R * 16 + PREP_THREADS - 1) / PREP_THREADS;   // q_hat outputs per thread
   __shared__ float sqh[R];
-  __shared__ uint32_t skey[SAMPLES];
-  __shared__ uint32_t shist[2048];
-  __shared__ uint32_t sscratch[8];
+  __shared__ uint32_t shist[PREP_BINS];
+  __shared__ float sred[2 * PREP_WAVES];
+  __shared__ uint32_t sscan[PREP_WAVES];
+  __shared__ uint32_t smisc[4];
   const int unit = blockIdx.x;
   const int b = unit / n_kv_heads;
   const int h = unit - b * n_kv_heads;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
   const int64_t kk = min((int64_t)k, n);
-  // stage M_h (r x d) in LDS with a padded row stride (conflict-free column reads);
-  // all of a thread's loads are issued before any is stored
-  constexpr int MV = R * HEAD_DIM / 4 / PREP_THREADS;    // float4 loads per thread
-  {
-    const f32x4* m4 = reinterpret_cast<const f32x4*>(M + (size_t)h * R * HEAD_DIM);
-    f32x4 mv[MV];
+  const bool sampling = kk < n;                       // uniform over the workgroup
+  const int S = (int)min((int64_t)SAMPLES, n);
+
+  // sample s sits in row pos(s) (evenly spaced); wave-wide loads as in the scan: in
+  // batch t a wave covers samples sb .. sb + 63 (sb = 64 * (wave + t * PREP_WAVES)),
+  // load i reading 16 bytes (lane column p) of sample sb + i * RPL + rs, so the LPR
+  // lanes of a sample read its row contiguously
+  const int p = lane % LPR, rs = lane / LPR;
+  u32x4 w[BATCHES][LPR];
+  if (sampling) {
+    const uint16_t* base = kproj + (size_t)unit * cap * R + p * 8;
 #pragma unroll
-    for (int i = 0; i < MV; ++i) mv[i] = m4[tid + i * PREP_THREADS];
+    for (int t = 0; t < BATCHES; ++t) {
 #pragma unroll
-    for (int i = 0; i < MV; ++i) {
-      const int e = (tid + i * PREP_THREADS) * 4;
-      const int j = e / HEAD_DIM, c = e - j * HEAD_DIM;
-      float* dst = sM + j * (HEAD_DIM + 1) + c;
-      dst[0] = mv[i].x; dst[1] = mv[i].y; dst[2] = mv[i].z; dst[3] = mv[i].w;
+      for (int i = 0; i < LPR; ++i) {
+        const int sidx = min(64 * (wave + t * PREP_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
+        const int64_t pos = (n <= SAMPLES) ? sidx : (int64_t)sidx * n / SAMPLES;
+        w[t][i] = ld16(base + pos * R);
+      }
     }
   }
-  if (tid < HEAD_DIM) {
-    // q[b, h*G + g, tid] for every head g (G <= 8), all loads issued before the sum,
-    // which runs in head order
-    const uint16_t* qg = q + (size_t)unit * group * HEAD_DIM + tid;
-    uint32_t qb[8];
+
+  // q_bar for channels 8*part .. 8*part + 7 (every lane of a 16-lane row computes it)
+  const int part = tid & 15;
+  float qbar[8];
+  {
+    const uint16_t* qg = q + (size_t)unit * group * HEAD_DIM + part * 8;
+    u32x4 qw[8];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) qb[g] = qg[(size_t)min(g, group - 1) * HEAD_DIM];
-    float acc = 0.f;
+    for (int g = 0; g < 8; ++g) qw[g] = ld16(qg + (size_t)min(g, group - 1) * HEAD_DIM);
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < group) acc += __uint_as_float(qb[g] << 16);
-    sq[tid] = acc / (float)group;
+    for (int c = 0; c < 8; ++c) qbar[c] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g < group) {
+        qbar[0] += bf_lo(qw[g].x); qbar[1] += bf_hi(qw[g].x);
+        qbar[2] += bf_lo(qw[g].y); qbar[3] += bf_hi(qw[g].y);
+        qbar[4] += bf_lo(qw[g].z); qbar[5] += bf_hi(qw[g].z);
+        qbar[6] += bf_lo(qw[g].w); qbar[7] += bf_hi(qw[g].w);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qbar[c] = qbar[c] / (float)group;
   }
-  __syncthreads();
-  if (tid < R) {
-    const float* mr = sM + tid * (HEAD_DIM + 1);
-    float acc = 0.f;
-    for (int c = 0; c < HEAD_DIM; ++c) acc = fmaf(mr[c], sq[c], acc);
-    qhat[(size_t)unit * QHAT_STRIDE + tid] = acc;
-    sqh[tid] = acc;
+#pragma unroll
+  for (int o = 0; o < OUTS; ++o) {
+    const int i = tid / 16 + o * (PREP_THREADS / 16);
+    const f32x4* m4 = reinterpret_cast<const f32x4*>(M + ((size_t)h * R + min(i, R - 1)) * HEAD_DIM + part * 8);
+    const f32x4 m0 = m4[0], m1 = m4[1];
+    float acc = m0.x * qbar[0];
+    acc = fmaf(m0.y, qbar[1], acc);
+    acc = fmaf(m0.z, qbar[2], acc);
+    acc = fmaf(m0.w, qbar[3], acc);
+    acc = fmaf(m1.x, qbar[4], acc);
+    acc = fmaf(m1.y, qbar[5], acc);
+    acc = fmaf(m1.z, qbar[6], acc);
+    acc = fmaf(m1.w, qbar[7], acc);
+    acc = row16_sum(acc);
+    if (part == 0 && i < R) {
+      qhat[(size_t)unit * QHAT_STRIDE + i] = acc;
+      sqh[i] = acc;
+    }
   }
+  for (int i = tid; i < PREP_BINS; i += PREP_THREADS) shist[i] = 0u;
+  if (tid == 0) smisc[0] = 0xffffffffu;
   __syncthreads();
-  if (kk >= n) {          // take every position (also n = 0): no threshold needed
+  if (!sampling) {        // take every position (also n = 0): no threshold needed
     if (tid == 0) { tlow[unit * 2] = 0u; tlow[unit * 2 + 1] = 1u; }
     return;
   }
-  const int S = (int)min((int64_t)SAMPLES, n);
-  float qreg[R];
+
+  // lane (rs, p) scores its 8 columns of the LPR rows of a batch; the transposed
+  // reduction leaves it the score of sample sb + p * RPL + rs
+  float qh[8];
 #pragma unroll
-  for (int i = 0; i < R; ++i) qreg[i] = sqh[i];
-  const uint16_t* base = kproj + (size_t)unit * cap * R;
-  // all sample rows of a thread are loaded before any is scored (positions past S
-  // are clamped to sample S-1 and not stored), so the loads overlap
-  constexpr int PER = SAMPLES / PREP_THREADS;
-  float sc[PER];
+  for (int e = 0; e < 8; ++e) qh[e] = sqh[p * 8 + e];
+  float sc[BATCHES];
+  int sid[BATCHES];
+  float lo = __builtin_inff(), hi = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int sidx = min(tid + i * PREP_THREADS, S - 1);
-    const int64_t pos = (n <= SAMPLES) ? sidx : (int64_t)sidx * n / SAMPLES;
-    sc[i] = row_score<R>(qreg, base + pos * R);
+  for (int t = 0; t < BATCHES; ++t) {
+    float a[LPR];
+#pragma unroll
+    for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(qh, w[t][i]);
+    sc[t] = transpose_reduce<LPR>(a, p);
+    sid[t] = 64 * (wave + t * PREP_WAVES) + p * RPL + rs;
+    if (sid[t] < S && __builtin_isfinite(sc[t])) {
+      lo = fminf(lo, sc[t]);
+      hi = fmaxf(hi, sc[t]);
+    }
   }
+  lo = wave_min_f32(lo);
+  hi = wave_max_f32(hi);
+  if (lane == 0) { sred[wave] = lo; sred[PREP_WAVES + wave] = hi; }
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (tid + i * PREP_THREADS < S) skey[tid + i * PREP_THREADS] = score_key(sc[i]);
+  for (int v = 0; v < PREP_WAVES; ++v) {
+    lo = fminf(lo, sred[v]);
+    hi = fmaxf(hi, sred[PREP_WAVES + v]);
+  }
+  const float scale = hi > lo ? (float)PREP_BINS / (hi - lo) : 0.f;
+  int bin[BATCHES];
+#pragma unroll
+  for (int t = 0; t < BATCHES; ++t) {
+    const float x = sc[t];
+    bin[t] = -1;
+    if (sid[t] < S && !(x != x) && x != -__builtin_inff()) {
+      const float f = (x - lo) * scale;                       // +inf -> top bin; NaN -> bin 0
+      bin[t] = f > 0.f ? (int)fminf(f, (float)(PREP_BINS - 1)) : 0;
+      atomicAdd(&shist[bin[t]], 1u);
+    }
+  }
   __syncthreads();
   // the number of samples at or above the true k-th key is Binomial(S, kk/n): taking
   // the sample of rank mean + 5 sd + 4 keeps the threshold below that key except with
@@ -172,46 +203,78 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
   const double mu = (double)S * pk;
   int64_t m = (int64_t)ceil(mu + 5.0 * sqrt(mu * (1.0 - pk)) + 4.0);
   m = m < 1 ? 1 : (m > S ? S : m);
-  const uint32_t t = lds_kth_largest(skey, S, (uint32_t)m, shist, sscratch);
-  if (tid == 0) { tlow[unit * 2] = t; tlow[unit * 2 + 1] = 0u; }
+  constexpr int BPT = PREP_BINS / PREP_THREADS;
+  const int b0 = tid * BPT;
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) local += shist[b0 + i];
+  uint32_t total;
+  const uint32_t inc = prep_block_scan(local, sscan, &total);
+  uint32_t above = total - inc;                 // samples in bins above this thread's bins
+  const uint32_t mm = (uint32_t)m;
+  if (above < mm && mm <= above + local) {
+    for (int i = BPT - 1; i >= 0; --i) {
+      const uint32_t c = shist[b0 + i];
+      if (above + c >= mm) { smisc[1] = (uint32_t)(b0 + i); break; }
+      above += c;
+    }
+  }
+  __syncthreads();
+  if (total >= mm) {
+    const int bsel = (int)smisc[1];
+#pragma unroll
+    for (int t = 0; t < BATCHES; ++t)
+      if (bin[t] == bsel) atomicMin(&smisc[0], score_key(sc[t]));
+  }
+  __syncthreads();
+  // fewer than m binned samples (most scores NaN or -inf): every row is a candidate
+  if (tid == 0) { tlow[unit * 2] = total >= mm ? smisc[0] : 0u; tlow[unit * 2 + 1] = 0u; }
 }
 
-// grid = (ceil(cap / TILE_ROWS), B * H_kv). A segment is the SEG_ROWS = 128 rows one
-// wave covers in one iteration (UNROLL groups of 64); the waves of a workgroup take
-// the tile's segments in turn (wave w: segments w, w + 4, ...), so the workgroup
-// streams one contiguous region. Loads are 128-bit and coalesced, each lane holding
-// 8 of a row's r values; the partial dots of the r/8 lanes of a row are reduced with
-// DPP lane moves in a transposed pattern, after which lane (rs, p) owns the score of
-// group row p*RPL + rs.
+// grid = (ceil(cap / TILE_ROWS), B * H_kv). A segment is the SEG_ROWS = 128 rows
+// one wave covers in one iteration (UNROLL groups of 64); the waves of a workgroup
+// take the tile's segments in turn (wave w: segments w, w + 4, ...), so the
+// workgroup streams one contiguous region. Loads are 128-bit and coalesced, each
+// lane holding 8 of a row's r values; the partial dots of the r/8 lanes of a row
+// are reduced with DPP lane moves in a transposed pattern, after which lane (rs, p)
+// owns the score of group row p*RPL + rs.
 //
 // Rows whose key reaches the unit's threshold are candidates, kept as (key, row)
 // pairs in position order: with a ballot of the flags in lane order, the number of
 // flagged rows before a row is the popcount of the ballot under a per-lane mask of
 // the lanes that hold earlier rows (earlier lane columns, and this column above this
-// lane). Each wave packs the candidates of its segments back to back, first into a
-// wave-private LDS stage, and writes them out once at the end into its region of the
-// candidate buffer (tile x, wave w: entries [x*TILE_ROWS + w*TILE_ROWS/4, +TILE_ROWS/4));
-// writes in the middle of the stream cost far more HBM time than their size. Each
-// segment's count goes to counts[]. With WRITE_DENSE every score is also stored.
+// lane). Each wave packs the candidates of its segments back to back into a
+// wave-private LDS stage and records each segment's count. At the end the
+// workgroup writes the tile's candidates, in position order, to its region of the
+// candidate buffer (entries [x*TILE_ROWS, ...) for tile x), and to counts[x] their
+// number (low word; TILE_OVERFLOW when a wave had more than CAND_STAGE) and their
+// greatest key (high word; 0 when there are none); writes in the
+// middle of the stream cost far more HBM time than their size. With WRITE_DENSE
+// every score is also stored.
 template <int R, int UNROLL, bool WRITE_DENSE>
 __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     const uint16_t* __restrict__ kproj, const float* __restrict__ qhat, const uint32_t* __restrict__ tlow,
     const int32_t* __restrict__ seq_len, float* __restrict__ scores, uint64_t* __restrict__ cand,
-    uint32_t* __restrict__ counts, int n_kv_heads, int64_t cap, int64_t stride, int64_t nseg_cap,
+    uint64_t* __restrict__ counts, int n_kv_heads, int64_t cap, int64_t stride, int64_t ntile_cap,
     int64_t cand_stride) {
   constexpr int LPR = R / 8;            // lanes per Kproj row (16 bytes each)
   constexpr int RPL = 64 / LPR;         // rows per wave-wide load
   static_assert(GROUP_ROWS * UNROLL == SEG_ROWS, "one wave iteration covers one segment");
+  static_assert(TILE_ROWS / SEG_ROWS <= 64, "one wave scans the segment counts");
   constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
-  constexpr int WAVE_REGION = TILE_ROWS / SCORE_WAVES;
   __shared__ uint64_t stage[SCORE_WAVES][CAND_STAGE];
+  __shared__ uint32_t segcnt[SEGS_PER_TILE];
+  __shared__ uint32_t segoff[SEGS_PER_TILE + 1];
+  __shared__ uint32_t sstart[SEGS_PER_TILE];
+  __shared__ uint32_t overflow[SCORE_WAVES];
+  __shared__ uint32_t wmax[SCORE_WAVES];
   const int unit = blockIdx.y;
   const int b = unit / n_kv_heads;
   const int n = (int)min((int64_t)max(seq_len[b], 0), cap);      // cap < 2^30
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int seg0 = blockIdx.x * SEGS_PER_TILE;
-  if ((seg0 + wave) * SEG_ROWS >= n) return;   // this wave has no segment below n
+  if (seg0 * SEG_ROWS >= n) return;            // the whole tile lies past the end
   const bool take_all = tlow[unit * 2 + 1] != 0u;
   if (take_all && !WRITE_DENSE) return;
   const uint32_t tkey = tlow[unit * 2];
@@ -229,12 +292,12 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
 
   const uint16_t* base = kproj + (size_t)unit * cap * R + p * 8;
   float* srow = scores + (size_t)unit * stride;
-  uint64_t* wreg = cand + (size_t)unit * cand_stride + (size_t)blockIdx.x * TILE_ROWS + (size_t)wave * WAVE_REGION;
-  uint32_t* cnt_unit = counts + (size_t)unit * nseg_cap;
   const int last = n - 1;
   uint32_t wcount = 0;                     // candidates of this wave so far
+  uint32_t kmax = 0;                       // greatest candidate key seen by this lane
 
-  for (int j = wave; j < SEGS_PER_TILE; j += SCORE_WAVES) {
+  int j = wave;
+  for (; j < SEGS_PER_TILE; j += SCORE_WAVES) {
     const int g0 = (seg0 + j) * SEG_ROWS;
     if (g0 >= n) break;
     u32x4 w[UNROLL][LPR];
@@ -263,21 +326,58 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
       const uint64_t m = __ballot(c);
       if (c) {
         const uint32_t at = wcount + count + (uint32_t)__popcll(m & earlier);
-        const uint64_t v = ((uint64_t)key << 32) | (uint64_t)(uint32_t)row;
-        if (at < (uint32_t)CAND_STAGE) stage[wave][at] = v;
-        else wreg[at] = v;                // stage full (more than CAND_STAGE candidates)
+        if (at < (uint32_t)CAND_STAGE) stage[wave][at] = ((uint64_t)key << 32) | (uint64_t)(uint32_t)row;
+        kmax = max(kmax, key);
       }
       count += (uint32_t)__popcll(m);
     }
-    if (lane == 0) cnt_unit[seg0 + j] = count;
+    if (lane == 0) segcnt[j] = count;
     wcount += count;
   }
-  // the stage is wave-private: order this wave's LDS writes before its reads
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint32_t nst = min(wcount, (uint32_t)CAND_STAGE);
-  for (uint32_t i = lane; i < nst; i += 64) wreg[i] = stage[wave][i];
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    for (; j < SEGS_PER_TILE; j += SCORE_WAVES) segcnt[j] = 0u;    // segments past the end
+    overflow[wave] = wcount > (uint32_t)CAND_STAGE ? 1u : 0u;
+    wmax[wave] = kmax;
+  }
+  __syncthreads();
+  // the tile's candidates in position order: segment jj's entries start at
+  // segoff[jj] (the counts of segments 0 .. jj-1) in the output and at sstart[jj]
+  // (the counts of the same wave's earlier segments) in its wave's stage
+  if (wave == 0) {
+    const uint32_t c = lane < SEGS_PER_TILE ? segcnt[lane] : 0u;
+    const uint32_t inc = wave_incl_scan(c);
+    if (lane < SEGS_PER_TILE) {
+      segoff[lane + 1] = inc;
+      uint32_t st = 0;
+      for (int q = lane % SCORE_WAVES; q < lane; q += SCORE_WAVES) st += segcnt[q];
+      sstart[lane] = st;
+    }
+    if (lane == 0) segoff[0] = 0u;
+  }
+  __syncthreads();
+  bool ovf = false;
+#pragma unroll
+  for (int v = 0; v < SCORE_WAVES; ++v) ovf = ovf || overflow[v] != 0u;
+  const uint32_t tot = segoff[SEGS_PER_TILE];
+  if (!ovf) {
+    // every thread writes entries e, e + 256, ...: coalesced, streamed past the caches
+    uint64_t* wtile = cand + (size_t)unit * cand_stride + (size_t)blockIdx.x * TILE_ROWS;
+    for (uint32_t e = threadIdx.x; e < tot; e += SCORE_THREADS) {
+      int lo = 0, hi = SEGS_PER_TILE;            // the segment holding entry e
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (segoff[mid] <= e) lo = mid; else hi = mid;
+      }
+      __builtin_nontemporal_store(stage[lo % SCORE_WAVES][sstart[lo] + (e - segoff[lo])], wtile + e);
+    }
+  }
+  if (threadIdx.x == 0) {
+    uint32_t tmax = 0;
+#pragma unroll
+    for (int v = 0; v < SCORE_WAVES; ++v) tmax = max(tmax, wmax[v]);
+    counts[(size_t)unit * ntile_cap + blockIdx.x] = ((uint64_t)tmax << 32) | (ovf ? TILE_OVERFLOW : tot);
+  }
 }
 
 constexpr int SCORE_UNROLL = 2;
@@ -304,13 +404,13 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kp
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* scores = reinterpret_cast<float*>(ws + L.off_scores);
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws + L.off_cand);
-  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.off_counts);
+  uint64_t* counts = reinterpret_cast<uint64_t*>(ws + L.off_counts);
   const dim3 grid((unsigned)((s.capacity + TILE_ROWS - 1) / TILE_ROWS), (unsigned)L.units), block(SCORE_THREADS);
   const bool dense = (s.flags & SJSA_FLAG_WRITE_SCORES) != 0;
 #define SJSA_SCAN(RR, DD)                                                                          \
   score_kernel<RR, SCORE_UNROLL, DD><<<grid, block, 0, st>>>(kproj, qhat, tlow, seq_len, scores, cand, \
                                                              counts, s.n_kv_heads, s.capacity,       \
-                                                             L.score_stride, L.nseg_cap, L.cand_stride)
+                                                             L.score_stride, L.ntile_cap, L.cand_stride)
   switch (s.rank) {
     case 16: if (dense) SJSA_SCAN(16, true); else SJSA_SCAN(16, false); break;
     case 32: if (dense) SJSA_SCAN(32, true); else SJSA_SCAN(32, false); break;

@@ -9,22 +9,23 @@
 // Scores are compared as order-preserving u32 keys. One 1024-thread workgroup per
 // unit, three paths:
 //  * take-all: k >= n, positions 0..n-1.
-//  * candidates (the usual case): the scan kept, per 1024-row segment and in
-//    position order, every row whose key reached the unit's sampled threshold.
-//    If their count c satisfies k <= c <= CAND_CAP, the exact top k is among
-//    them: the segments are gathered into LDS in order, three radix rounds
-//    (12 + 10 + 10 bits) find the exact k-th key T and how many keys equal to T
-//    are taken (lowest positions first), and one ordered ballot compaction writes
-//    the ascending result.
+//  * candidates (the usual case): the scan kept, per tile and in position order,
+//    every row whose key reached the unit's sampled threshold. If their count c
+//    satisfies k <= c <= CAND_CAP (and no tile overflowed), the exact top k is
+//    among them: the tiles are gathered into LDS in order, radix rounds over the
+//    offsets key - (least candidate key), at most 12 bits each and usually two,
+//    find the exact k-th key T and how many keys equal to T are taken (lowest
+//    positions first), and one ordered ballot compaction writes the ascending
+//    result.
 //  * dense: exact selection over a full score row. Used for caller-provided
 //    scores, and when the sampled threshold misjudged the distribution (fewer than
-//    k candidates, or more than fit in LDS); the unit's scores are then recomputed
-//    first with arithmetic bit-identical to the scan's. The first radix digit's
-//    histogram locates the bin b1 of the k-th key; one ordered pass compacts the
-//    positions above b1 (list A) and the (key, position) pairs in b1 (list C) into
-//    LDS; C is resolved exactly and merged with A by rank. If A or C would not fit,
-//    the remaining digits are resolved by passes over the row and a final ordered
-//    pass writes the result.
+//    k candidates, more than fit in LDS, or more than a scan wave could stage);
+//    the unit's scores are then recomputed first with arithmetic bit-identical to
+//    the scan's. The first radix digit's histogram locates the bin b1 of the k-th
+//    key; one ordered pass compacts the positions above b1 (list A) and the (key,
+//    position) pairs in b1 (list C) into LDS; C is resolved exactly and merged with
+//    A by rank. If A or C would not fit, the remaining digits are resolved by
+//    passes over the row and a final ordered pass writes the result.
 #include "sjsa_device.h"
 #include "sjsa_internal.h"
 
@@ -71,19 +72,21 @@ __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
   return inc + before;
 }
 
-// Given a histogram of `nbins` bins (LDS) and 1 <= need <= total count, find the bin
-// b with count(bins > b) < need <= count(bins >= b). Results: misc[0] = b,
-// misc[1] = count above b, misc[2] = count in b. All threads call.
+// Given a histogram of `nbins` bins (LDS, nbins a power of two <= HIST_BINS) and
+// 1 <= need <= total count, find the bin b with count(bins > b) < need <=
+// count(bins >= b). Results: misc[0] = b, misc[1] = count above b, misc[2] = count
+// in b. All threads call.
 __device__ void find_bucket(const uint32_t* hist, int nbins, uint32_t need, SelShared& sh) {
-  const int per = nbins / SEL_THREADS;         // 4 or 1 bins per thread
+  const int per = (nbins + SEL_THREADS - 1) / SEL_THREADS;     // 4, 1 or (small nbins) 1
   const int lo = threadIdx.x * per;
+  const int cnt = max(0, min(per, nbins - lo));
   uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[lo + i];
+  for (int i = 0; i < cnt; ++i) local += hist[lo + i];
   uint32_t total;
   const uint32_t inc = block_incl_scan(local, sh.scan, &total);
   uint32_t above = total - inc;                // keys in bins above this thread's range
   if (above < need && need <= above + local) {
-    for (int i = per - 1; i >= 0; --i) {
+    for (int i = cnt - 1; i >= 0; --i) {
       const uint32_t c = hist[lo + i];
       if (above + c >= need) {
         sh.misc[0] = lo + i;
@@ -106,15 +109,16 @@ __device__ __forceinline__ f32x4 load4(const float* row, int64_t pos, int64_t la
 }
 
 // Ordered compaction helper: ranks of the flagged elements of one sub-chunk (each
-// thread holds EPT consecutive positions; lanes, then waves, are in position order).
+// thread holds NE consecutive positions; lanes, then waves, are in position order).
 // Returns this thread's first output slot relative to the sub-chunk start and the
 // sub-chunk total (through per-wave totals in wtot_row). One barrier.
-__device__ __forceinline__ uint32_t ballot_rank(const bool (&f)[EPT], uint32_t* wtot_row, uint32_t* total) {
+template <int NE>
+__device__ __forceinline__ uint32_t ballot_rank(const bool (&f)[NE], uint32_t* wtot_row, uint32_t* total) {
   const int wave = threadIdx.x >> 6;
   const uint64_t lt = lanemask_lt();
   uint32_t below = 0, wave_cnt = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
+  for (int e = 0; e < NE; ++e) {
     const uint64_t m = __ballot(f[e]);
     below += __popcll(m & lt);
     wave_cnt += __popcll(m);
@@ -133,47 +137,88 @@ __device__ __forceinline__ uint32_t ballot_rank(const bool (&f)[EPT], uint32_t* 
 }
 
 // Exact resolution of the threshold inside an LDS key list: the keys all share the
-// bits selected by `mask` (value `prefix`); `need` of them are to be taken. The
-// remaining bits are resolved 10 at a time (after an optional 12-bit first round).
-// Returns T; *needT receives how many keys equal to T are taken.
+// bits selected by `mask` (value `prefix`, the first 12-bit digit); `need` of them
+// are to be taken. The remaining 20 bits are resolved 10 at a time. Returns T;
+// *needT receives how many keys equal to T are taken.
 __device__ uint32_t lds_threshold(const uint32_t* keys, int cnt, uint32_t prefix, uint32_t mask, uint32_t need,
-                                  bool first12, SelShared& sh, uint32_t* needT) {
+                                  SelShared& sh, uint32_t* needT) {
   const int tid = threadIdx.x;
-  const int nrounds = first12 ? 3 : 2;
-  for (int round = 0; round < nrounds; ++round) {
-    const bool big = first12 && round == 0;
-    const int shift = big ? 20 : (round == nrounds - 1 ? 0 : 10);
-    const int nb = big ? HIST_BINS : 1024;
-    for (int i = tid; i < nb; i += SEL_THREADS) sh.hist[i] = 0u;
+  for (int round = 0; round < 2; ++round) {
+    const int shift = round == 0 ? 10 : 0;
+    for (int i = tid; i < 1024; i += SEL_THREADS) sh.hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < cnt; i += SEL_THREADS) {
       const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    find_bucket(sh.hist, nb, need, sh);
+    find_bucket(sh.hist, 1024, need, sh);
     need -= (uint32_t)sh.misc[1];
     prefix |= (uint32_t)sh.misc[0] << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
+    mask |= 1023u << shift;
   }
   *needT = need;
   return prefix;
 }
 
+// Exact threshold of an LDS key list whose keys all lie in [kmin, kmax]: the keys
+// are ranked by their offset key - kmin, whose significant bits are resolved at most
+// 12 at a time from the top, so the first histogram spreads the keys over up to
+// 4096 bins whatever part of the key range they occupy. When the bin holding rank
+// `need` is taken whole, the threshold stops there. Returns T and *needT such that
+// the selection is: keys above T, plus the first needT keys equal to T.
+__device__ uint32_t lds_threshold_range(const uint32_t* keys, int cnt, uint32_t kmin, uint32_t kmax,
+                                        uint32_t need, SelShared& sh, uint32_t* needT) {
+  const int tid = threadIdx.x;
+  int hi = 32 - __clz(kmax - kmin);           // significant bits of the offsets
+  uint32_t prefix = 0;                        // resolved bits hi.. of the k-th offset
+  while (hi > 0) {
+    const int shift = max(hi - 12, 0);
+    const int nb = 1 << (hi - shift);
+    for (int i = tid; i < nb; i += SEL_THREADS) sh.hist[i] = 0u;
+    __syncthreads();
+    const uint64_t want = (uint64_t)prefix >> hi;
+    for (int i = tid; i < cnt; i += SEL_THREADS) {
+      const uint32_t off = keys[i] - kmin;
+      if (((uint64_t)off >> hi) == want) atomicAdd(&sh.hist[(off >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bucket(sh.hist, nb, need, sh);
+    const uint32_t bin = (uint32_t)sh.misc[0];
+    const uint32_t above = (uint32_t)sh.misc[1];
+    const uint32_t inbin = (uint32_t)sh.misc[2];
+    need -= above;
+    prefix |= bin << shift;
+    hi = shift;
+    __syncthreads();                          // misc is rewritten by the next round
+    if (hi > 0 && inbin == need) {            // every key of the bin is taken
+      const uint32_t lo_key = kmin + prefix;  // smallest key the bin can hold
+      if (lo_key == 0u) { *needT = 0xffffffffu; return 0u; }
+      *needT = 0u;
+      return lo_key - 1u;
+    }
+  }
+  *needT = need;
+  return kmin + prefix;
+}
+
 // Ordered compaction of an LDS (key, position) list in position order: keep keys
 // above T, and the first needT keys equal to T. With to_lds the kept positions are
 // written back into pos_l[] (in place); otherwise to out[]. Returns the kept count.
+constexpr int CEPT = 8;                         // list entries per thread per compaction pass
+constexpr int CSUB = SEL_THREADS * CEPT;
+
 __device__ uint32_t compact_list(const uint32_t* key_l, int32_t* pos_l, int cnt, uint32_t T, uint32_t needT,
                                  bool take_all, bool to_lds, int32_t* out, SelShared& sh) {
   const int tid = threadIdx.x;
   uint32_t baseS = 0, baseEq = 0;
-  for (int c0 = 0; c0 < cnt; c0 += SUB) {
-    const int i0 = c0 + tid * EPT;
-    bool sel[EPT], eq[EPT];
-    int32_t pos[EPT];
-    uint32_t key[EPT];
+  for (int c0 = 0; c0 < cnt; c0 += CSUB) {
+    const int i0 = c0 + tid * CEPT;
+    bool sel[CEPT], eq[CEPT];
+    int32_t pos[CEPT];
+    uint32_t key[CEPT];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
+    for (int e = 0; e < CEPT; ++e) {
       const bool valid = i0 + e < cnt;
       key[e] = valid ? key_l[i0 + e] : 0u;
       pos[e] = valid ? pos_l[i0 + e] : 0;
@@ -183,7 +228,7 @@ __device__ uint32_t compact_list(const uint32_t* key_l, int32_t* pos_l, int cnt,
     const uint32_t req = ballot_rank(eq, sh.wtot[0], &totEq);
     uint32_t r = baseEq + req;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
+    for (int e = 0; e < CEPT; ++e) {
       const bool valid = i0 + e < cnt;
       if (take_all) sel[e] = valid;
       else if (eq[e]) { sel[e] = r < needT; ++r; }
@@ -194,7 +239,7 @@ __device__ uint32_t compact_list(const uint32_t* key_l, int32_t* pos_l, int cnt,
     __syncthreads();     // every thread has read its entries before any is overwritten
     uint32_t o = baseS + rs;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
+    for (int e = 0; e < CEPT; ++e) {
       if (sel[e]) {
         if (to_lds) pos_l[o] = pos[e];
         else out[o] = pos[e];
@@ -316,7 +361,7 @@ __device__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, 
     const bool take_all_c = need == (uint32_t)cntC;
     uint32_t T = 0, needT = need;
     if (!take_all_c)
-      T = lds_threshold(ckey, cntC, b1 << HIST_SHIFT, 0xfff00000u, need, false, sh, &needT);
+      T = lds_threshold(ckey, cntC, b1 << HIST_SHIFT, 0xfff00000u, need, sh, &needT);
     compact_list(ckey, cpos, cntC, T, needT, take_all_c, true, nullptr, sh);
     const int nS = kk - cntA;
 
@@ -407,8 +452,9 @@ template <int R>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
     int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const uint16_t* __restrict__ kproj,
-    const float* __restrict__ qhat, const uint64_t* __restrict__ cand, const uint32_t* __restrict__ counts,
-    float* __restrict__ dense, int64_t dense_stride, int64_t nseg_cap, int64_t cand_stride) {
+    const float* __restrict__ qhat, const uint32_t* __restrict__ tlow, const uint64_t* __restrict__ cand,
+    const uint64_t* __restrict__ counts, float* __restrict__ dense, int64_t dense_stride, int64_t ntile_cap,
+    int64_t cand_stride) {
   __shared__ SelShared sh;
   const int unit = blockIdx.x;
   const int b = unit / n_kv_heads;
@@ -428,64 +474,69 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     return;
   }
 
-  // Gather the candidates into LDS in position order. The scan packed them per
-  // (tile, wave): segment s (tile t = s / SEGS_PER_TILE, j = s % SEGS_PER_TILE, wave
-  // j % 4, i-th segment of that wave for i = j / 4) starts at entry
-  // t*TILE_ROWS + (j % 4)*TILE_ROWS/4 + (counts of that wave's earlier segments).
-  // Per chunk of SEL_THREADS segments (whole tiles): a block scan of the counts gives
-  // each segment's output offset, a short sum its offset inside its wave's region
-  // (both kept in LDS, reusing the histogram words), then every thread copies
-  // entries of the chunk's flat range, finding the owning segment by binary search.
-  // The loads are unconditional (clamped into the range), so a batch stays in flight.
-  constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
-  constexpr int SCAN_WAVES = 4;
-  static_assert(SEL_THREADS % SEGS_PER_TILE == 0, "chunks hold whole tiles");
+  // Gather the candidates into LDS in position order. Scan tile x (rows
+  // [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in position order, at entries
+  // [x*TILE_ROWS, ...); counts[x] holds their number (TILE_OVERFLOW when it could not
+  // keep them all) and their greatest key. Every candidate key is at least the
+  // scan's threshold key, so [threshold, greatest key] bounds the keys.
+  // Per chunk of CHUNK_T tiles, wave w owns TPW consecutive tiles; it loads their
+  // first SPEC*64 entries unconditionally (entries past the count are never used)
+  // together with the counts, so a single memory round trip serves the chunk; a
+  // block scan of the counts gives the output offsets. Tiles with more candidates
+  // copy the rest in a second loop.
+  constexpr int TPW = 2;
+  constexpr int SPEC = 4;
+  constexpr int CHUNK_T = SEL_WAVES * TPW;
+  const int lane = tid & 63, wave = tid >> 6;
   uint32_t* ckey = sh.buf;
   int32_t* cpos = reinterpret_cast<int32_t*>(sh.buf + CAND_CAP);
-  uint32_t* segoff = sh.hist;                     // SEL_THREADS + 1 output offsets
-  uint32_t* segcnt = sh.hist + 2048;              // SEL_THREADS counts, then region offsets
-  const int64_t nseg = (n + SEG_ROWS - 1) / SEG_ROWS;
-  const uint32_t* cnt_u = counts + (size_t)unit * nseg_cap;
+  uint32_t* toff = sh.hist;                       // CHUNK_T + 1 output offsets
+  const int64_t ntiles = (n + TILE_ROWS - 1) / TILE_ROWS;
+  const uint64_t* cnt_u = counts + (size_t)unit * ntile_cap;
   const uint64_t* cand_u = cand + (size_t)unit * cand_stride;
   uint32_t total = 0;
-  for (int64_t s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
-    const int64_t sg = s0 + tid;
-    const int nchunk = (int)min((int64_t)SEL_THREADS, nseg - s0);
-    const uint32_t c = sg < nseg ? cnt_u[sg] : 0u;
+  uint32_t kmax = 0u;                             // wave 0: greatest candidate key so far
+  bool ovf = false;
+  for (int64_t t0 = 0; t0 < ntiles; t0 += CHUNK_T) {
+    const uint64_t cw = cnt_u[min(t0 + min(tid, CHUNK_T - 1), ntiles - 1)];
+    const uint32_t c = (uint32_t)cw;
+    uint64_t v[TPW][SPEC];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int64_t t = min(t0 + wave * TPW + i, ntiles - 1);
+#pragma unroll
+      for (int e = 0; e < SPEC; ++e) v[i][e] = cand_u[t * TILE_ROWS + 64 * e + lane];
+    }
+    const bool own = tid < CHUNK_T && t0 + tid < ntiles;
+    ovf = ovf || (own && c == TILE_OVERFLOW);
+    if (wave == 0) kmax = max(kmax, wave_max_u32(own ? (uint32_t)(cw >> 32) : 0u));
     uint32_t chunk_total;
-    const uint32_t incl = block_incl_scan(c, sh.scan, &chunk_total);
-    segoff[tid + 1] = incl;
-    if (tid == 0) segoff[0] = 0u;
-    segcnt[tid] = c;
+    const uint32_t incl = block_incl_scan(own && c != TILE_OVERFLOW ? c : 0u, sh.scan, &chunk_total);
+    if (tid < CHUNK_T) toff[tid + 1] = incl;
+    if (tid == 0) toff[0] = 0u;
     __syncthreads();
-    // offset of this segment inside its wave's region, and the region's start
-    const int j = tid % SEGS_PER_TILE;
-    uint32_t roff = 0;
-    for (int jj = j % SCAN_WAVES; jj < j; jj += SCAN_WAVES) roff += segcnt[tid - j + jj];
-    const uint32_t src0 = (uint32_t)((s0 + tid) / SEGS_PER_TILE) * TILE_ROWS +
-                          (uint32_t)(j % SCAN_WAVES) * (TILE_ROWS / SCAN_WAVES) + roff;
-    __syncthreads();
-    segcnt[tid] = src0;
-    __syncthreads();
-    const uint32_t room = total < (uint32_t)CAND_CAP ? (uint32_t)CAND_CAP - total : 0u;
-    const uint32_t ncopy = min(chunk_total, room);
-    constexpr int GU = 4;
-    for (uint32_t f0 = 0; f0 < ncopy; f0 += SEL_THREADS * GU) {
-      uint64_t v[GU];
-      uint32_t dst[GU];
 #pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        const uint32_t f = min(f0 + (uint32_t)(u * SEL_THREADS + tid), ncopy - 1);
-        int lo = 0, hi = nchunk;                    // last segment with offset <= f
-        while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (segoff[mid] <= f) lo = mid; else hi = mid; }
-        v[u] = cand_u[segcnt[lo] + (f - segoff[lo])];
-        dst[u] = total + f;
+    for (int i = 0; i < TPW; ++i) {
+      const int tl = wave * TPW + i;
+      const uint32_t o = toff[tl];
+      const uint32_t ct = toff[tl + 1] - o;       // 0 for tiles past the end
+#pragma unroll
+      for (int e = 0; e < SPEC; ++e) {
+        const uint32_t j = (uint32_t)(64 * e + lane);
+        const uint32_t dst = total + o + j;
+        if (j < ct && dst < (uint32_t)CAND_CAP) {
+          const uint32_t key = (uint32_t)(v[i][e] >> 32);
+          ckey[dst] = key;
+          cpos[dst] = (int32_t)(uint32_t)v[i][e];
+        }
       }
-#pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        if (f0 + (uint32_t)(u * SEL_THREADS + tid) < ncopy) {
-          ckey[dst[u]] = (uint32_t)(v[u] >> 32);
-          cpos[dst[u]] = (int32_t)(uint32_t)v[u];
+      for (uint32_t j = SPEC * 64 + lane; j < ct; j += 64) {     // tiles with many candidates
+        const uint32_t dst = total + o + j;
+        if (dst < (uint32_t)CAND_CAP) {
+          const uint64_t x = cand_u[(t0 + tl) * TILE_ROWS + j];
+          const uint32_t key = (uint32_t)(x >> 32);
+          ckey[dst] = key;
+          cpos[dst] = (int32_t)(uint32_t)x;
         }
       }
     }
@@ -493,9 +544,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     __syncthreads();
   }
 
-  if (total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
+  const bool overflowed = __syncthreads_or(ovf) != 0;
+  if (!overflowed && total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
+    // key range of the candidates (for the first radix digit)
+    if (tid == 0) sh.misc[5] = (int32_t)kmax;
+    __syncthreads();
+    const uint32_t kmin = tlow[unit * 2];
+    kmax = (uint32_t)sh.misc[5];
     uint32_t needT;
-    const uint32_t T = lds_threshold(ckey, (int)total, 0u, 0u, (uint32_t)kk, true, sh, &needT);
+    const uint32_t T = lds_threshold_range(ckey, (int)total, kmin, kmax, (uint32_t)kk, sh, &needT);
     compact_list(ckey, cpos, (int)total, T, needT, false, false, out, sh);
     return;
   }
@@ -512,12 +569,13 @@ hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scor
                          hipStream_t st) {
   const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
   const uint64_t* cand = reinterpret_cast<const uint64_t*>(ws + L.off_cand);
-  const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + L.off_counts);
+  const uint64_t* counts = reinterpret_cast<const uint64_t*>(ws + L.off_counts);
+  const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* dense = reinterpret_cast<float*>(ws + L.off_scores);
   const dim3 grid((unsigned)L.units), block(SEL_THREADS);
 #define SJSA_SEL(RR)                                                                                   \
   select_kernel<RR><<<grid, block, 0, st>>>(scores, stride, seq_len, s.n_kv_heads, s.capacity, k, idx, \
-                                            kproj, qhat, cand, counts, dense, L.score_stride, L.nseg_cap,  \
+                                            kproj, qhat, tlow, cand, counts, dense, L.score_stride, L.ntile_cap,  \
                                             L.cand_stride)
   switch (s.rank) {
     case 16: SJSA_SEL(16); break;

@@ -105,15 +105,41 @@ __device__ __forceinline__ float dot8_bf16(const float* q, u32x4 w) {
   return a;
 }
 
-// Wave-wide (64 lanes) inclusive prefix sum of a u32.
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Wave-wide (64 lanes) inclusive prefix sum of a u32: DPP scans inside the four rows
+// of 16 lanes, then each row adds the totals of the rows before it (read from lanes
+// 15, 31 and 47). Every lane of the wave must be active.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v = row16_incl_scan(v);
+  const uint32_t t0 = readlane_u32(v, 15), t1 = readlane_u32(v, 31), t2 = readlane_u32(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
+// Wave-wide min / max (the result is uniform). Every lane must be active.
+__device__ __forceinline__ float wave_min_f32(float v) {
+  v = fminf(v, dpp<DPP_ROW_ROR8>(v));
+  v = fminf(v, dpp<DPP_ROW_ROR4>(v));
+  v = fminf(v, dpp<DPP_QUAD_XOR2>(v));
+  v = fminf(v, dpp<DPP_QUAD_XOR1>(v));
+  return fminf(fminf(readlane_f32(v, 0), readlane_f32(v, 16)), fminf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_ROW_ROR8>(v));
+  v = max(v, dpp_u32<DPP_ROW_ROR4>(v));
+  v = max(v, dpp_u32<DPP_QUAD_XOR2>(v));
+  v = max(v, dpp_u32<DPP_QUAD_XOR1>(v));
+  return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -158,15 +184,16 @@ __device__ __forceinline__ float transpose_reduce(float (&a)[LPR], int p) {
   }
 }
 
-// Score of one projected row by one lane: the r/8 partial dots are summed in the
-// balanced tree the transposed wave reduction uses, so identical rows get
-// bit-identical scores whichever code path computes them. q holds q_hat (r fp32).
+// Score of one projected row by one lane from its r/8 16-byte words: the partial
+// dots are summed in the balanced tree the transposed wave reduction uses, so
+// identical rows get bit-identical scores whichever code path computes them. q holds
+// q_hat (r fp32).
 template <int R>
-__device__ __forceinline__ float row_score(const float* q, const uint16_t* rowp) {
+__device__ __forceinline__ float row_score_words(const float* q, const u32x4 (&w)[R / 8]) {
   constexpr int LPR = R / 8;
   float a[LPR];
 #pragma unroll
-  for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(q + 8 * i, ld16(rowp + 8 * i));
+  for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(q + 8 * i, w[i]);
   if constexpr (LPR == 2) {
     return a[0] + a[1];
   } else if constexpr (LPR == 4) {
@@ -174,6 +201,14 @@ __device__ __forceinline__ float row_score(const float* q, const uint16_t* rowp)
   } else {
     return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
+}
+
+template <int R>
+__device__ __forceinline__ float row_score(const float* q, const uint16_t* rowp) {
+  u32x4 w[R / 8];
+#pragma unroll
+  for (int i = 0; i < R / 8; ++i) w[i] = ld16(rowp + 8 * i);
+  return row_score_words<R>(q, w);
 }
 
 }  // namespace sjsa

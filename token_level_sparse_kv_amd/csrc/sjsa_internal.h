@@ -14,8 +14,9 @@ constexpr int HIST_BINS = 4096;      // first radix digit: top 12 bits of the sc
 constexpr int HIST_SHIFT = 20;
 constexpr int QHAT_STRIDE = 64;      // floats reserved per unit for q_hat (r <= 64)
 constexpr int SEG_ROWS = 128;        // rows per scan segment (one wave iteration)
-constexpr int TILE_ROWS = 4096;      // rows per scan workgroup; candidate region of a workgroup
-constexpr int CAND_STAGE = 256;      // candidates a scan wave stages in LDS before writing
+constexpr int TILE_ROWS = 4096;      // rows per scan workgroup; one candidate region
+constexpr int CAND_STAGE = 512;      // candidates a scan wave can stage in LDS
+constexpr uint32_t TILE_OVERFLOW = 0xffffffffu;   // tile count: a wave's stage overflowed
 constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
 
 struct Layout {
@@ -23,7 +24,7 @@ struct Layout {
   int64_t score_stride = 0;   // floats per unit row of the score buffer
   int nsplit = 1;             // attention splits per unit
   int chunk = 0;              // selected indices per split
-  int64_t nseg_cap = 0;       // scan segments per unit row (capacity / SEG_ROWS, rounded up)
+  int64_t ntile_cap = 0;      // scan tiles per unit (capacity / TILE_ROWS, rounded up)
   int64_t cand_stride = 0;    // candidate entries per unit (capacity rounded up to TILE_ROWS)
   size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
   size_t scores_end = 0, total = 0;
