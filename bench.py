@@ -4,8 +4,9 @@
 A step is the whole hot path on one batch: append the current token (K, V and its
 projected scoring row), scoring prep, the full-context score scan, per-KV-head
 top-k, and gather-free attention with the split merge. Inputs are resident in HBM
-before timing starts. Each stage is bracketed by HIP events on the stream the
-kernels run on, so the scan kernel's own duration is measured in the timed region.
+before timing starts. Throughput comes from steps run back to back between one
+pair of events; a second timed pass brackets every stage with HIP events on the
+stream the kernels run on, which gives the scan kernel's own duration.
 
 Prints one JSON line. Default: --gpus 1 --steps 200 --warmup 20.
 """
