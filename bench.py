@@ -2,8 +2,8 @@
 """Benchmark one sparse decode step of the 128K batched-decode workload on one MI355X.
 
 A step is the whole hot path on one batch: append the current token (K, V and its
-projected scoring row), scoring prep, the full-context score scan, per-KV-head
-top-k, and gather-free attention with the split merge. Inputs are resident in HBM
+projected scoring row, done by the prep kernel), scoring prep, the full-context
+score scan, per-KV-head top-k, and gather-free attention with the split merge. Inputs are resident in HBM
 before timing starts. Throughput comes from steps run back to back between one
 pair of events; a second timed pass brackets every stage with HIP events on the
 stream the kernels run on, which gives the scan kernel's own duration.
@@ -143,24 +143,23 @@ def main():
     t_setup = time.time() - t_setup
 
     def step(i, ev=None):
+        # the stage calls of sjsa_decode_step_append: the prep kernel appends the new
+        # token (K, V and projected rows), then scan, select, attend + merge
         q = q_sets[i % q_sets.shape[0]]
         if ev is not None:
             ev[0].record()
-        sj.append_kv(k_new, v_new, M, pos_new, K, V, Kp)
+        sj.prep_append(shape, k_new, v_new, pos_new, q, K, V, M, Kp, seq_len, k, ws)
         if ev is not None:
             ev[1].record()
-        sj.prep(shape, q, M, Kp, seq_len, k, ws)
-        if ev is not None:
-            ev[2].record()
         sj.scan(shape, Kp, seq_len, ws)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
         sj.select(shape, Kp, seq_len, k, ws, idx=idx)
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
         sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
         if ev is not None:
-            ev[5].record()
+            ev[4].record()
 
     for i in range(args.warmup):
         step(i)
@@ -181,12 +180,12 @@ def main():
     # stages, all on the stream the kernels run on (torch's current stream); each
     # interval also holds the launch latency of its first kernel, so these figures
     # slightly overstate the kernels' own durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    names = ["append", "prep", "scan", "select", "attend"]
+    names = ["append+prep", "scan", "select", "attend"]
     stage_ms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, nm in enumerate(names)}
 
     tb = step_bytes(B, Hkv, G, d, r, n, k)

@@ -121,6 +121,25 @@ int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, cons
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * A decode step that first appends the step's new token: the same as
+ * sjsa_append_kv with n_new = 1 followed by sjsa_decode_step, with identical
+ * results (the K, V and Kproj rows written are bit-identical to the append
+ * call's), but the append is done by the first kernel of the step instead of a
+ * launch of its own. Source: JSSA article, section 局限 (the current token is
+ * appended first and then competes like any other position) and section
+ * 投影打分缓存与校准成本 (the scoring cache is extended on append).
+ *   k_new, v_new [B, H_kv, 1, d] bf16; pos [B] int32: slot of the new token (a
+ *   slot outside [0, cap) writes nothing); seq_len normally pos + 1.
+ *   Other arguments as sjsa_decode_step; K, V and Kproj are written.
+ * Errors: as sjsa_decode_step.
+ */
+int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const void* v_new,
+                            const int32_t* pos, const void* q, void* K, void* V, void* Kproj,
+                            const float* M, const int32_t* seq_len, int32_t k, float sm_scale,
+                            void* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * Stage 1+2 of the step: scoring prep (q_bar, q_hat; section 打分误差的定义)
  * and the full-context score scan over Kproj (section 原理详解(二): scoring
  * still scans every candidate position). The scan keeps, per (b, h), only the
@@ -141,6 +160,12 @@ int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const 
  * scan over Kproj). Same workspace rules as sjsa_score. */
 int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, const void* Kproj,
               const int32_t* seq_len, int32_t k, void* workspace, size_t workspace_bytes, void* stream);
+/* sjsa_prep that first appends the step's new token, as sjsa_decode_step_append
+ * does (arguments as there). */
+int sjsa_prep_append(const sjsa_shape* shape, const void* k_new, const void* v_new, const int32_t* pos,
+                     const void* q, void* K, void* V, void* Kproj, const float* M,
+                     const int32_t* seq_len, int32_t k, void* workspace, size_t workspace_bytes,
+                     void* stream);
 int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
               size_t workspace_bytes, void* stream);
 

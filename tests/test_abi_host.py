@@ -111,6 +111,25 @@ def test_stage_validation():
         assert isinstance(L.sjsa_status_string(st), bytes)
 
 
+def test_fused_append_validation():
+    L = sj.lib()
+    s = _shape()
+    f = ctypes.c_void_p(FAKE)
+    args = [f] * 9                              # k_new, v_new, pos, q, K, V, Kproj, M, seq_len
+    bad = list(args)
+    bad[0] = None
+    assert L.sjsa_decode_step_append(ctypes.byref(s), *bad, 16, 0.0, f, f, f, 1 << 30, None) == -1
+    bad = list(args)
+    bad[2] = ctypes.c_void_p(FAKE + 2)          # pos needs 4-byte alignment
+    assert L.sjsa_decode_step_append(ctypes.byref(s), *bad, 16, 0.0, f, f, f, 1 << 30, None) == -7
+    assert L.sjsa_decode_step_append(ctypes.byref(s), *args, 0, 0.0, f, f, f, 1 << 30, None) == -4
+    assert L.sjsa_decode_step_append(ctypes.byref(s), *args, 16, 0.0, f, f, f, 1024, None) == -5
+    assert L.sjsa_prep_append(ctypes.byref(s), *args, 16, f, 1024, None) == -5
+    bad = list(args)
+    bad[4] = None
+    assert L.sjsa_prep_append(ctypes.byref(s), *bad, 16, f, 1 << 30, None) == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 4, 128, dtype=torch.bfloat16)

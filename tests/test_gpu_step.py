@@ -168,9 +168,9 @@ def test_candidate_overflow_falls_back_exactly():
 
 
 def test_candidate_underflow_falls_back_exactly():
-    # every other row the prep stage samples (positions s*n/2048, s even) scores high,
-    # all others low: the sampled threshold lands on the high score, and only 1024
-    # rows (fewer than k) reach it
+    # the prep stage samples 1024 pairs of adjacent rows (2*floor(i*n/2048) and the row
+    # after it); the first row of every pair scores high, all others low: the sampled
+    # threshold lands on the high score, and only 1024 rows (fewer than k) reach it
     say("step candidate underflow -> exact fallback")
     n, k = 40000, 2000
     wl = workloads.gaussian(1, 1, 4, 128, 16, n, k, seed=26, device="cuda")
@@ -182,8 +182,8 @@ def test_candidate_underflow_falls_back_exactly():
     from oracle.numerics import round_to_bf16
     high = round_to_bf16(high)
     kp = np.tile(low, (1, 1, n, 1)).astype(np.uint16)
-    sampled = (np.arange(2048, dtype=np.int64) * n) // 2048
-    kp[0, 0, sampled[::2]] = high
+    first_of_pair = 2 * ((np.arange(1024, dtype=np.int64) * n) // 2048)
+    kp[0, 0, first_of_pair] = high
     _ties_check(wl, kp, k, "underflow")
 
 

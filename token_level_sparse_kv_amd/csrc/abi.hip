@@ -120,6 +120,33 @@ int sjsa_append_kv(const sjsa_shape* shape, const void* k_new, const void* v_new
                                  (uint16_t*)K, (uint16_t*)V, (uint16_t*)Kproj, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the fused append entry points (one new token per sequence).
+int check_append_one(const void* k_new, const void* v_new, const int32_t* pos, const void* K, const void* V,
+                     const void* Kproj) {
+  if (!k_new || !v_new || !pos || !K || !V || !Kproj) return SJSA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4)) return SJSA_ERR_ALIGN;
+  return SJSA_OK;
+}
+
+PrepAppend make_append(const void* k_new, const void* v_new, const int32_t* pos, void* K, void* V, void* Kproj) {
+  PrepAppend ap;
+  ap.k_new = (const uint16_t*)k_new;
+  ap.v_new = (const uint16_t*)v_new;
+  ap.pos = pos;
+  ap.K = (uint16_t*)K;
+  ap.V = (uint16_t*)V;
+  ap.Kproj = (uint16_t*)Kproj;
+  return ap;
+}
+
+}  // namespace
+
+extern "C" {
+
 int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const float* M,
                const int32_t* seq_len, int32_t k, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
@@ -151,6 +178,24 @@ int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, const void
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
   return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k,
                                (unsigned char*)workspace, (hipStream_t)stream));
+}
+
+int sjsa_prep_append(const sjsa_shape* shape, const void* k_new, const void* v_new, const int32_t* pos,
+                     const void* q, void* K, void* V, void* Kproj, const float* M, const int32_t* seq_len,
+                     int32_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if ((st = check_append_one(k_new, v_new, pos, K, V, Kproj))) return st;
+  if (!q || !M || !seq_len || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(M, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Kproj, 16) ||
+      !aligned(seq_len, 4) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  const PrepAppend ap = make_append(k_new, v_new, pos, K, V, Kproj);
+  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k,
+                               (unsigned char*)workspace, (hipStream_t)stream, &ap));
 }
 
 int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
@@ -230,6 +275,33 @@ int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, cons
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s);
+  if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
+  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx, ws, s);
+  if (e == hipSuccess)
+    e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
+                      resolve_scale(sm_scale), out, ws, s);
+  return status_of(e);
+}
+
+int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const void* v_new, const int32_t* pos,
+                            const void* q, void* K, void* V, void* Kproj, const float* M, const int32_t* seq_len,
+                            int32_t k, float sm_scale, void* out, int32_t* idx, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if ((st = check_append_one(k_new, v_new, pos, K, V, Kproj))) return st;
+  if (!q || !M || !seq_len || !out || !idx || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Kproj, 16) || !aligned(M, 16) ||
+      !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(out, 16) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  if (!isfinite(sm_scale)) return SJSA_ERR_DIMS;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const PrepAppend ap = make_append(k_new, v_new, pos, K, V, Kproj);
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s, &ap);
   if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
   if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx, ws, s);
   if (e == hipSuccess)

@@ -3,8 +3,7 @@
 // Source: JSSA article, section 投影打分缓存与校准成本 (the scoring cache Kproj =
 // K M^T is kept next to the original KV cache) and section 组件级拆解 (projecting
 // each new key is the pipeline's cheapest stage).
-#include "sjsa_device.h"
-#include "sjsa_internal.h"
+#include "key_proj.h"
 
 namespace sjsa {
 namespace {
@@ -13,19 +12,18 @@ constexpr int APPEND_THREADS = 256;
 constexpr int APPEND_ROWS = 64;                 // token rows per workgroup
 
 // grid = (ceil(n_new / APPEND_ROWS), B * H_kv). Threads copy the workgroup's K and
-// V rows (16 bytes each), then project them: output i of a projected row is split
-// over TPO = 256 / R lanes, lane `part` owning channels part*CH .. part*CH + CH - 1
-// of basis row i, which it holds in registers for all the workgroup's rows. The
-// TPO partial dots (each in channel order) are combined with DPP lane moves, so a
-// projected row's bits do not depend on how many tokens one call appends.
+// V rows (16 bytes each), then project them with the KeyProj layout, each thread
+// holding its basis slice in registers for all the workgroup's rows, so a projected
+// row's bits do not depend on how many tokens one call appends.
 template <int R>
 __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n_new,
     const float* __restrict__ M, const int32_t* __restrict__ pos,
     uint16_t* __restrict__ K, uint16_t* __restrict__ V, uint16_t* __restrict__ Kproj,
     int n_kv_heads, int64_t cap) {
-  constexpr int TPO = APPEND_THREADS / R;      // lanes per output (16, 8 or 4)
-  constexpr int CH = HEAD_DIM / TPO;           // channels per lane (8, 16 or 32)
+  using KP = KeyProj<R>;
+  static_assert(KP::THREADS == APPEND_THREADS, "one projection layout");
+  constexpr int TPO = KP::TPO, CH = KP::CH;
   const int unit = blockIdx.y;
   const int b = unit / n_kv_heads;
   const int h = unit - b * n_kv_heads;
@@ -46,35 +44,12 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
   }
 
   const int i = tid / TPO, part = tid % TPO;
-  const f32x4* m4 = reinterpret_cast<const f32x4*>(M + ((size_t)h * R + i) * HEAD_DIM + part * CH);
   f32x4 mv[CH / 4];
-#pragma unroll
-  for (int c = 0; c < CH / 4; ++c) mv[c] = m4[c];
-  const uint16_t* kbase = k_new + src0 + part * CH;
+  KP::load_basis(M + (size_t)h * R * HEAD_DIM, tid, mv);
   for (int r = 0; r < rows; ++r) {
     u32x4 kv[CH / 8];
-#pragma unroll
-    for (int c = 0; c < CH / 8; ++c) kv[c] = ld16(kbase + (size_t)r * HEAD_DIM + c * 8);
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH / 8; ++c) {
-      const f32x4 m0 = mv[2 * c], m1 = mv[2 * c + 1];
-      acc = fmaf(m0.x, bf_lo(kv[c].x), acc);
-      acc = fmaf(m0.y, bf_hi(kv[c].x), acc);
-      acc = fmaf(m0.z, bf_lo(kv[c].y), acc);
-      acc = fmaf(m0.w, bf_hi(kv[c].y), acc);
-      acc = fmaf(m1.x, bf_lo(kv[c].z), acc);
-      acc = fmaf(m1.y, bf_hi(kv[c].z), acc);
-      acc = fmaf(m1.z, bf_lo(kv[c].w), acc);
-      acc = fmaf(m1.w, bf_hi(kv[c].w), acc);
-    }
-    if constexpr (TPO == 16) {
-      acc = row16_sum(acc);
-    } else {
-      acc += dpp<DPP_QUAD_XOR1>(acc);
-      acc += dpp<DPP_QUAD_XOR2>(acc);
-      if constexpr (TPO == 8) acc += swz_xor4(acc);
-    }
+    KP::load_key(k_new + src0 + (size_t)r * HEAD_DIM, tid, kv);
+    const float acc = KP::dot(mv, kv);
     const int64_t p = p0 + r;
     if (part == 0 && p >= 0 && p < cap)
       Kproj[((size_t)unit * cap + p) * R + i] = (uint16_t)f32_to_bf16_rne(acc);

@@ -17,8 +17,7 @@
 //              full score of one row. Rows whose score key reaches the threshold
 //              are kept as candidates for the top-k stage (and, on request, every
 //              score is stored).
-#include "sjsa_device.h"
-#include "sjsa_internal.h"
+#include "key_proj.h"
 
 namespace sjsa {
 namespace {
@@ -50,12 +49,21 @@ __device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
   return inc + before;
 }
 
+// Row of sample s (0 <= s < min(SAMPLES, n)): every row when n <= SAMPLES; else the
+// samples come in adjacent pairs (2i, 2i + 1 share a 128-byte cache line whenever a
+// projected row is at most 64 bytes), the pairs evenly spaced over the sequence.
+__device__ __forceinline__ int64_t sample_row(int s, int64_t n) {
+  if (n <= SAMPLES) return s;
+  return 2 * (((int64_t)(s >> 1) * n) / SAMPLES) + (s & 1);
+}
+
 // One workgroup per (b, h).
 //  * q_bar in fp32 (sum in head order, then divide by G) and q_hat = M_h q_bar: output
 //    i is split over 16 lanes of 8 channels each (fp32 partial dots, DPP row sum).
-//  * Threshold for the scan: the scores of SAMPLES evenly spaced rows (all rows when
-//    n <= SAMPLES) are binned linearly between their least and greatest finite value
-//    (+inf in the top bin, -inf and NaN left out); the bin that holds the sample of
+//  * Threshold for the scan: the scores of SAMPLES rows (evenly spaced pairs of
+//    adjacent rows; all rows when n <= SAMPLES) are binned linearly between their
+//    least and greatest finite value (+inf in the top bin, -inf and NaN left out);
+//    the bin that holds the sample of
 //    rank m (see below) is found, and the least key in it becomes the unit's
 //    candidate threshold, so at least m samples reach it. The exact top k is among
 //    the rows that reach it unless the sample misjudges the distribution, a case the
@@ -63,11 +71,17 @@ __device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
 //    work the select stage does, never its result.
 //  * mode: 1 when k >= n (every position is selected and the scan has no work).
 // The sample rows are loaded first, so their latency overlaps the q_hat work.
-template <int R>
+//
+// With APPEND the workgroup first appends its unit's new token (decode: one token
+// per sequence at slot pos[b]): threads 256..287 copy its K and V rows and threads
+// 0..255 write its projected row with the KeyProj layout (bit-identical to the
+// append kernel). A sample that lands on that slot may read the row before or
+// after the write; either way only the threshold moves, never the result.
+template <int R, bool APPEND>
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ M, const uint16_t* __restrict__ kproj,
+    const uint16_t* __restrict__ q, const float* __restrict__ M, const uint16_t* kproj,
     const int32_t* __restrict__ seq_len, int k, float* __restrict__ qhat, uint32_t* __restrict__ tlow,
-    int n_kv_heads, int group, int64_t cap) {
+    int n_kv_heads, int group, int64_t cap, PrepAppend ap) {
   constexpr int LPR = R / 8;                          // 16-byte words per Kproj row
   constexpr int RPL = 64 / LPR;                       // samples per wave-wide load
   constexpr int BATCHES = SAMPLES / PREP_THREADS;     // 64-sample batches per wave (= samples per lane)
@@ -81,6 +95,26 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
   const int b = unit / n_kv_heads;
   const int h = unit - b * n_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  using KP = KeyProj<R>;
+  static_assert(KP::THREADS + 32 <= PREP_THREADS, "projection and row copies fit the workgroup");
+  f32x4 amv[KP::CH / 4];
+  u32x4 akv[KP::CH / 8];
+  int64_t apos = -1;
+  if constexpr (APPEND) {
+    apos = ap.pos[b];
+    const uint16_t* krow = ap.k_new + (size_t)unit * HEAD_DIM;
+    if (tid < KP::THREADS) {
+      KP::load_basis(M + (size_t)h * R * HEAD_DIM, tid, amv);
+      KP::load_key(krow, tid, akv);
+    } else if (tid < KP::THREADS + 32 && apos >= 0 && apos < cap) {
+      const int part = tid & 15;
+      const bool is_v = (tid - KP::THREADS) >= 16;
+      const u32x4 x = ld16((is_v ? ap.v_new : ap.k_new) + (size_t)unit * HEAD_DIM + part * 8);
+      *reinterpret_cast<u32x4*>((is_v ? ap.V : ap.K) + ((size_t)unit * cap + apos) * HEAD_DIM + part * 8) = x;
+    }
+  }
+
   const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
   const int64_t kk = min((int64_t)k, n);
   const bool sampling = kk < n;                       // uniform over the workgroup
@@ -99,7 +133,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 #pragma unroll
       for (int i = 0; i < LPR; ++i) {
         const int sidx = min(64 * (wave + t * PREP_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
-        const int64_t pos = (n <= SAMPLES) ? sidx : (int64_t)sidx * n / SAMPLES;
+        const int64_t pos = sample_row(sidx, n);
         w[t][i] = ld16(base + pos * R);
       }
     }
@@ -144,6 +178,13 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     if (part == 0 && i < R) {
       qhat[(size_t)unit * QHAT_STRIDE + i] = acc;
       sqh[i] = acc;
+    }
+  }
+  if constexpr (APPEND) {
+    if (tid < KP::THREADS) {                          // whole waves: the DPP combine needs them
+      const float acc = KP::dot(amv, akv);
+      if (tid % KP::TPO == 0 && apos >= 0 && apos < cap)
+        ap.Kproj[((size_t)unit * cap + apos) * R + tid / KP::TPO] = (uint16_t)f32_to_bf16_rne(acc);
     }
   }
   for (int i = tid; i < PREP_BINS; i += PREP_THREADS) shist[i] = 0u;
@@ -385,16 +426,24 @@ constexpr int SCORE_UNROLL = 2;
 }  // namespace
 
 hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
-                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st) {
+                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
+                       const PrepAppend* ap) {
   float* qhat = reinterpret_cast<float*>(ws + L.off_qhat);
   uint32_t* tlow = reinterpret_cast<uint32_t*>(ws + L.off_tlow);
   const dim3 grid((unsigned)L.units), block(PREP_THREADS);
+  const PrepAppend none{};
+#define SJSA_PREP(RR)                                                                                   \
+  if (ap) prep_kernel<RR, true><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads,  \
+                                                          s.group, s.capacity, *ap);                      \
+  else prep_kernel<RR, false><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads,   \
+                                                        s.group, s.capacity, none)
   switch (s.rank) {
-    case 16: prep_kernel<16><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads, s.group, s.capacity); break;
-    case 32: prep_kernel<32><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads, s.group, s.capacity); break;
-    case 64: prep_kernel<64><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads, s.group, s.capacity); break;
+    case 16: SJSA_PREP(16); break;
+    case 32: SJSA_PREP(32); break;
+    case 64: SJSA_PREP(64); break;
     default: return hipErrorInvalidValue;
   }
+#undef SJSA_PREP
   return hipGetLastError();
 }
 

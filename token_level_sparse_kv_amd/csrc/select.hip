@@ -45,11 +45,16 @@ constexpr int C_CAP = 12288;
 constexpr int CAND_CAP = LDS_WORDS / 2;         // candidate path: ckey | cpos
 static_assert(A_CAP + 2 * C_CAP == LDS_WORDS, "dense lists fill the list storage");
 
+constexpr int HIST2_BINS = 2048;                // second histogram (candidate path, round 1)
+
 struct SelShared {
   uint32_t hist[HIST_BINS];
   uint32_t buf[LDS_WORDS];
+  uint32_t hist2[HIST2_BINS];
+  uint32_t toff[64];                 // candidate path: tile output offsets of a chunk
   uint32_t wtot[2][2 * SEL_WAVES];   // [buffer][A totals of waves | C totals of waves]
   uint32_t scan[SEL_WAVES];
+  uint32_t scan2[SEL_WAVES];
   int32_t misc[8];
 };
 
@@ -161,42 +166,92 @@ __device__ uint32_t lds_threshold(const uint32_t* keys, int cnt, uint32_t prefix
   return prefix;
 }
 
+// find_bucket with two barriers (the wave totals go through sh.scan2, which the
+// next call rewrites only after two more barriers).
+__device__ void find_bucket_fast(const uint32_t* hist, int nbins, uint32_t need, SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per = (nbins + SEL_THREADS - 1) / SEL_THREADS;
+  const int lo = threadIdx.x * per;
+  const int cnt = max(0, min(per, nbins - lo));
+  uint32_t local = 0;
+  for (int i = 0; i < cnt; ++i) local += hist[lo + i];
+  const uint32_t inc = wave_incl_scan(local);
+  if (lane == 63) sh.scan2[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const uint32_t t = sh.scan2[w];
+    before += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  uint32_t above = tot - (inc + before);       // keys in bins above this thread's range
+  if (above < need && need <= above + local) {
+    for (int i = cnt - 1; i >= 0; --i) {
+      const uint32_t c = hist[lo + i];
+      if (above + c >= need) {
+        sh.misc[0] = lo + i;
+        sh.misc[1] = (int32_t)above;
+        sh.misc[2] = (int32_t)c;
+        break;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+}
+
 // Exact threshold of an LDS key list whose keys all lie in [kmin, kmax]: the keys
-// are ranked by their offset key - kmin, whose significant bits are resolved at most
-// 12 at a time from the top, so the first histogram spreads the keys over up to
-// 4096 bins whatever part of the key range they occupy. When the bin holding rank
-// `need` is taken whole, the threshold stops there. Returns T and *needT such that
-// the selection is: keys above T, plus the first needT keys equal to T.
+// are ranked by their offset key - kmin, whose significant bits are resolved from
+// the top, 12 at a time in sh.hist and 11 in sh.hist2 for the second round (both
+// must be zero on entry, so that the first two rounds need no clearing pass), so
+// the first histogram spreads the keys over up to 4096 bins whatever part of the
+// key range they occupy. When the bin holding rank `need` is taken whole, the
+// threshold stops there. Returns T and *needT such that the selection is: keys
+// above T, plus the first needT keys equal to T; *all_eq is set when that takes
+// every key equal to T.
 __device__ uint32_t lds_threshold_range(const uint32_t* keys, int cnt, uint32_t kmin, uint32_t kmax,
-                                        uint32_t need, SelShared& sh, uint32_t* needT) {
+                                        uint32_t need, SelShared& sh, uint32_t* needT, bool* all_eq) {
+  *all_eq = false;
   const int tid = threadIdx.x;
   int hi = 32 - __clz(kmax - kmin);           // significant bits of the offsets
   uint32_t prefix = 0;                        // resolved bits hi.. of the k-th offset
-  while (hi > 0) {
-    const int shift = max(hi - 12, 0);
+  for (int round = 0; hi > 0; ++round) {
+    const bool second = round == 1;
+    const int shift = max(hi - (second ? 11 : 12), 0);
     const int nb = 1 << (hi - shift);
-    for (int i = tid; i < nb; i += SEL_THREADS) sh.hist[i] = 0u;
-    __syncthreads();
+    uint32_t* hist = second ? sh.hist2 : sh.hist;
+    if (round >= 2) {                         // rare: a third round reuses sh.hist
+      for (int i = tid; i < nb; i += SEL_THREADS) hist[i] = 0u;
+      __syncthreads();
+    }
     const uint64_t want = (uint64_t)prefix >> hi;
-    for (int i = tid; i < cnt; i += SEL_THREADS) {
-      const uint32_t off = keys[i] - kmin;
-      if (((uint64_t)off >> hi) == want) atomicAdd(&sh.hist[(off >> shift) & (uint32_t)(nb - 1)], 1u);
+    // KU keys per thread per batch: all their LDS reads are issued before any atomic
+    constexpr int KU = 8;
+    for (int i0 = tid; i0 < cnt; i0 += KU * SEL_THREADS) {
+      uint32_t off[KU];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) off[u] = keys[min(i0 + u * SEL_THREADS, cnt - 1)] - kmin;
+#pragma unroll
+      for (int u = 0; u < KU; ++u)
+        if (i0 + u * SEL_THREADS < cnt && ((uint64_t)off[u] >> hi) == want)
+          atomicAdd(&hist[(off[u] >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    find_bucket(sh.hist, nb, need, sh);
+    find_bucket_fast(hist, nb, need, sh);
     const uint32_t bin = (uint32_t)sh.misc[0];
     const uint32_t above = (uint32_t)sh.misc[1];
     const uint32_t inbin = (uint32_t)sh.misc[2];
     need -= above;
     prefix |= bin << shift;
     hi = shift;
-    __syncthreads();                          // misc is rewritten by the next round
     if (hi > 0 && inbin == need) {            // every key of the bin is taken
       const uint32_t lo_key = kmin + prefix;  // smallest key the bin can hold
       if (lo_key == 0u) { *needT = 0xffffffffu; return 0u; }
       *needT = 0u;
       return lo_key - 1u;
     }
+    if (hi == 0) *all_eq = inbin == need;     // the last bin holds one key value
   }
   *needT = need;
   return kmin + prefix;
@@ -248,6 +303,81 @@ __device__ uint32_t compact_list(const uint32_t* key_l, int32_t* pos_l, int cnt,
     }
     baseS += totS;
     baseEq += totEq;
+    __syncthreads();
+  }
+  return baseS;
+}
+
+// Ranks for a strided ordered compaction: element e of thread t in a pass is list
+// entry e*SEL_THREADS + t, so consecutive lanes touch consecutive LDS words (no bank
+// conflicts) and the list order is (e, wave, lane). A ballot per e gives the order
+// inside a wave; the counts of every (e, wave) are scanned by wave 0 in that order.
+// rank[e] receives the output slot of flagged element e relative to the pass start,
+// *total the pass's flagged count. `table` needs NE*SEL_WAVES + 1 words. Two barriers.
+template <int NE>
+__device__ __forceinline__ void strided_rank(const bool (&f)[NE], uint32_t (&rank)[NE], uint32_t* table,
+                                             uint32_t* total) {
+  static_assert(NE * SEL_WAVES == 128, "wave 0 scans two counts per lane");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t lt = lanemask_lt();
+  uint64_t m[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) m[e] = __ballot(f[e]);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) table[e * SEL_WAVES + wave] = (uint32_t)__popcll(m[e]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t a = table[2 * lane], c = table[2 * lane + 1];
+    const uint32_t incl = wave_incl_scan(a + c);
+    table[2 * lane] = incl - (a + c);
+    table[2 * lane + 1] = incl - c;
+    if (lane == 63) table[NE * SEL_WAVES] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < NE; ++e) rank[e] = table[e * SEL_WAVES + wave] + (uint32_t)__popcll(m[e] & lt);
+  *total = table[NE * SEL_WAVES];
+}
+
+// Ordered compaction of the candidate list in place: keep keys above T, and the
+// first needT keys equal to T (all of them when all_eq). pos_l[0 .. kept) receives
+// the kept positions in list order. Returns the kept count.
+__device__ uint32_t compact_candidates(const uint32_t* key_l, int32_t* pos_l, int cnt, uint32_t T,
+                                       uint32_t needT, bool all_eq, SelShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t* table = sh.hist;
+  uint32_t* table2 = sh.hist + 256;
+  uint32_t baseS = 0, baseEq = 0;
+  for (int c0 = 0; c0 < cnt; c0 += CSUB) {
+    bool sel[CEPT], eq[CEPT];
+    int32_t pos[CEPT];
+#pragma unroll
+    for (int e = 0; e < CEPT; ++e) {
+      const int i = c0 + e * SEL_THREADS + tid;
+      const bool valid = i < cnt;
+      const uint32_t key = valid ? key_l[i] : 0u;
+      pos[e] = valid ? pos_l[i] : 0;
+      eq[e] = valid && key == T;
+      sel[e] = valid && key > T;
+    }
+    if (all_eq) {
+#pragma unroll
+      for (int e = 0; e < CEPT; ++e) sel[e] = sel[e] || eq[e];
+    } else {
+      uint32_t req[CEPT], totEq;
+      strided_rank(eq, req, table2, &totEq);
+#pragma unroll
+      for (int e = 0; e < CEPT; ++e) sel[e] = sel[e] || (eq[e] && baseEq + req[e] < needT);
+      baseEq += totEq;
+    }
+    uint32_t rs[CEPT], totS;
+    strided_rank(sel, rs, table, &totS);    // its barriers also order every read above before the writes
+#pragma unroll
+    for (int e = 0; e < CEPT; ++e)
+      if (sel[e]) pos_l[baseS + rs[e]] = pos[e];
+    baseS += totS;
     __syncthreads();
   }
   return baseS;
@@ -459,13 +589,48 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const int unit = blockIdx.x;
   const int b = unit / n_kv_heads;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  // Candidates. Scan tile x (rows [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in
+  // position order, at entries [x*TILE_ROWS, ...); counts[x] holds their number
+  // (TILE_OVERFLOW when it could not keep them all) and their greatest key. Every
+  // candidate key is at least the scan's threshold key, so [threshold, greatest
+  // key] bounds the keys. Tiles are gathered in chunks of CHUNK_T; wave w owns TPW
+  // consecutive tiles of a chunk and loads their first SPEC*64 entries
+  // unconditionally (entries past the count are never used) together with the
+  // counts, so one memory round trip serves a chunk. The first chunk's loads are
+  // issued before the sequence length is known (tiles clamped to the capacity), so
+  // they overlap the kernel's first load; later chunks clamp to the sequence.
+  constexpr int TPW = 2;
+  constexpr int SPEC = 4;
+  constexpr int CHUNK_T = SEL_WAVES * TPW;
+  const uint64_t* cnt_u = counts + (size_t)unit * ntile_cap;
+  const uint64_t* cand_u = cand + (size_t)unit * cand_stride;
+  uint64_t cw = 0;
+  uint64_t v[TPW][SPEC];
+  auto load_chunk = [&](int64_t t0, int64_t tiles) {
+    cw = cnt_u[min(t0 + min(tid, CHUNK_T - 1), tiles - 1)];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int64_t t = min(t0 + wave * TPW + i, tiles - 1);
+#pragma unroll
+      for (int e = 0; e < SPEC; ++e) v[i][e] = cand_u[t * TILE_ROWS + 64 * e + lane];
+    }
+  };
+  const bool cand_path = scores == nullptr;
+  uint32_t tkey = 0;
+  if (cand_path) {
+    tkey = tlow[unit * 2];
+    load_chunk(0, ntile_cap);
+  }
+
   const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
   const int kk = (int)min((int64_t)k, n);
   int32_t* out = idx + (size_t)unit * k;
 
   for (int i = kk + tid; i < k; i += SEL_THREADS) out[i] = -1;
   if (kk == 0) return;
-  if (scores != nullptr) {
+  if (!cand_path) {
     select_dense(scores + (size_t)unit * stride, n, kk, out, sh);
     return;
   }
@@ -474,42 +639,26 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     return;
   }
 
-  // Gather the candidates into LDS in position order. Scan tile x (rows
-  // [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in position order, at entries
-  // [x*TILE_ROWS, ...); counts[x] holds their number (TILE_OVERFLOW when it could not
-  // keep them all) and their greatest key. Every candidate key is at least the
-  // scan's threshold key, so [threshold, greatest key] bounds the keys.
-  // Per chunk of CHUNK_T tiles, wave w owns TPW consecutive tiles; it loads their
-  // first SPEC*64 entries unconditionally (entries past the count are never used)
-  // together with the counts, so a single memory round trip serves the chunk; a
-  // block scan of the counts gives the output offsets. Tiles with more candidates
-  // copy the rest in a second loop.
-  constexpr int TPW = 2;
-  constexpr int SPEC = 4;
-  constexpr int CHUNK_T = SEL_WAVES * TPW;
-  const int lane = tid & 63, wave = tid >> 6;
   uint32_t* ckey = sh.buf;
   int32_t* cpos = reinterpret_cast<int32_t*>(sh.buf + CAND_CAP);
-  uint32_t* toff = sh.hist;                       // CHUNK_T + 1 output offsets
+  uint32_t* toff = sh.toff;                       // CHUNK_T + 1 output offsets
+  static_assert(CHUNK_T + 1 <= 64, "toff holds a chunk's offsets");
+  // the threshold's first two histograms start from zero
+  for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
+  for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) sh.hist2[i] = 0u;
   const int64_t ntiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-  const uint64_t* cnt_u = counts + (size_t)unit * ntile_cap;
-  const uint64_t* cand_u = cand + (size_t)unit * cand_stride;
   uint32_t total = 0;
   uint32_t kmax = 0u;                             // wave 0: greatest candidate key so far
   bool ovf = false;
   for (int64_t t0 = 0; t0 < ntiles; t0 += CHUNK_T) {
-    const uint64_t cw = cnt_u[min(t0 + min(tid, CHUNK_T - 1), ntiles - 1)];
+    if (t0 > 0) load_chunk(t0, ntiles);
     const uint32_t c = (uint32_t)cw;
-    uint64_t v[TPW][SPEC];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int64_t t = min(t0 + wave * TPW + i, ntiles - 1);
-#pragma unroll
-      for (int e = 0; e < SPEC; ++e) v[i][e] = cand_u[t * TILE_ROWS + 64 * e + lane];
-    }
     const bool own = tid < CHUNK_T && t0 + tid < ntiles;
     ovf = ovf || (own && c == TILE_OVERFLOW);
-    if (wave == 0) kmax = max(kmax, wave_max_u32(own ? (uint32_t)(cw >> 32) : 0u));
+    if (wave == 0) {
+      kmax = max(kmax, wave_max_u32(own ? (uint32_t)(cw >> 32) : 0u));
+      if (lane == 0) sh.misc[5] = (int32_t)kmax;     // read after the loop's last barrier
+    }
     uint32_t chunk_total;
     const uint32_t incl = block_incl_scan(own && c != TILE_OVERFLOW ? c : 0u, sh.scan, &chunk_total);
     if (tid < CHUNK_T) toff[tid + 1] = incl;
@@ -525,8 +674,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         const uint32_t j = (uint32_t)(64 * e + lane);
         const uint32_t dst = total + o + j;
         if (j < ct && dst < (uint32_t)CAND_CAP) {
-          const uint32_t key = (uint32_t)(v[i][e] >> 32);
-          ckey[dst] = key;
+          ckey[dst] = (uint32_t)(v[i][e] >> 32);
           cpos[dst] = (int32_t)(uint32_t)v[i][e];
         }
       }
@@ -534,8 +682,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         const uint32_t dst = total + o + j;
         if (dst < (uint32_t)CAND_CAP) {
           const uint64_t x = cand_u[(t0 + tl) * TILE_ROWS + j];
-          const uint32_t key = (uint32_t)(x >> 32);
-          ckey[dst] = key;
+          ckey[dst] = (uint32_t)(x >> 32);
           cpos[dst] = (int32_t)(uint32_t)x;
         }
       }
@@ -547,13 +694,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const bool overflowed = __syncthreads_or(ovf) != 0;
   if (!overflowed && total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
     // key range of the candidates (for the first radix digit)
-    if (tid == 0) sh.misc[5] = (int32_t)kmax;
-    __syncthreads();
-    const uint32_t kmin = tlow[unit * 2];
     kmax = (uint32_t)sh.misc[5];
     uint32_t needT;
-    const uint32_t T = lds_threshold_range(ckey, (int)total, kmin, kmax, (uint32_t)kk, sh, &needT);
-    compact_list(ckey, cpos, (int)total, T, needT, false, false, out, sh);
+    bool all_eq;
+    const uint32_t T = lds_threshold_range(ckey, (int)total, tkey, kmax, (uint32_t)kk, sh, &needT, &all_eq);
+    // compact in place in LDS, then write the result with coalesced stores
+    compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, sh);
+    for (int i = tid; i < kk; i += SEL_THREADS) out[i] = cpos[i];
     return;
   }
   // the sampled threshold misjudged this unit: exact selection over recomputed scores

@@ -36,8 +36,19 @@ Layout make_layout(const sjsa_shape& s, int k);
 hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
                          const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, uint16_t* Kproj,
                          hipStream_t st);
+// The new token of a decode step, appended by the prep kernel (one token per sequence).
+struct PrepAppend {
+  const uint16_t* k_new = nullptr;   // [B, H_kv, d]
+  const uint16_t* v_new = nullptr;
+  const int32_t* pos = nullptr;      // [B]
+  uint16_t* K = nullptr;
+  uint16_t* V = nullptr;
+  uint16_t* Kproj = nullptr;
+};
+// ap != nullptr: the prep kernel also appends the new token (see PrepAppend).
 hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
-                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st);
+                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
+                       const PrepAppend* ap = nullptr);
 hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kproj, const int32_t* seq_len,
                         unsigned char* ws, hipStream_t st);
 // scores == nullptr: select from the scan's candidates in the workspace (recomputing a

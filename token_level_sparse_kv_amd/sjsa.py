@@ -48,6 +48,10 @@ _SIGS = {
     "sjsa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
     "sjsa_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_decode_step_append": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_int32, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_prep_append": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                        _P, ctypes.c_size_t, _P]),
     "sjsa_score": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t,
                                   _P]),
     "sjsa_prep": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
@@ -189,6 +193,37 @@ def decode_step(q, K, V, Kproj, M, seq_len, k, sm_scale=0.0, out=None, idx=None,
     return out, idx
 
 
+def _append_one_checks(k_new, v_new, pos, K, M):
+    B, Hkv, cap, d = K.shape
+    _need(k_new, "k_new", torch.bfloat16, (B, Hkv, 1, d))
+    _need(v_new, "v_new", torch.bfloat16, (B, Hkv, 1, d))
+    _need(pos, "pos", torch.int32, (B,))
+
+
+def decode_step_append(k_new, v_new, pos, q, K, V, Kproj, M, seq_len, k, sm_scale=0.0, out=None, idx=None,
+                       workspace=None, out_f32=False, stream=None):
+    """Append the step's new token (k_new, v_new [B, H_kv, 1, d] at slots pos[b]) to K, V
+    and Kproj, then run one sparse decode step; the same results as append_kv followed
+    by decode_step. Returns (out, idx)."""
+    _step_checks(q, K, V, Kproj, M, seq_len)
+    _append_one_checks(k_new, v_new, pos, K, M)
+    shape = shape_of(q, K, M, out_f32)
+    B, Hkv = shape.batch, shape.n_kv_heads
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hkv, int(k)), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, q.shape)
+    _need(idx, "idx", torch.int32, (B, Hkv, int(k)))
+    if workspace is None:
+        workspace = alloc_workspace(shape, k, q.device)
+    _check(lib().sjsa_decode_step_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(q),
+                                         _ptr(K), _ptr(V), _ptr(Kproj), _ptr(M), _ptr(seq_len), int(k),
+                                         float(sm_scale), _ptr(out), _ptr(idx), _ptr(workspace),
+                                         workspace.numel(), _stream(stream)))
+    return out, idx
+
+
 def score(q, Kproj, M, seq_len, k, workspace, write_scores=False, stream=None):
     """Scoring prep + score scan into the workspace (candidates for budget k). With
     write_scores the dense fp32 scores are stored too and returned as a
@@ -213,6 +248,20 @@ def prep(shape: Shape, q, M, Kproj, seq_len, k, workspace, stream=None):
     _need(seq_len, "seq_len", torch.int32, (shape.batch,))
     _check(lib().sjsa_prep(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(Kproj), _ptr(seq_len), int(k),
                            _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def prep_append(shape: Shape, k_new, v_new, pos, q, K, V, M, Kproj, seq_len, k, workspace, stream=None):
+    """Scoring prep that first appends the step's new token (as decode_step_append)."""
+    _need(q, "q", torch.bfloat16, (shape.batch, shape.n_kv_heads * shape.group, shape.head_dim))
+    _need(M, "M", torch.float32, (shape.n_kv_heads, shape.rank, shape.head_dim))
+    _need(K, "K", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.head_dim))
+    _need(V, "V", torch.bfloat16, K.shape)
+    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need(seq_len, "seq_len", torch.int32, (shape.batch,))
+    _append_one_checks(k_new, v_new, pos, K, M)
+    _check(lib().sjsa_prep_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(q), _ptr(K),
+                                  _ptr(V), _ptr(Kproj), _ptr(M), _ptr(seq_len), int(k), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
 
 
 def scan(shape: Shape, Kproj, seq_len, workspace, stream=None):
