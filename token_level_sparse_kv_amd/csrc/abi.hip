@@ -60,7 +60,7 @@ Layout make_layout(const sjsa_shape& s, int k) {
   L.off_counts = off;
   off = align_up(off + (size_t)L.units * L.ntile_cap * sizeof(uint64_t), WS_ALIGN);
   L.off_cand = off;
-  off = align_up(off + (size_t)L.units * L.cand_stride * sizeof(uint64_t), WS_ALIGN);
+  off = align_up(off + (size_t)L.units * L.cand_stride * sizeof(uint32_t), WS_ALIGN);
   L.off_scores = off;
   off = align_up(off + (size_t)L.units * L.score_stride * sizeof(float), WS_ALIGN);
   L.scores_end = off;

@@ -9,11 +9,14 @@
 //
 // grid = (nsplit, B * H_kv), 256 threads = 16 row slots of 16 lanes. A workgroup
 // handles `chunk` consecutive entries of its unit's index list; each slot walks
-// its share of rows, U rows at a time, computing the G logits per row (lane t
-// holds head dims 8t..8t+7; a DPP row reduction finishes each dot), and keeps an
-// online softmax (running max m, sum l, accumulator acc) per query head, in the
-// exp2 domain with q pre-scaled by sm_scale*log2(e). Slots are combined in LDS;
-// with one split the workgroup writes the output directly, otherwise it writes its
+// its share of rows, U rows at a time (nontemporal loads: every row is read once),
+// computing the G logits per row (lane t holds head dims 8t..8t+7, dotted as bf16
+// pairs; a DPP row reduction finishes each dot), and keeps an online softmax
+// (reference m, sum l, accumulator acc) per query head in the exp2 domain (logits
+// scaled by sm_scale*log2(e)); the reference is raised only when a logit exceeds it
+// by more than RESCALE_SLACK, so most iterations skip the rescale. Slots are
+// combined in LDS; with one split the workgroup writes the output directly,
+// otherwise it writes its
 // (m, l, acc) partial and merge_kernel (one workgroup per (unit, query head),
 // launched next on the same stream) combines the partials in split order with a
 // log-sum-exp merge.
@@ -27,6 +30,7 @@ constexpr int ATT_THREADS = 256;
 constexpr int SLOTS = ATT_THREADS / 16;
 constexpr int ATT_U = 4;             // rows in flight per slot
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_SLACK = 8.f;  // log2 units a logit may exceed the softmax reference by
 
 template <int G, int U>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attend_kernel(
@@ -35,7 +39,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
     void* __restrict__ out, int out_f32) {
   __shared__ int32_t sidx[1024];
-  __shared__ float sq[G][HEAD_DIM];
+  __shared__ uint32_t sq2[G][HEAD_DIM / 2];     // query heads as packed bf16 pairs
   __shared__ float sm_m[SLOTS][G];
   __shared__ float sm_l[SLOTS][G];
   __shared__ float sm_acc[SLOTS][G][HEAD_DIM];
@@ -53,10 +57,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   const int32_t* ids = idx + (size_t)unit * k + first;
   for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
 
-  // query heads, pre-scaled into the exp2 domain, kept in LDS (read per use: fewer
-  // registers, more waves in flight)
-  for (int i = tid; i < G * HEAD_DIM; i += ATT_THREADS)
-    sq[i / HEAD_DIM][i % HEAD_DIM] = __uint_as_float((uint32_t)q[(size_t)unit * G * HEAD_DIM + i] << 16) * qscale;
+  // query heads kept in LDS as bf16 pairs (read per use: fewer registers, more
+  // waves in flight); the exp2-domain scale is applied to each finished dot
+  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + (size_t)unit * G * HEAD_DIM);
+  for (int i = tid; i < G * HEAD_DIM / 2; i += ATT_THREADS) sq2[i / (HEAD_DIM / 2)][i % (HEAD_DIM / 2)] = q2[i];
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -81,44 +85,54 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       ok[u] = j[u] >= 0 && (int64_t)j[u] < n;
     }
     // loads are unconditional (an invalid entry reads row 0, which always exists, and
-    // gets zero weight), so the compiler can keep every load of the batch in flight
+    // gets zero weight), so the compiler can keep every load of the batch in flight;
+    // each selected row is read once, so the loads are nontemporal
 #pragma unroll
-    for (int u = 0; u < U; ++u) kw[u] = ld16(Kb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
+    for (int u = 0; u < U; ++u) kw[u] = ld16_stream(Kb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
 #pragma unroll
-    for (int u = 0; u < U; ++u) vw[u] = ld16(Vb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
+    for (int u = 0; u < U; ++u) vw[u] = ld16_stream(Vb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
 
-    // logits: per query head, its q slice is read from LDS once and dotted with the U
-    // packed K rows (bf16 unpacked on the fly: a shift or a mask); the reduction runs
-    // for every row (a DPP row is one slot) and invalid rows are masked afterwards
+    // logits: per query head, its q slice (8 bf16) is read from LDS once and dotted
+    // with the U packed K rows by bf16 pair dot products (fp32 accumulation); the row
+    // reduction runs for every row (a DPP row is one slot) and invalid rows are
+    // masked afterwards
     float z[U][G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float qv[8];
-      *reinterpret_cast<f32x4*>(&qv[0]) = *reinterpret_cast<const f32x4*>(&sq[g][t * 8]);
-      *reinterpret_cast<f32x4*>(&qv[4]) = *reinterpret_cast<const f32x4*>(&sq[g][t * 8 + 4]);
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(&sq2[g][t * 4]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float a = row16_sum(dot8_bf16(qv, kw[u]));
-        z[u][g] = ok[u] ? a : -INFINITY;
+        float a = dot2_bf16(qv.x, kw[u].x, 0.f);
+        a = dot2_bf16(qv.y, kw[u].y, a);
+        a = dot2_bf16(qv.z, kw[u].z, a);
+        a = dot2_bf16(qv.w, kw[u].w, a);
+        a = row16_sum(a);
+        z[u][g] = ok[u] ? a * qscale : -INFINITY;
       }
     }
-    // online softmax update, branch free: with no valid logit yet (mx = -inf) the
-    // reference point is 0, so every weight and the rescale factor come out 0
+    // online softmax with a lazy reference: the running reference m only moves (and
+    // the accumulators are rescaled) when a logit exceeds it by more than
+    // RESCALE_SLACK (weights stay <= 2^RESCALE_SLACK); with no valid logit yet
+    // (m = -inf) the reference point is 0 and every weight comes out 0
     float p[U][G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = m[g];
+      float mx = z[0][g];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, z[u][g]);
-      const float ref = mx == -INFINITY ? 0.f : mx;
-      const float sc = exp2f(m[g] - ref);
-      float ps = 0.f;
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, z[u][g]);
+      if (mx > m[g] + RESCALE_SLACK) {
+        const float sc = exp2f(m[g] - mx);
+        l[g] *= sc;
 #pragma unroll
-      for (int u = 0; u < U; ++u) { p[u][g] = exp2f(z[u][g] - ref); ps += p[u][g]; }
-      l[g] = fmaf(l[g], sc, ps);
-      m[g] = mx;
+        for (int e = 0; e < 8; ++e) acc[g][e] *= sc;
+        m[g] = mx;
+      }
+      const float ref = m[g] == -INFINITY ? 0.f : m[g];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= sc;
+      for (int u = 0; u < U; ++u) {
+        p[u][g] = exp2f(z[u][g] - ref);
+        l[g] += p[u][g];
+      }
     }
     // weighted V rows: each V row is unpacked once and added into the G accumulators
 #pragma unroll

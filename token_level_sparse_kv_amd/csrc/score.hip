@@ -27,7 +27,11 @@ constexpr int PREP_WAVES = PREP_THREADS / 64;
 constexpr int SCORE_THREADS = 256;
 constexpr int SCORE_WAVES = SCORE_THREADS / 64;
 constexpr int GROUP_ROWS = 64;       // rows covered by r/8 wave-wide 16-byte loads
-constexpr int SAMPLES = 2048;        // rows scored by the prep kernel to place the threshold
+// rows scored by the prep kernel to place the threshold: more samples give a tighter
+// threshold (fewer candidates) but cost the prep kernel about as much time as the
+// later stages save (measured with 4096 at the 128K batch-16 shape)
+template <int R>
+constexpr int samples_for() { return 2048; }
 constexpr int PREP_BINS = 4096;      // linear score bins of the threshold histogram
 
 // Block-wide (PREP_THREADS) inclusive scan of one u32 per thread; the block total
@@ -49,23 +53,24 @@ __device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
   return inc + before;
 }
 
-// Row of sample s (0 <= s < min(SAMPLES, n)): every row when n <= SAMPLES; else the
-// samples come in adjacent pairs (2i, 2i + 1 share a 128-byte cache line whenever a
+// Row of sample s (0 <= s < min(NS, n)): every row when n <= NS; else the samples
+// come in adjacent pairs (2i, 2i + 1 share a 128-byte cache line whenever a
 // projected row is at most 64 bytes), the pairs evenly spaced over the sequence.
+template <int NS>
 __device__ __forceinline__ int64_t sample_row(int s, int64_t n) {
-  if (n <= SAMPLES) return s;
-  return 2 * (((int64_t)(s >> 1) * n) / SAMPLES) + (s & 1);
+  if (n <= NS) return s;
+  return 2 * (((int64_t)(s >> 1) * n) / NS) + (s & 1);
 }
 
 // One workgroup per (b, h).
 //  * q_bar in fp32 (sum in head order, then divide by G) and q_hat = M_h q_bar: output
 //    i is split over 16 lanes of 8 channels each (fp32 partial dots, DPP row sum).
-//  * Threshold for the scan: the scores of SAMPLES rows (evenly spaced pairs of
-//    adjacent rows; all rows when n <= SAMPLES) are binned linearly between their
-//    least and greatest finite value (+inf in the top bin, -inf and NaN left out);
-//    the bin that holds the sample of
-//    rank m (see below) is found, and the least key in it becomes the unit's
-//    candidate threshold, so at least m samples reach it. The exact top k is among
+//  * Threshold for the scan: the scores of NS rows (NS = samples_for<R>(), evenly
+//    spaced pairs of adjacent rows; all rows when n <= NS) are binned linearly
+//    between their least and greatest finite value (+inf in the top bin, -inf and
+//    NaN left out); the bin that holds the sample of rank m (see below) is found,
+//    and the least key in it becomes the unit's candidate threshold, so at least m
+//    samples reach it. The exact top k is among
 //    the rows that reach it unless the sample misjudges the distribution, a case the
 //    select stage detects and handles exactly: the threshold only decides how much
 //    work the select stage does, never its result.
@@ -84,7 +89,8 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     int n_kv_heads, int group, int64_t cap, PrepAppend ap) {
   constexpr int LPR = R / 8;                          // 16-byte words per Kproj row
   constexpr int RPL = 64 / LPR;                       // samples per wave-wide load
-  constexpr int BATCHES = SAMPLES / PREP_THREADS;     // 64-sample batches per wave (= samples per lane)
+  constexpr int NS = samples_for<R>();
+  constexpr int BATCHES = NS / PREP_THREADS;          // 64-sample batches per wave (= samples per lane)
   constexpr int OUTS = (R * 16 + PREP_THREADS - 1) / PREP_THREADS;   // q_hat outputs per thread
   __shared__ float sqh[R];
   __shared__ uint32_t shist[PREP_BINS];
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
   const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
   const int64_t kk = min((int64_t)k, n);
   const bool sampling = kk < n;                       // uniform over the workgroup
-  const int S = (int)min((int64_t)SAMPLES, n);
+  const int S = (int)min((int64_t)NS, n);
 
   // sample s sits in row pos(s) (evenly spaced); wave-wide loads as in the scan: in
   // batch t a wave covers samples sb .. sb + 63 (sb = 64 * (wave + t * PREP_WAVES)),
@@ -133,8 +139,8 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 #pragma unroll
       for (int i = 0; i < LPR; ++i) {
         const int sidx = min(64 * (wave + t * PREP_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
-        const int64_t pos = sample_row(sidx, n);
-        w[t][i] = ld16(base + pos * R);
+        const int64_t pos = sample_row<NS>(sidx, n);
+        w[t][i] = ld16_stream(base + pos * R);
       }
     }
   }
@@ -280,8 +286,9 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 // are reduced with DPP lane moves in a transposed pattern, after which lane (rs, p)
 // owns the score of group row p*RPL + rs.
 //
-// Rows whose key reaches the unit's threshold are candidates, kept as (key, row)
-// pairs in position order: with a ballot of the flags in lane order, the number of
+// Rows whose key reaches the unit's threshold are candidates, kept as 32-bit entries
+// (the key's top 20 bits, the row's offset in its tile; see cand_entry) in position
+// order: with a ballot of the flags in lane order, the number of
 // flagged rows before a row is the popcount of the ballot under a per-lane mask of
 // the lanes that hold earlier rows (earlier lane columns, and this column above this
 // lane). Each wave packs the candidates of its segments back to back into a
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 template <int R, int UNROLL, bool WRITE_DENSE>
 __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     const uint16_t* __restrict__ kproj, const float* __restrict__ qhat, const uint32_t* __restrict__ tlow,
-    const int32_t* __restrict__ seq_len, float* __restrict__ scores, uint64_t* __restrict__ cand,
+    const int32_t* __restrict__ seq_len, float* __restrict__ scores, uint32_t* __restrict__ cand,
     uint64_t* __restrict__ counts, int n_kv_heads, int64_t cap, int64_t stride, int64_t ntile_cap,
     int64_t cand_stride) {
   constexpr int LPR = R / 8;            // lanes per Kproj row (16 bytes each)
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
   static_assert(GROUP_ROWS * UNROLL == SEG_ROWS, "one wave iteration covers one segment");
   static_assert(TILE_ROWS / SEG_ROWS <= 64, "one wave scans the segment counts");
   constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
-  __shared__ uint64_t stage[SCORE_WAVES][CAND_STAGE];
+  __shared__ uint32_t stage[SCORE_WAVES][CAND_STAGE];
   __shared__ uint32_t segcnt[SEGS_PER_TILE];
   __shared__ uint32_t segoff[SEGS_PER_TILE + 1];
   __shared__ uint32_t sstart[SEGS_PER_TILE];
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
       const uint64_t m = __ballot(c);
       if (c) {
         const uint32_t at = wcount + count + (uint32_t)__popcll(m & earlier);
-        if (at < (uint32_t)CAND_STAGE) stage[wave][at] = ((uint64_t)key << 32) | (uint64_t)(uint32_t)row;
+        if (at < (uint32_t)CAND_STAGE) stage[wave][at] = cand_entry(key, row);
         kmax = max(kmax, key);
       }
       count += (uint32_t)__popcll(m);
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
   const uint32_t tot = segoff[SEGS_PER_TILE];
   if (!ovf) {
     // every thread writes entries e, e + 256, ...: coalesced, streamed past the caches
-    uint64_t* wtile = cand + (size_t)unit * cand_stride + (size_t)blockIdx.x * TILE_ROWS;
+    uint32_t* wtile = cand + (size_t)unit * cand_stride + (size_t)blockIdx.x * TILE_ROWS;
     for (uint32_t e = threadIdx.x; e < tot; e += SCORE_THREADS) {
       int lo = 0, hi = SEGS_PER_TILE;            // the segment holding entry e
       while (hi - lo > 1) {
@@ -452,7 +459,7 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kp
   const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* scores = reinterpret_cast<float*>(ws + L.off_scores);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + L.off_cand);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(ws + L.off_cand);
   uint64_t* counts = reinterpret_cast<uint64_t*>(ws + L.off_counts);
   const dim3 grid((unsigned)((s.capacity + TILE_ROWS - 1) / TILE_ROWS), (unsigned)L.units), block(SCORE_THREADS);
   const bool dense = (s.flags & SJSA_FLAG_WRITE_SCORES) != 0;

@@ -52,6 +52,7 @@ struct SelShared {
   uint32_t buf[LDS_WORDS];
   uint32_t hist2[HIST2_BINS];
   uint32_t toff[64];                 // candidate path: tile output offsets of a chunk
+  float qh[64];                      // candidate path: q_hat, for exact scores at the boundary
   uint32_t wtot[2][2 * SEL_WAVES];   // [buffer][A totals of waves | C totals of waves]
   uint32_t scan[SEL_WAVES];
   uint32_t scan2[SEL_WAVES];
@@ -582,7 +583,7 @@ template <int R>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
     int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const uint16_t* __restrict__ kproj,
-    const float* __restrict__ qhat, const uint32_t* __restrict__ tlow, const uint64_t* __restrict__ cand,
+    const float* __restrict__ qhat, const uint32_t* __restrict__ tlow, const uint32_t* __restrict__ cand,
     const uint64_t* __restrict__ counts, float* __restrict__ dense, int64_t dense_stride, int64_t ntile_cap,
     int64_t cand_stride) {
   __shared__ SelShared sh;
@@ -592,29 +593,30 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const int lane = tid & 63, wave = tid >> 6;
 
   // Candidates. Scan tile x (rows [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in
-  // position order, at entries [x*TILE_ROWS, ...); counts[x] holds their number
-  // (TILE_OVERFLOW when it could not keep them all) and their greatest key. Every
-  // candidate key is at least the scan's threshold key, so [threshold, greatest
-  // key] bounds the keys. Tiles are gathered in chunks of CHUNK_T; wave w owns TPW
-  // consecutive tiles of a chunk and loads their first SPEC*64 entries
-  // unconditionally (entries past the count are never used) together with the
-  // counts, so one memory round trip serves a chunk. The first chunk's loads are
-  // issued before the sequence length is known (tiles clamped to the capacity), so
-  // they overlap the kernel's first load; later chunks clamp to the sequence.
+  // position order, at entries [x*TILE_ROWS, ...) as (top CAND_KEY_BITS key bits,
+  // row offset in the tile); counts[x] holds their number (TILE_OVERFLOW when it
+  // could not keep them all) and their greatest key. Every candidate key is at least
+  // the scan's threshold key, so [threshold, greatest key] bounds the keys. Tiles are
+  // gathered in chunks of CHUNK_T; wave w owns TPW consecutive tiles of a chunk and
+  // loads their first SPEC*64 entries unconditionally (entries past the count are
+  // never used) together with the counts, so one memory round trip serves a chunk.
+  // The first chunk's loads are issued before the sequence length is known (tiles
+  // clamped to the capacity), so they overlap the kernel's first load; later chunks
+  // clamp to the sequence.
   constexpr int TPW = 2;
   constexpr int SPEC = 4;
   constexpr int CHUNK_T = SEL_WAVES * TPW;
   const uint64_t* cnt_u = counts + (size_t)unit * ntile_cap;
-  const uint64_t* cand_u = cand + (size_t)unit * cand_stride;
+  const uint32_t* cand_u = cand + (size_t)unit * cand_stride;
   uint64_t cw = 0;
-  uint64_t v[TPW][SPEC];
+  uint32_t v[TPW][SPEC];
   auto load_chunk = [&](int64_t t0, int64_t tiles) {
     cw = cnt_u[min(t0 + min(tid, CHUNK_T - 1), tiles - 1)];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int64_t t = min(t0 + wave * TPW + i, tiles - 1);
 #pragma unroll
-      for (int e = 0; e < SPEC; ++e) v[i][e] = cand_u[t * TILE_ROWS + 64 * e + lane];
+      for (int e = 0; e < SPEC; ++e) v[i][e] = __builtin_nontemporal_load(cand_u + t * TILE_ROWS + 64 * e + lane);
     }
   };
   const bool cand_path = scores == nullptr;
@@ -622,6 +624,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   if (cand_path) {
     tkey = tlow[unit * 2];
     load_chunk(0, ntile_cap);
+    if (tid < R) sh.qh[tid] = qhat[(size_t)unit * QHAT_STRIDE + tid];
+    if (tid == 0) sh.misc[6] = 0;                 // boundary entry counter (read after many barriers)
   }
 
   const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
@@ -674,16 +678,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         const uint32_t j = (uint32_t)(64 * e + lane);
         const uint32_t dst = total + o + j;
         if (j < ct && dst < (uint32_t)CAND_CAP) {
-          ckey[dst] = (uint32_t)(v[i][e] >> 32);
-          cpos[dst] = (int32_t)(uint32_t)v[i][e];
+          ckey[dst] = v[i][e] >> CAND_ROW_BITS;
+          cpos[dst] = (int32_t)((t0 + tl) * TILE_ROWS + (v[i][e] & CAND_ROW_MASK));
         }
       }
       for (uint32_t j = SPEC * 64 + lane; j < ct; j += 64) {     // tiles with many candidates
         const uint32_t dst = total + o + j;
         if (dst < (uint32_t)CAND_CAP) {
-          const uint64_t x = cand_u[(t0 + tl) * TILE_ROWS + j];
-          ckey[dst] = (uint32_t)(x >> 32);
-          cpos[dst] = (int32_t)(uint32_t)x;
+          const uint32_t x = __builtin_nontemporal_load(cand_u + (t0 + tl) * TILE_ROWS + j);
+          ckey[dst] = x >> CAND_ROW_BITS;
+          cpos[dst] = (int32_t)((t0 + tl) * TILE_ROWS + (x & CAND_ROW_MASK));
         }
       }
     }
@@ -693,11 +697,63 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
   const bool overflowed = __syncthreads_or(ovf) != 0;
   if (!overflowed && total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
-    // key range of the candidates (for the first radix digit)
+    // threshold on the truncated keys (range [threshold, greatest key] >> CAND_ROW_BITS)
     kmax = (uint32_t)sh.misc[5];
     uint32_t needT;
     bool all_eq;
-    const uint32_t T = lds_threshold_range(ckey, (int)total, tkey, kmax, (uint32_t)kk, sh, &needT, &all_eq);
+    uint32_t T = lds_threshold_range(ckey, (int)total, tkey >> CAND_ROW_BITS, kmax >> CAND_ROW_BITS,
+                                     (uint32_t)kk, sh, &needT, &all_eq);
+    if (needT == 0xffffffffu) all_eq = true;
+    const uint16_t* kp_unit = kproj + (size_t)unit * cap * R;
+    int nb = 0;                                   // entries on the boundary truncated key T
+    if (!all_eq && needT > 0) {
+      // only some entries of the boundary truncated key T are taken: list them
+      uint32_t* bidx = sh.hist2;
+      for (int i = tid; i < (int)total; i += SEL_THREADS)
+        if (ckey[i] == T) {
+          const int at = atomicAdd(&sh.misc[6], 1);
+          if (at < HIST2_BINS) bidx[at] = (uint32_t)i;
+        }
+      __syncthreads();
+      nb = sh.misc[6];
+    }
+    if (!all_eq && needT > 0 && nb <= 64) {
+      // few boundary entries (the usual case): wave 0 recomputes their exact keys
+      // (arithmetic bit-identical to the scan) and ranks them (larger key first, then
+      // lower list index, i.e. lower position); the taken ones are lifted above T
+      if (wave == 0) {
+        const uint32_t* bidx = sh.hist2;
+        int li = 0x7fffffff;
+        uint32_t ex = 0u;
+        if (lane < nb) {
+          li = (int)bidx[lane];
+          ex = score_key(row_score<R>(sh.qh, kp_unit + (size_t)cpos[li] * R));
+        }
+        uint32_t rank = 0;
+        for (int j = 0; j < nb; ++j) {
+          const uint32_t exj = readlane_u32(ex, j);
+          const int lij = (int)readlane_u32((uint32_t)li, j);
+          rank += (exj > ex || (exj == ex && lij < li)) ? 1u : 0u;
+        }
+        if (lane < nb && rank < needT) ckey[li] = T + 1u;
+      }
+      __syncthreads();
+      needT = 0;                                  // keep the keys above T
+    } else if (!all_eq && needT > 0) {
+      // many boundary entries: recompute their exact keys and rank on full keys, each
+      // entry's key becoming (truncated key, low key bits or 0 off the boundary)
+      for (int i = tid; i < (int)total; i += SEL_THREADS) {
+        const uint32_t kt = ckey[i];
+        uint32_t low = 0;
+        if (kt == T) low = score_key(row_score<R>(sh.qh, kp_unit + (size_t)cpos[i] * R)) & CAND_ROW_MASK;
+        ckey[i] = (kt << CAND_ROW_BITS) | low;
+      }
+      for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
+      for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) sh.hist2[i] = 0u;
+      __syncthreads();
+      const uint32_t lo = T << CAND_ROW_BITS;
+      T = lds_threshold_range(ckey, (int)total, lo, lo | CAND_ROW_MASK, needT, sh, &needT, &all_eq);
+    }
     // compact in place in LDS, then write the result with coalesced stores
     compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, sh);
     for (int i = tid; i < kk; i += SEL_THREADS) out[i] = cpos[i];
@@ -715,7 +771,7 @@ hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scor
                          const uint16_t* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
                          hipStream_t st) {
   const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
-  const uint64_t* cand = reinterpret_cast<const uint64_t*>(ws + L.off_cand);
+  const uint32_t* cand = reinterpret_cast<const uint32_t*>(ws + L.off_cand);
   const uint64_t* counts = reinterpret_cast<const uint64_t*>(ws + L.off_counts);
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* dense = reinterpret_cast<float*>(ws + L.off_scores);

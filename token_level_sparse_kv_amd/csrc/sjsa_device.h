@@ -112,6 +112,13 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// a.lo*b.lo + a.hi*b.hi + c for two packed bf16 pairs, fp32 accumulation
+// (v_dot2c_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // Wave-wide (64 lanes) inclusive prefix sum of a u32: DPP scans inside the four rows
 // of 16 lanes, then each row adds the totals of the rows before it (read from lanes
 // 15, 31 and 47). Every lane of the wave must be active.

@@ -17,6 +17,17 @@ constexpr int SEG_ROWS = 128;        // rows per scan segment (one wave iteratio
 constexpr int TILE_ROWS = 4096;      // rows per scan workgroup; one candidate region
 constexpr int CAND_STAGE = 512;      // candidates a scan wave can stage in LDS
 constexpr uint32_t TILE_OVERFLOW = 0xffffffffu;   // tile count: a wave's stage overflowed
+// A candidate entry holds the top CAND_KEY_BITS bits of its score key and the row's
+// offset inside its scan tile (TILE_ROWS = 2^CAND_ROW_BITS rows): the selection
+// ranks by the truncated keys and recomputes the exact score only of the entries
+// that share the boundary's truncated key.
+constexpr int CAND_ROW_BITS = 12;
+constexpr int CAND_KEY_BITS = 32 - CAND_ROW_BITS;
+constexpr uint32_t CAND_ROW_MASK = (1u << CAND_ROW_BITS) - 1u;
+static_assert(TILE_ROWS == 1 << CAND_ROW_BITS, "a tile offset fills the entry's low bits");
+__host__ __device__ constexpr uint32_t cand_entry(uint32_t key, int row) {
+  return (key & ~CAND_ROW_MASK) | ((uint32_t)row & CAND_ROW_MASK);
+}
 constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
 
 struct Layout {
@@ -25,7 +36,7 @@ struct Layout {
   int nsplit = 1;             // attention splits per unit
   int chunk = 0;              // selected indices per split
   int64_t ntile_cap = 0;      // scan tiles per unit (capacity / TILE_ROWS, rounded up)
-  int64_t cand_stride = 0;    // candidate entries per unit (capacity rounded up to TILE_ROWS)
+  int64_t cand_stride = 0;    // 4-byte candidate entries per unit (capacity rounded up to TILE_ROWS)
   size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
   size_t scores_end = 0, total = 0;
 };
