@@ -55,8 +55,29 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   const int first = split * chunk;
   const int cnt = max(0, min(chunk, k - first));
   const int32_t* ids = idx + (size_t)unit * k + first;
-  for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
+  const uint16_t* Kb = K + (size_t)unit * cap * HEAD_DIM + t * 8;
+  const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + t * 8;
 
+  // loads are unconditional (an invalid entry reads row 0, which always exists, and
+  // gets zero weight), so the compiler can keep every load of a batch in flight;
+  // each selected row is read once, so the loads are nontemporal
+  auto load_rows = [&](const int32_t (&j)[U], u32x4 (&kw)[U], u32x4 (&vw)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = (j[u] >= 0 && (int64_t)j[u] < cap) ? j[u] : 0;
+      kw[u] = ld16_stream(Kb + (size_t)row * HEAD_DIM);
+      vw[u] = ld16_stream(Vb + (size_t)row * HEAD_DIM);
+    }
+  };
+  // the slot's first batch of rows is requested straight from the index list, before
+  // the workgroup stages the list and the queries in LDS
+  int32_t j0[U];
+  u32x4 kw0[U], vw0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) j0[u] = slot * U + u < cnt ? ids[slot * U + u] : -1;
+  load_rows(j0, kw0, vw0);
+
+  for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
   // query heads kept in LDS as bf16 pairs (read per use: fewer registers, more
   // waves in flight); the exp2-domain scale is applied to each finished dot
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + (size_t)unit * G * HEAD_DIM);
@@ -71,27 +92,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   }
   __syncthreads();
 
-  const uint16_t* Kb = K + (size_t)unit * cap * HEAD_DIM + t * 8;
-  const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + t * 8;
-
-  for (int base = slot * U; base < cnt; base += SLOTS * U) {
-    int32_t j[U];
+  auto consume = [&](const int32_t (&j)[U], const u32x4 (&kw)[U], const u32x4 (&vw)[U]) {
     bool ok[U];
-    u32x4 kw[U], vw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u;
-      j[u] = i < cnt ? sidx[i] : -1;
-      ok[u] = j[u] >= 0 && (int64_t)j[u] < n;
-    }
-    // loads are unconditional (an invalid entry reads row 0, which always exists, and
-    // gets zero weight), so the compiler can keep every load of the batch in flight;
-    // each selected row is read once, so the loads are nontemporal
-#pragma unroll
-    for (int u = 0; u < U; ++u) kw[u] = ld16_stream(Kb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
-#pragma unroll
-    for (int u = 0; u < U; ++u) vw[u] = ld16_stream(Vb + (size_t)(ok[u] ? j[u] : 0) * HEAD_DIM);
-
+    for (int u = 0; u < U; ++u) ok[u] = j[u] >= 0 && (int64_t)j[u] < n;
     // logits: per query head, its q slice (8 bf16) is read from LDS once and dotted
     // with the U packed K rows by bf16 pair dot products (fp32 accumulation); the row
     // reduction runs for every row (a DPP row is one slot) and invalid rows are
@@ -146,6 +150,16 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
       }
     }
+  };
+
+  if (slot * U < cnt) consume(j0, kw0, vw0);
+  for (int base = slot * U + SLOTS * U; base < cnt; base += SLOTS * U) {
+    int32_t j[U];
+    u32x4 kw[U], vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) j[u] = base + u < cnt ? sidx[base + u] : -1;
+    load_rows(j, kw, vw);
+    consume(j, kw, vw);
   }
 
   // ---- combine the 16 slots of this workgroup
