@@ -33,6 +33,9 @@ Readings taken where the pages are silent (each is also listed in the design not
   * n_b = 0: nothing is selected and the output is zero.
   * the attention itself is exact: fp64 logits, fp64 softmax, fp64 weighted sum
     of the bf16 V rows.
+  * scoring-cache format: bf16 by default; "fp8" is OCP E4M3 (the page keeps the
+    cache in FP8 without naming a variant), written unscaled and saturating at
+    +-448, rounded once from the fp64 dot.
 """
 from __future__ import annotations
 
@@ -40,7 +43,7 @@ import math
 
 import numpy as np
 
-from .numerics import bf16_to_f32, round_to_bf16
+from .numerics import bf16_to_f32, fp8e4m3_to_f32, round_to_bf16, round_to_fp8e4m3
 
 
 # --------------------------------------------------------------------------- prep
@@ -62,26 +65,42 @@ def project_query(q_bar: np.ndarray, M: np.ndarray) -> np.ndarray:
     return (Md * qd[None, :]).sum(axis=1).astype(np.float32)
 
 
-def project_keys(k_bits: np.ndarray, M: np.ndarray) -> np.ndarray:
-    """Projected scoring-cache rows Kproj = K M^T, rounded to bf16 (ties to even).
+KPROJ_FORMATS = ("bf16", "fp8")   # fp8: OCP E4M3, unscaled, saturating
 
-    k_bits [..., d] bf16 bits, M [r, d] fp32 -> [..., r] bf16 bits. The dot products
-    are taken in fp64 and rounded once to bf16 (section "投影打分缓存与校准成本":
-    the scoring cache holds every key projected onto the basis)."""
+
+def project_keys(k_bits: np.ndarray, M: np.ndarray, fmt: str = "bf16") -> np.ndarray:
+    """Projected scoring-cache rows Kproj = K M^T, rounded to the cache format.
+
+    k_bits [..., d] bf16 bits, M [r, d] fp32 -> [..., r] bits (uint16 for bf16, uint8
+    for fp8). The dot products are taken in fp64 and rounded once, ties to even (section
+    "投影打分缓存与校准成本": the scoring cache holds every key projected onto the
+    basis; the page keeps it in FP8, which is the "fp8" format here)."""
     kf = bf16_to_f32(k_bits).astype(np.float64)
     Md = np.asarray(M, dtype=np.float32).astype(np.float64)
     prod = kf[..., None, :] * Md            # [..., r, d]
-    return round_to_bf16(prod.sum(axis=-1))
+    dots = prod.sum(axis=-1)
+    if fmt == "fp8":
+        return round_to_fp8e4m3(dots)
+    assert fmt == "bf16", fmt
+    return round_to_bf16(dots)
+
+
+def decode_kproj(kproj_bits: np.ndarray, fmt: str = "bf16") -> np.ndarray:
+    """Stored scoring-cache values as fp32 (exact)."""
+    if fmt == "fp8":
+        return fp8e4m3_to_f32(kproj_bits)
+    assert fmt == "bf16", fmt
+    return bf16_to_f32(kproj_bits)
 
 
 # ------------------------------------------------------------------------ scoring
-def score_positions(q_hat: np.ndarray, kproj_bits: np.ndarray) -> np.ndarray:
+def score_positions(q_hat: np.ndarray, kproj_bits: np.ndarray, fmt: str = "bf16") -> np.ndarray:
     """s_j = q_hat . Kproj_j for every row j of the stored projected cache.
 
-    kproj_bits [n, r] bf16 bits -> fp32 [n]. The products of an fp32 and a bf16
-    are exact in fp64; the r-term sum is done row by row in the same order for
-    every row and rounded once to fp32."""
-    kp = bf16_to_f32(kproj_bits).astype(np.float64)
+    kproj_bits [n, r] (bf16 or fp8 bits) -> fp32 [n]. The products of an fp32 and a
+    stored value are exact in fp64; the r-term sum is done row by row in the same
+    order for every row and rounded once to fp32."""
+    kp = decode_kproj(kproj_bits, fmt).astype(np.float64)
     qd = np.asarray(q_hat, dtype=np.float32).astype(np.float64)
     return (kp * qd[None, :]).sum(axis=1).astype(np.float32)
 
@@ -135,19 +154,19 @@ def default_sm_scale(head_dim: int) -> float:
 
 
 # ------------------------------------------------------------------ one full step
-def decode_unit(q_heads_bits, K_bits, V_bits, kproj_bits, M, n, k, sm_scale):
+def decode_unit(q_heads_bits, K_bits, V_bits, kproj_bits, M, n, k, sm_scale, fmt="bf16"):
     """One (sequence, KV head) unit of the step. Arrays are that unit's slices:
-    q_heads [G, d], K/V [cap, d], kproj [cap, r] (bf16 bits), M [r, d] fp32.
-    Returns (out fp64 [G, d], idx int32 [k], scores fp32 [n])."""
+    q_heads [G, d], K/V [cap, d] (bf16 bits), kproj [cap, r] (bits of `fmt`), M [r, d]
+    fp32. Returns (out fp64 [G, d], idx int32 [k], scores fp32 [n])."""
     q_bar = mean_query(q_heads_bits)
     q_hat = project_query(q_bar, M)
-    s = score_positions(q_hat, kproj_bits[:n])
+    s = score_positions(q_hat, kproj_bits[:n], fmt)
     idx = select_topk(s, k)
     out = attend(q_heads_bits, K_bits[:n], V_bits[:n], idx, sm_scale)
     return out, idx, s
 
 
-def decode_step(q_bits, K_bits, V_bits, kproj_bits, M, seq_len, k, sm_scale=0.0, units=None):
+def decode_step(q_bits, K_bits, V_bits, kproj_bits, M, seq_len, k, sm_scale=0.0, units=None, fmt="bf16"):
     """The whole step over a batch.
 
     q [B, H_q, d], K/V [B, H_kv, cap, d], kproj [B, H_kv, cap, r] (bf16 bits),
@@ -165,13 +184,13 @@ def decode_step(q_bits, K_bits, V_bits, kproj_bits, M, seq_len, k, sm_scale=0.0,
     for b, h in todo:
         n = int(min(max(int(seq_len[b]), 0), cap))
         o, ix, _ = decode_unit(q_bits[b, h * G:(h + 1) * G], K_bits[b, h], V_bits[b, h],
-                               kproj_bits[b, h], M[h], n, k, scale)
+                               kproj_bits[b, h], M[h], n, k, scale, fmt)
         out[b, h * G:(h + 1) * G] = o
         idx[b, h] = ix
     return out, idx
 
 
-def append_rows(k_new_bits, v_new_bits, M, pos, K_bits, V_bits, kproj_bits):
+def append_rows(k_new_bits, v_new_bits, M, pos, K_bits, V_bits, kproj_bits, fmt="bf16"):
     """Append T new tokens per (b, h) at positions pos[b] .. pos[b]+T-1 (in place):
     K and V get the rows as given, Kproj gets project_keys of the new keys.
     Rows that would land outside [0, cap) are dropped."""
@@ -179,7 +198,7 @@ def append_rows(k_new_bits, v_new_bits, M, pos, K_bits, V_bits, kproj_bits):
     cap = K_bits.shape[2]
     for b in range(B):
         for h in range(Hkv):
-            rows = project_keys(k_new_bits[b, h], M[h])
+            rows = project_keys(k_new_bits[b, h], M[h], fmt)
             for t in range(T):
                 p = int(pos[b]) + t
                 if 0 <= p < cap:

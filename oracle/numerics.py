@@ -50,3 +50,50 @@ def round_to_bf16(x) -> np.ndarray:
 def f32_round(x) -> np.ndarray:
     """Round real values held in fp64 to the nearest fp32 (ties to even; IEEE cast)."""
     return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------- fp8
+# OCP FP8 E4M3 ("E4M3FN"): 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits;
+# exponent 0 holds subnormals (fraction/8 * 2^-6); there are no infinities and only
+# the all-ones exponent-and-fraction pattern (0x7F / 0xFF) is NaN, so the largest
+# finite magnitude is 1.75 * 2^8 = 448. The projected scoring cache in this format
+# is written unscaled and saturating: magnitudes beyond 448 store as 448.
+FP8_MAX = 448.0
+FP8_MIN_QUANTUM_EXP = -9      # subnormal step: 2^-3 * 2^-6
+
+
+def fp8e4m3_to_f32(bits) -> np.ndarray:
+    """Exact decoding of E4M3 bit patterns (uint8) to fp32; NaN patterns give NaN."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = sign * mag
+    val = np.where((e == 15) & ((b & 0x7) == 7), np.nan, val)
+    return val.astype(np.float32)
+
+
+def round_to_fp8e4m3(x) -> np.ndarray:
+    """Round real values (fp64 or fp32) to E4M3 in one step: nearest, ties to even,
+    saturating at +-448; NaN gives 0x7F. Returns uint8 bit patterns.
+
+    Method: as for bf16, x / quantum is an exact power-of-two scaling with quantum
+    2^(e-4) for x = m * 2^e (0.5 <= |m| < 1; 4 significant bits), never below the
+    subnormal step 2^-9; rint() rounds half to even. The rounded magnitude is then
+    clamped to 448 and re-encoded field by field."""
+    x = np.asarray(x, dtype=np.float64)
+    nan = np.isnan(x)
+    xs = np.where(nan, 0.0, np.clip(x, -FP8_MAX, FP8_MAX))
+    _, e = np.frexp(xs)
+    qexp = np.maximum(e - 4, FP8_MIN_QUANTUM_EXP)
+    r = np.minimum(np.abs(np.ldexp(np.rint(np.ldexp(xs, -qexp)), qexp)), FP8_MAX)
+    sign = np.signbit(xs).astype(np.int64) << 7
+    sub = r < 2.0 ** -6
+    fexp = np.floor(np.log2(np.where(r > 0, r, 1.0))).astype(np.int64)
+    frac_n = np.rint((np.ldexp(np.where(sub, 1.0, r), -np.where(sub, 0, fexp)) - 1.0) * 8.0).astype(np.int64)
+    code_n = ((fexp + 7) << 3) | frac_n
+    code_s = np.rint(np.ldexp(r, 9)).astype(np.int64)
+    code = np.where(sub, code_s, code_n) | sign
+    code = np.where(nan, 0x7F, code)
+    return code.astype(np.uint8)
