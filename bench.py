@@ -95,6 +95,48 @@ def cpu_baseline(host, units, k, scale, gpu_out, gpu_idx):
     return dt, workers, ok, worst
 
 
+def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, warmup, step_bytes, peak):
+    """The same step over an FP8 E4M3 scoring cache (one byte per element), timed the
+    same way. Reported beside the bf16 figure, which stays the headline."""
+    import numpy as np
+    import torch
+    B, Hkv, G, d, r, n, k = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim, wl.rank, wl.capacity, wl.k
+    dev = K.device
+    K, V = K.clone(), V.clone()
+    Kp8 = torch.empty(B, Hkv, n, r, dtype=torch.uint8, device=dev)
+    T = 8192
+    for t0 in range(0, n, T):
+        pos = torch.full((B,), t0, dtype=torch.int32, device=dev)
+        sj.append_kv(K[:, :, t0:t0 + T].contiguous(), V[:, :, t0:t0 + T].contiguous(), M, pos, K, V, Kp8)
+    shape = sj.make_shape(B, Hkv, G, d, r, n, kproj_fp8=True)
+    ws = sj.alloc_workspace(shape, k, dev)
+    idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hkv * G, d, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        q = q_sets[i % q_sets.shape[0]]
+        sj.prep_append(shape, k_new, v_new, pos_new, q, K, V, M, Kp8, seq_len, k, ws)
+        sj.scan(shape, Kp8, seq_len, ws)
+        sj.select(shape, Kp8, seq_len, k, ws, idx=idx)
+        sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
+
+    for i in range(warmup):
+        step(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    tb = step_bytes(B, Hkv, G, d, r, n, k, kb=1)
+    gbs = tb["total"] / (ms * 1e-3) / 1e9
+    return {"kproj_dtype": "fp8_e4m3", "value": round(1000.0 / ms, 2), "unit": "steps/s",
+            "ms_per_step": round(ms, 5), "algorithmic_bytes_per_step": tb["total"], "hbm_gbs": round(gbs, 1),
+            "hbm_frac_of_peak": round(gbs / peak, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +145,7 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=16, help="units sampled for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-fp8-variant", action="store_true", help="skip the FP8 scoring-cache measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -221,6 +264,9 @@ def main():
     }
 
     print(f"timed: {ms_per_step * 1000:.1f} us/step, stages (us) {line['stage_us']}", file=sys.stderr, flush=True)
+    if not args.no_fp8_variant:
+        line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, args.steps,
+                                                args.warmup, step_bytes, MI355X_HBM_PEAK_GBS)
     if not args.no_cpu_baseline:
         rng = np.random.default_rng(3)
         all_units = [(b, h) for b in range(B) for h in range(Hkv)]

@@ -16,7 +16,8 @@
  *   - Tensors are row-major and contiguous. bf16 is passed as 16-bit patterns.
  *       q      [B, H_q, d]        bf16, H_q = H_kv * G, query head hq -> KV head hq / G
  *       K, V   [B, H_kv, cap, d]  bf16
- *       Kproj  [B, H_kv, cap, r]  bf16 (projected scoring cache, K M^T)
+ *       Kproj  [B, H_kv, cap, r]  bf16 (projected scoring cache, K M^T), or one-byte
+ *                                 FP8 E4M3 values with SJSA_FLAG_KPROJ_FP8
  *       M      [H_kv, r, d]       fp32, orthonormal rows (one basis per KV head)
  *       seq_len[B]                int32: tokens valid in each sequence's cache
  *       idx    [B, H_kv, k]       int32
@@ -61,9 +62,14 @@ typedef enum sjsa_status {
 /* sjsa_shape.flags bits.
  * SJSA_FLAG_OUT_F32: `out` is fp32 instead of bf16.
  * SJSA_FLAG_WRITE_SCORES: the score scan also stores every fp32 score in the
- *   workspace (for inspection; see sjsa_score). Results do not change. */
+ *   workspace (for inspection; see sjsa_score). Results do not change.
+ * SJSA_FLAG_KPROJ_FP8: the projected scoring cache Kproj holds OCP FP8 E4M3 values
+ *   (one byte each, unscaled, saturating at +-448; the JSSA article's section
+ *   投影打分缓存与校准成本 keeps the cache in FP8) instead of bf16. Appends round the
+ *   fp32 projection to nearest (ties to even); scoring decodes exactly. */
 #define SJSA_FLAG_OUT_F32 1
 #define SJSA_FLAG_WRITE_SCORES 2
+#define SJSA_FLAG_KPROJ_FP8 4
 /* Largest supported token budget per call, and largest cache capacity. */
 #define SJSA_MAX_K (1 << 20)
 #define SJSA_MAX_CAPACITY ((int64_t)1 << 30)

@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 from oracle import jssa
-from oracle.numerics import bf16_to_f32
+from oracle.numerics import bf16_to_f32, fp8e4m3_to_f32
 from tests.util import band_check, bits, from_bits
 
 # Output tolerance of the step for bf16 inputs with fp32 accumulation, bf16 output.
@@ -21,14 +21,15 @@ def say(*a):
     sys.stdout.flush()
 
 
-def kproj_oracle(K_bits: np.ndarray, M: np.ndarray) -> np.ndarray:
-    """Projected cache for every (b, h) from the oracle's key projection."""
+def kproj_oracle(K_bits: np.ndarray, M: np.ndarray, fmt: str = "bf16") -> np.ndarray:
+    """Projected cache for every (b, h) from the oracle's key projection (bf16 bits,
+    or FP8 E4M3 bytes with fmt="fp8")."""
     B, H, cap, _ = K_bits.shape
-    out = np.empty((B, H, cap, M.shape[1]), dtype=np.uint16)
+    out = np.empty((B, H, cap, M.shape[1]), dtype=np.uint8 if fmt == "fp8" else np.uint16)
     for b in range(B):
         for h in range(H):
             for r0 in range(0, cap, 4096):
-                out[b, h, r0:r0 + 4096] = jssa.project_keys(K_bits[b, h, r0:r0 + 4096], M[h])
+                out[b, h, r0:r0 + 4096] = jssa.project_keys(K_bits[b, h, r0:r0 + 4096], M[h], fmt)
     return out
 
 
@@ -48,6 +49,21 @@ def kproj_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, K_bits: np.ndarray, 
     return ok, float(np.mean(gpu_bits == ref_bits))
 
 
+def kproj_close_fp8(gpu_bytes: np.ndarray, ref_bytes: np.ndarray, K_bits: np.ndarray, M: np.ndarray):
+    """FP8 projected-cache parity: the GPU rounds its fp32 dot to E4M3 (saturating),
+    the oracle rounds the fp64 dot once. Allowed gap per element: one E4M3 quantum at
+    the larger magnitude (2^(e-3) for normals, 2^-9 below 2^-6) plus the fp32 dot error
+    bound. Returns (ok, fraction of identical bytes)."""
+    g = fp8e4m3_to_f32(gpu_bytes).astype(np.float64)
+    r = fp8e4m3_to_f32(ref_bytes).astype(np.float64)
+    kf = np.abs(bf16_to_f32(K_bits).astype(np.float64))
+    err = kf @ np.abs(M.astype(np.float64)).T * (M.shape[1] * 2.0 ** -24)
+    mag = np.maximum(np.abs(g), np.abs(r))
+    quantum = np.exp2(np.maximum(np.floor(np.log2(np.maximum(mag, 2.0 ** -9))), -6) - 3)
+    ok = bool(np.all(np.abs(g - r) <= quantum + err))
+    return ok, float(np.mean(gpu_bytes == ref_bytes))
+
+
 def kproj_torch(K: torch.Tensor, M: torch.Tensor) -> torch.Tensor:
     """Projected cache built with plain torch ops on the GPU (fp32 products, bf16
     round to nearest even). Used only to prepare inputs at sizes where the oracle's
@@ -60,16 +76,17 @@ def kproj_torch(K: torch.Tensor, M: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def ref_unit(q_bits, K_bits, V_bits, kproj_bits, M, b, h, G, n, k, scale):
+def ref_unit(q_bits, K_bits, V_bits, kproj_bits, M, b, h, G, n, k, scale, fmt="bf16"):
     """Oracle results for one unit: (out fp64 [G, d], idx, scores)."""
     return jssa.decode_unit(q_bits[b, h * G:(h + 1) * G], K_bits[b, h], V_bits[b, h], kproj_bits[b, h],
-                            M[h], n, k, scale)
+                            M[h], n, k, scale, fmt)
 
 
-def check_unit(gpu_out, gpu_idx, q_bits, K_bits, V_bits, kproj_bits, M, b, h, G, n, k, scale, tol, tag=""):
+def check_unit(gpu_out, gpu_idx, q_bits, K_bits, V_bits, kproj_bits, M, b, h, G, n, k, scale, tol, tag="",
+               fmt="bf16"):
     """Index-set parity (band rule) and output parity (oracle attention over the
     GPU's own index set; also over the oracle's set when the two sets agree)."""
-    ref_out, ref_idx, s = ref_unit(q_bits, K_bits, V_bits, kproj_bits, M, b, h, G, n, k, scale)
+    ref_out, ref_idx, s = ref_unit(q_bits, K_bits, V_bits, kproj_bits, M, b, h, G, n, k, scale, fmt)
     gi = np.asarray(gpu_idx)
     ok, msg = band_check(gi, ref_idx, s, n, k)
     assert ok, f"{tag} unit ({b},{h}): {msg}"
@@ -82,5 +99,5 @@ def check_unit(gpu_out, gpu_idx, q_bits, K_bits, V_bits, kproj_bits, M, b, h, G,
     return msg
 
 
-__all__ = ["kproj_close", "bits", "from_bits", "bf16_to_f32", "band_check", "kproj_oracle", "kproj_torch", "check_unit", "say",
+__all__ = ["kproj_close", "kproj_close_fp8", "bits", "from_bits", "bf16_to_f32", "band_check", "kproj_oracle", "kproj_torch", "check_unit", "say",
            "OUT_TOL_BF16", "OUT_TOL_F32"]

@@ -65,7 +65,7 @@ def _step(shape, k=16, ws_bytes=1 << 30, ptrs=None, sm_scale=0.0):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), -3), (dict(rank=24), -3), (dict(group=3), -3), (dict(group=16), -3),
-    (dict(flags=4), -3),
+    (dict(flags=8), -3),
     (dict(batch=0), -2), (dict(capacity=0), -2), (dict(capacity=(1 << 30) + 1), -2),
     (dict(batch=1000, n_kv_heads=100), -2),
 ])

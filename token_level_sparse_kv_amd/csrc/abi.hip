@@ -24,7 +24,7 @@ int check_shape(const sjsa_shape* s) {
   if (s->head_dim != HEAD_DIM) return SJSA_ERR_UNSUPPORTED;
   if (s->rank != 16 && s->rank != 32 && s->rank != 64) return SJSA_ERR_UNSUPPORTED;
   if (s->group != 1 && s->group != 2 && s->group != 4 && s->group != 8) return SJSA_ERR_UNSUPPORTED;
-  if (s->flags & ~(SJSA_FLAG_OUT_F32 | SJSA_FLAG_WRITE_SCORES)) return SJSA_ERR_UNSUPPORTED;
+  if (s->flags & ~(SJSA_FLAG_OUT_F32 | SJSA_FLAG_WRITE_SCORES | SJSA_FLAG_KPROJ_FP8)) return SJSA_ERR_UNSUPPORTED;
   return SJSA_OK;
 }
 
@@ -117,7 +117,7 @@ int sjsa_append_kv(const sjsa_shape* shape, const void* k_new, const void* v_new
     return SJSA_ERR_ALIGN;
   if ((n_new + 63) / 64 > 2147483647) return SJSA_ERR_DIMS;
   return status_of(launch_append(*shape, (const uint16_t*)k_new, (const uint16_t*)v_new, n_new, M, pos,
-                                 (uint16_t*)K, (uint16_t*)V, (uint16_t*)Kproj, (hipStream_t)stream));
+                                 (uint16_t*)K, (uint16_t*)V, Kproj, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -139,7 +139,7 @@ PrepAppend make_append(const void* k_new, const void* v_new, const int32_t* pos,
   ap.pos = pos;
   ap.K = (uint16_t*)K;
   ap.V = (uint16_t*)V;
-  ap.Kproj = (uint16_t*)Kproj;
+  ap.Kproj = (unsigned char*)Kproj;
   return ap;
 }
 
@@ -160,8 +160,8 @@ int sjsa_score(const sjsa_shape* shape, const void* q, const void* Kproj, const 
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s);
-  if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s);
+  if (e == hipSuccess) e = launch_score(*shape, L, (const void*)Kproj, seq_len, ws, s);
   return status_of(e);
 }
 
@@ -176,7 +176,7 @@ int sjsa_prep(const sjsa_shape* shape, const void* q, const float* M, const void
     return SJSA_ERR_ALIGN;
   const Layout L = make_layout(*shape, k);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
-  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k,
+  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k,
                                (unsigned char*)workspace, (hipStream_t)stream));
 }
 
@@ -194,7 +194,7 @@ int sjsa_prep_append(const sjsa_shape* shape, const void* k_new, const void* v_n
   const Layout L = make_layout(*shape, k);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
   const PrepAppend ap = make_append(k_new, v_new, pos, K, V, Kproj);
-  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k,
+  return status_of(launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k,
                                (unsigned char*)workspace, (hipStream_t)stream, &ap));
 }
 
@@ -206,7 +206,7 @@ int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len
   if (!aligned(Kproj, 16) || !aligned(seq_len, 4) || !aligned(workspace, WS_ALIGN)) return SJSA_ERR_ALIGN;
   const Layout L = make_layout(*shape, 1);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
-  return status_of(launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, (unsigned char*)workspace,
+  return status_of(launch_score(*shape, L, (const void*)Kproj, seq_len, (unsigned char*)workspace,
                                 (hipStream_t)stream));
 }
 
@@ -220,7 +220,7 @@ int sjsa_select(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_l
     return SJSA_ERR_ALIGN;
   const Layout L = make_layout(*shape, k);
   if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
-  return status_of(launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx,
+  return status_of(launch_select(*shape, L, nullptr, 0, (const void*)Kproj, seq_len, k, idx,
                                  (unsigned char*)workspace, (hipStream_t)stream));
 }
 
@@ -274,9 +274,9 @@ int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, cons
   if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s);
-  if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
-  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx, ws, s);
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s);
+  if (e == hipSuccess) e = launch_score(*shape, L, (const void*)Kproj, seq_len, ws, s);
+  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const void*)Kproj, seq_len, k, idx, ws, s);
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
                       resolve_scale(sm_scale), out, ws, s);
@@ -301,9 +301,9 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const PrepAppend ap = make_append(k_new, v_new, pos, K, V, Kproj);
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const uint16_t*)Kproj, seq_len, k, ws, s, &ap);
-  if (e == hipSuccess) e = launch_score(*shape, L, (const uint16_t*)Kproj, seq_len, ws, s);
-  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const uint16_t*)Kproj, seq_len, k, idx, ws, s);
+  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s, &ap);
+  if (e == hipSuccess) e = launch_score(*shape, L, (const void*)Kproj, seq_len, ws, s);
+  if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const void*)Kproj, seq_len, k, idx, ws, s);
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
                       resolve_scale(sm_scale), out, ws, s);

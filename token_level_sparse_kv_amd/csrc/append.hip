@@ -1,5 +1,6 @@
 // Cache append: write the new tokens' K and V rows and their projected scoring
-// rows Kproj = bf16_rne(M_h k_new) (fp32 dot over d).
+// rows Kproj = M_h k_new (fp32 dot over d, rounded to bf16 or, with
+// SJSA_FLAG_KPROJ_FP8, to FP8 E4M3).
 // Source: JSSA article, section 投影打分缓存与校准成本 (the scoring cache Kproj =
 // K M^T is kept next to the original KV cache) and section 组件级拆解 (projecting
 // each new key is the pipeline's cheapest stage).
@@ -15,11 +16,11 @@ constexpr int APPEND_ROWS = 64;                 // token rows per workgroup
 // V rows (16 bytes each), then project them with the KeyProj layout, each thread
 // holding its basis slice in registers for all the workgroup's rows, so a projected
 // row's bits do not depend on how many tokens one call appends.
-template <int R>
+template <int R, int KB>
 __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n_new,
     const float* __restrict__ M, const int32_t* __restrict__ pos,
-    uint16_t* __restrict__ K, uint16_t* __restrict__ V, uint16_t* __restrict__ Kproj,
+    uint16_t* __restrict__ K, uint16_t* __restrict__ V, unsigned char* __restrict__ Kproj,
     int n_kv_heads, int64_t cap) {
   using KP = KeyProj<R>;
   static_assert(KP::THREADS == APPEND_THREADS, "one projection layout");
@@ -51,24 +52,31 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(
     KP::load_key(k_new + src0 + (size_t)r * HEAD_DIM, tid, kv);
     const float acc = KP::dot(mv, kv);
     const int64_t p = p0 + r;
-    if (part == 0 && p >= 0 && p < cap)
-      Kproj[((size_t)unit * cap + p) * R + i] = (uint16_t)f32_to_bf16_rne(acc);
+    if (part == 0 && p >= 0 && p < cap) KP::template store<KB>(Kproj + ((size_t)unit * cap + p) * R * KB, i, acc);
   }
 }
 
 }  // namespace
 
 hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
-                         const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, uint16_t* Kproj,
+                         const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, void* Kproj_v,
                          hipStream_t st) {
+  unsigned char* Kproj = static_cast<unsigned char*>(Kproj_v);
+  const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
   const dim3 block(APPEND_THREADS);
   const dim3 grid((n_new + APPEND_ROWS - 1) / APPEND_ROWS, s.batch * s.n_kv_heads);
+#define SJSA_APPEND(RR)                                                                                          \
+  if (fp8) append_kernel<RR, 1><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads, \
+                                                         s.capacity);                                            \
+  else append_kernel<RR, 2><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads,      \
+                                                     s.capacity)
   switch (s.rank) {
-    case 16: append_kernel<16><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads, s.capacity); break;
-    case 32: append_kernel<32><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads, s.capacity); break;
-    case 64: append_kernel<64><<<grid, block, 0, st>>>(k_new, v_new, n_new, M, pos, K, V, Kproj, s.n_kv_heads, s.capacity); break;
+    case 16: SJSA_APPEND(16); break;
+    case 32: SJSA_APPEND(32); break;
+    case 64: SJSA_APPEND(64); break;
     default: return hipErrorInvalidValue;
   }
+#undef SJSA_APPEND
   return hipGetLastError();
 }
 

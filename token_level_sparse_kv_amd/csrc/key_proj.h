@@ -1,6 +1,7 @@
-// Projection of one new key row onto the scoring basis, Kproj = bf16_rne(M_h k)
-// (fp32 dot over d), shared by the append kernel and the fused append in the prep
-// kernel so that a projected row's bits do not depend on which call wrote it.
+// Projection of one new key row onto the scoring basis, Kproj = M_h k (fp32 dot over
+// d, rounded to the cache format: bf16 or FP8 E4M3), shared by the append kernel
+// and the fused append in the prep kernel so that a projected row's bits do not
+// depend on which call wrote it.
 //
 // 256 threads: output i of the projected row is split over TPO = 256 / R lanes,
 // lane `part` owning channels part*CH .. part*CH + CH - 1 (CH = d / TPO) of basis
@@ -30,6 +31,13 @@ struct KeyProj {
   __device__ static void load_key(const uint16_t* krow, int t, u32x4 (&kv)[CH / 8]) {
 #pragma unroll
     for (int c = 0; c < CH / 8; ++c) kv[c] = ld16(krow + (t % TPO) * CH + c * 8);
+  }
+  // element i of a projected row in the cache format: bf16 (KB = 2, nearest even) or
+  // OCP FP8 E4M3 (KB = 1, nearest even, saturating)
+  template <int KB>
+  __device__ static void store(unsigned char* row, int i, float v) {
+    if constexpr (KB == 2) reinterpret_cast<uint16_t*>(row)[i] = (uint16_t)f32_to_bf16_rne(v);
+    else row[i] = (unsigned char)f32_to_fp8_sat(v);
   }
   // combined dot (valid in the lane with t % TPO == 0); every lane of the wave calls
   __device__ static float dot(const f32x4 (&mv)[CH / 4], const u32x4 (&kv)[CH / 8]) {

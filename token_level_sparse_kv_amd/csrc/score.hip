@@ -82,12 +82,13 @@ __device__ __forceinline__ int64_t sample_row(int s, int64_t n) {
 // 0..255 write its projected row with the KeyProj layout (bit-identical to the
 // append kernel). A sample that lands on that slot may read the row before or
 // after the write; either way only the threshold moves, never the result.
-template <int R, bool APPEND>
+template <int R, int KB, bool APPEND>
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ M, const uint16_t* kproj,
+    const uint16_t* __restrict__ q, const float* __restrict__ M, const unsigned char* kproj,
     const int32_t* __restrict__ seq_len, int k, float* __restrict__ qhat, uint32_t* __restrict__ tlow,
     int n_kv_heads, int group, int64_t cap, PrepAppend ap) {
-  constexpr int LPR = R / 8;                          // 16-byte words per Kproj row
+  constexpr int LPR = R * KB / 16;                    // 16-byte words per Kproj row
+  constexpr int VPC = 16 / KB;                        // values per 16-byte word
   constexpr int RPL = 64 / LPR;                       // samples per wave-wide load
   constexpr int NS = samples_for<R>();
   constexpr int BATCHES = NS / PREP_THREADS;          // 64-sample batches per wave (= samples per lane)
@@ -133,14 +134,14 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
   const int p = lane % LPR, rs = lane / LPR;
   u32x4 w[BATCHES][LPR];
   if (sampling) {
-    const uint16_t* base = kproj + (size_t)unit * cap * R + p * 8;
+    const unsigned char* base = kproj + (size_t)unit * cap * R * KB + p * 16;
 #pragma unroll
     for (int t = 0; t < BATCHES; ++t) {
 #pragma unroll
       for (int i = 0; i < LPR; ++i) {
         const int sidx = min(64 * (wave + t * PREP_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
         const int64_t pos = sample_row<NS>(sidx, n);
-        w[t][i] = ld16_stream(base + pos * R);
+        w[t][i] = ld16_stream(base + pos * R * KB);
       }
     }
   }
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     if (tid < KP::THREADS) {                          // whole waves: the DPP combine needs them
       const float acc = KP::dot(amv, akv);
       if (tid % KP::TPO == 0 && apos >= 0 && apos < cap)
-        ap.Kproj[((size_t)unit * cap + apos) * R + tid / KP::TPO] = (uint16_t)f32_to_bf16_rne(acc);
+        KP::template store<KB>(ap.Kproj + ((size_t)unit * cap + apos) * R * KB, tid / KP::TPO, acc);
     }
   }
   for (int i = tid; i < PREP_BINS; i += PREP_THREADS) shist[i] = 0u;
@@ -201,11 +202,11 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     return;
   }
 
-  // lane (rs, p) scores its 8 columns of the LPR rows of a batch; the transposed
+  // lane (rs, p) scores its VPC columns of the LPR rows of a batch; the transposed
   // reduction leaves it the score of sample sb + p * RPL + rs
-  float qh[8];
+  float qh[VPC];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qh[e] = sqh[p * 8 + e];
+  for (int e = 0; e < VPC; ++e) qh[e] = sqh[p * VPC + e];
   float sc[BATCHES];
   int sid[BATCHES];
   float lo = __builtin_inff(), hi = -__builtin_inff();
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
   for (int t = 0; t < BATCHES; ++t) {
     float a[LPR];
 #pragma unroll
-    for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(qh, w[t][i]);
+    for (int i = 0; i < LPR; ++i) a[i] = dot_chunk<KB>(qh, w[t][i]);
     sc[t] = transpose_reduce<LPR>(a, p);
     sid[t] = 64 * (wave + t * PREP_WAVES) + p * RPL + rs;
     if (sid[t] < S && __builtin_isfinite(sc[t])) {
@@ -299,13 +300,14 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 // greatest key (high word; 0 when there are none); writes in the
 // middle of the stream cost far more HBM time than their size. With WRITE_DENSE
 // every score is also stored.
-template <int R, int UNROLL, bool WRITE_DENSE>
+template <int R, int KB, int UNROLL, bool WRITE_DENSE>
 __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
-    const uint16_t* __restrict__ kproj, const float* __restrict__ qhat, const uint32_t* __restrict__ tlow,
+    const unsigned char* __restrict__ kproj, const float* __restrict__ qhat, const uint32_t* __restrict__ tlow,
     const int32_t* __restrict__ seq_len, float* __restrict__ scores, uint32_t* __restrict__ cand,
     uint64_t* __restrict__ counts, int n_kv_heads, int64_t cap, int64_t stride, int64_t ntile_cap,
     int64_t cand_stride) {
-  constexpr int LPR = R / 8;            // lanes per Kproj row (16 bytes each)
+  constexpr int LPR = R * KB / 16;      // lanes per Kproj row (16 bytes each)
+  constexpr int VPC = 16 / KB;          // values per 16-byte word
   constexpr int RPL = 64 / LPR;         // rows per wave-wide load
   static_assert(GROUP_ROWS * UNROLL == SEG_ROWS, "one wave iteration covers one segment");
   static_assert(TILE_ROWS / SEG_ROWS <= 64, "one wave scans the segment counts");
@@ -334,11 +336,11 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
   for (int i = 0; i < RPL; ++i) col0 |= 1ull << (i * LPR);
   const uint64_t earlier = col0 * ((1ull << p) - 1) | ((col0 << p) & ((1ull << (LPR * rs)) - 1));
 
-  float qh[8];
+  float qh[VPC];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qh[e] = qhat[(size_t)unit * QHAT_STRIDE + p * 8 + e];
+  for (int e = 0; e < VPC; ++e) qh[e] = qhat[(size_t)unit * QHAT_STRIDE + p * VPC + e];
 
-  const uint16_t* base = kproj + (size_t)unit * cap * R + p * 8;
+  const unsigned char* base = kproj + (size_t)unit * cap * R * KB + p * 16;
   float* srow = scores + (size_t)unit * stride;
   const int last = n - 1;
   uint32_t wcount = 0;                     // candidates of this wave so far
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
         // rows past the end are clamped to the last valid row (never reported), so
         // every load is unconditional and the whole batch stays in flight
         const int row = min(g0 + u * GROUP_ROWS + i * RPL + rs, last);
-        w[u][i] = ld16_stream(base + (size_t)row * R);
+        w[u][i] = ld16_stream(base + (size_t)row * R * KB);
       }
     }
     uint32_t count = 0;
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     for (int u = 0; u < UNROLL; ++u) {
       float a[LPR];
 #pragma unroll
-      for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(qh, w[u][i]);
+      for (int i = 0; i < LPR; ++i) a[i] = dot_chunk<KB>(qh, w[u][i]);
       const float s = transpose_reduce<LPR>(a, p);
       const int row = g0 + u * GROUP_ROWS + p * RPL + rs;
       const bool valid = row < n;
@@ -433,17 +435,20 @@ constexpr int SCORE_UNROLL = 2;
 }  // namespace
 
 hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
-                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
+                       const void* kproj_v, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
                        const PrepAppend* ap) {
+  const unsigned char* kproj = static_cast<const unsigned char*>(kproj_v);
+  const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
   float* qhat = reinterpret_cast<float*>(ws + L.off_qhat);
   uint32_t* tlow = reinterpret_cast<uint32_t*>(ws + L.off_tlow);
   const dim3 grid((unsigned)L.units), block(PREP_THREADS);
   const PrepAppend none{};
-#define SJSA_PREP(RR)                                                                                   \
-  if (ap) prep_kernel<RR, true><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads,  \
-                                                          s.group, s.capacity, *ap);                      \
-  else prep_kernel<RR, false><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads,   \
-                                                        s.group, s.capacity, none)
+#define SJSA_PREP2(RR, KB)                                                                              \
+  if (ap) prep_kernel<RR, KB, true><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads, \
+                                                              s.group, s.capacity, *ap);                   \
+  else prep_kernel<RR, KB, false><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads,  \
+                                                            s.group, s.capacity, none)
+#define SJSA_PREP(RR) if (fp8) { SJSA_PREP2(RR, 1); } else { SJSA_PREP2(RR, 2); }
   switch (s.rank) {
     case 16: SJSA_PREP(16); break;
     case 32: SJSA_PREP(32); break;
@@ -451,11 +456,14 @@ hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, 
     default: return hipErrorInvalidValue;
   }
 #undef SJSA_PREP
+#undef SJSA_PREP2
   return hipGetLastError();
 }
 
-hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kproj, const int32_t* seq_len,
+hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj_v, const int32_t* seq_len,
                         unsigned char* ws, hipStream_t st) {
+  const unsigned char* kproj = static_cast<const unsigned char*>(kproj_v);
+  const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
   const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* scores = reinterpret_cast<float*>(ws + L.off_scores);
@@ -463,17 +471,24 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kp
   uint64_t* counts = reinterpret_cast<uint64_t*>(ws + L.off_counts);
   const dim3 grid((unsigned)((s.capacity + TILE_ROWS - 1) / TILE_ROWS), (unsigned)L.units), block(SCORE_THREADS);
   const bool dense = (s.flags & SJSA_FLAG_WRITE_SCORES) != 0;
-#define SJSA_SCAN(RR, DD)                                                                          \
-  score_kernel<RR, SCORE_UNROLL, DD><<<grid, block, 0, st>>>(kproj, qhat, tlow, seq_len, scores, cand, \
+#define SJSA_SCAN2(RR, KB, DD)                                                                     \
+  score_kernel<RR, KB, SCORE_UNROLL, DD><<<grid, block, 0, st>>>(kproj, qhat, tlow, seq_len, scores, cand, \
                                                              counts, s.n_kv_heads, s.capacity,       \
                                                              L.score_stride, L.ntile_cap, L.cand_stride)
+#define SJSA_SCAN(RR)                                              \
+  if (fp8) {                                                       \
+    if (dense) SJSA_SCAN2(RR, 1, true); else SJSA_SCAN2(RR, 1, false); \
+  } else {                                                         \
+    if (dense) SJSA_SCAN2(RR, 2, true); else SJSA_SCAN2(RR, 2, false); \
+  }
   switch (s.rank) {
-    case 16: if (dense) SJSA_SCAN(16, true); else SJSA_SCAN(16, false); break;
-    case 32: if (dense) SJSA_SCAN(32, true); else SJSA_SCAN(32, false); break;
-    case 64: if (dense) SJSA_SCAN(64, true); else SJSA_SCAN(64, false); break;
+    case 16: SJSA_SCAN(16); break;
+    case 32: SJSA_SCAN(32); break;
+    case 64: SJSA_SCAN(64); break;
     default: return hipErrorInvalidValue;
   }
 #undef SJSA_SCAN
+#undef SJSA_SCAN2
   return hipGetLastError();
 }
 

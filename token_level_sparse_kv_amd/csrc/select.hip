@@ -568,21 +568,21 @@ __device__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, 
 }
 
 // Recompute a unit's dense scores (bit-identical to the scan) into row[0..n).
-template <int R>
-__device__ void recompute_scores(const uint16_t* kproj_unit, const float* qhat_unit, int64_t n, float* row) {
+template <int R, int KB>
+__device__ void recompute_scores(const unsigned char* kproj_unit, const float* qhat_unit, int64_t n, float* row) {
   float q[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) q[i] = qhat_unit[i];
-  for (int64_t j = threadIdx.x; j < n; j += SEL_THREADS) row[j] = row_score<R>(q, kproj_unit + j * R);
+  for (int64_t j = threadIdx.x; j < n; j += SEL_THREADS) row[j] = row_score<R, KB>(q, kproj_unit + j * R * KB);
   __syncthreads();
 }
 
 // grid = B * H_kv. scores != nullptr: dense selection over caller scores (stride
 // `stride`). Otherwise: take-all, candidate path, or recompute + dense selection.
-template <int R>
+template <int R, int KB>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
-    int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const uint16_t* __restrict__ kproj,
+    int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const unsigned char* __restrict__ kproj,
     const float* __restrict__ qhat, const uint32_t* __restrict__ tlow, const uint32_t* __restrict__ cand,
     const uint64_t* __restrict__ counts, float* __restrict__ dense, int64_t dense_stride, int64_t ntile_cap,
     int64_t cand_stride) {
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     uint32_t T = lds_threshold_range(ckey, (int)total, tkey >> CAND_ROW_BITS, kmax >> CAND_ROW_BITS,
                                      (uint32_t)kk, sh, &needT, &all_eq);
     if (needT == 0xffffffffu) all_eq = true;
-    const uint16_t* kp_unit = kproj + (size_t)unit * cap * R;
+    const unsigned char* kp_unit = kproj + (size_t)unit * cap * R * KB;
     int nb = 0;                                   // entries on the boundary truncated key T
     if (!all_eq && needT > 0) {
       // only some entries of the boundary truncated key T are taken: list them
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         uint32_t ex = 0u;
         if (lane < nb) {
           li = (int)bidx[lane];
-          ex = score_key(row_score<R>(sh.qh, kp_unit + (size_t)cpos[li] * R));
+          ex = score_key(row_score<R, KB>(sh.qh, kp_unit + (size_t)cpos[li] * R * KB));
         }
         uint32_t rank = 0;
         for (int j = 0; j < nb; ++j) {
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       for (int i = tid; i < (int)total; i += SEL_THREADS) {
         const uint32_t kt = ckey[i];
         uint32_t low = 0;
-        if (kt == T) low = score_key(row_score<R>(sh.qh, kp_unit + (size_t)cpos[i] * R)) & CAND_ROW_MASK;
+        if (kt == T) low = score_key(row_score<R, KB>(sh.qh, kp_unit + (size_t)cpos[i] * R * KB)) & CAND_ROW_MASK;
         ckey[i] = (kt << CAND_ROW_BITS) | low;
       }
       for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
@@ -761,14 +761,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   }
   // the sampled threshold misjudged this unit: exact selection over recomputed scores
   float* row = dense + (size_t)unit * dense_stride;
-  recompute_scores<R>(kproj + (size_t)unit * cap * R, qhat + (size_t)unit * QHAT_STRIDE, n, row);
+  recompute_scores<R, KB>(kproj + (size_t)unit * cap * R * KB, qhat + (size_t)unit * QHAT_STRIDE, n, row);
   select_dense(row, n, kk, out, sh);
 }
 
 }  // namespace
 
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
-                         const uint16_t* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
+                         const void* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
                          hipStream_t st) {
   const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
   const uint32_t* cand = reinterpret_cast<const uint32_t*>(ws + L.off_cand);
@@ -776,14 +776,16 @@ hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scor
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* dense = reinterpret_cast<float*>(ws + L.off_scores);
   const dim3 grid((unsigned)L.units), block(SEL_THREADS);
-#define SJSA_SEL(RR)                                                                                   \
-  select_kernel<RR><<<grid, block, 0, st>>>(scores, stride, seq_len, s.n_kv_heads, s.capacity, k, idx, \
-                                            kproj, qhat, tlow, cand, counts, dense, L.score_stride, L.ntile_cap,  \
-                                            L.cand_stride)
+  const unsigned char* kp = static_cast<const unsigned char*>(kproj);
+  const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
+#define SJSA_SEL(RR, KB)                                                                                \
+  select_kernel<RR, KB><<<grid, block, 0, st>>>(scores, stride, seq_len, s.n_kv_heads, s.capacity, k, idx, \
+                                                kp, qhat, tlow, cand, counts, dense, L.score_stride,      \
+                                                L.ntile_cap, L.cand_stride)
   switch (s.rank) {
-    case 16: SJSA_SEL(16); break;
-    case 32: SJSA_SEL(32); break;
-    case 64: SJSA_SEL(64); break;
+    case 16: if (fp8) SJSA_SEL(16, 1); else SJSA_SEL(16, 2); break;
+    case 32: if (fp8) SJSA_SEL(32, 1); else SJSA_SEL(32, 2); break;
+    case 64: if (fp8) SJSA_SEL(64, 1); else SJSA_SEL(64, 2); break;
     default: return hipErrorInvalidValue;
   }
 #undef SJSA_SEL

@@ -119,6 +119,40 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Dot of 16 fp32 values with the 16 OCP FP8 E4M3 values packed in a 128-bit word
+// (hardware decoding, two values per instruction; sum in element order).
+__device__ __forceinline__ float dot16_fp8(const float* q, u32x4 w) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[i], true);
+    a = i == 0 ? q[0] * lo[0] : fmaf(q[4 * i], lo[0], a);
+    a = fmaf(q[4 * i + 1], lo[1], a);
+    a = fmaf(q[4 * i + 2], hi[0], a);
+    a = fmaf(q[4 * i + 3], hi[1], a);
+  }
+  return a;
+}
+
+// Dot of the q slice with one 16-byte chunk of a projected row: 8 bf16 values
+// (KB = 2 bytes per element) or 16 fp8 values (KB = 1).
+template <int KB>
+__device__ __forceinline__ float dot_chunk(const float* q, u32x4 w) {
+  if constexpr (KB == 2) return dot8_bf16(q, w);
+  else return dot16_fp8(q, w);
+}
+
+// OCP FP8 E4M3 code of an fp32 value: nearest, ties to even, saturating at +-448,
+// NaN to 0x7F (the hardware conversion rounds to nearest even; the clamp makes it
+// saturate).
+__device__ __forceinline__ uint32_t f32_to_fp8_sat(float f) {
+  if (f != f) return 0x7Fu;
+  const float c = fminf(fmaxf(f, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.f, 0, false) & 0xFFu;
+}
+
 // Wave-wide (64 lanes) inclusive prefix sum of a u32: DPP scans inside the four rows
 // of 16 lanes, then each row adds the totals of the rows before it (read from lanes
 // 15, 31 and 47). Every lane of the wave must be active.
@@ -161,6 +195,9 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // distances 1 and 2, a swizzle for 4).
 template <int LPR>
 __device__ __forceinline__ float transpose_reduce(float (&a)[LPR], int p) {
+  if constexpr (LPR == 1) {
+    return a[0];
+  } else {
   float b[LPR / 2];
   const bool odd = p & 1;
 #pragma unroll
@@ -189,19 +226,23 @@ __device__ __forceinline__ float transpose_reduce(float (&a)[LPR], int p) {
       return keep + swz_xor4(send);
     }
   }
+  }
 }
 
-// Score of one projected row by one lane from its r/8 16-byte words: the partial
-// dots are summed in the balanced tree the transposed wave reduction uses, so
-// identical rows get bit-identical scores whichever code path computes them. q holds
-// q_hat (r fp32).
-template <int R>
-__device__ __forceinline__ float row_score_words(const float* q, const u32x4 (&w)[R / 8]) {
-  constexpr int LPR = R / 8;
+// Score of one projected row by one lane from its 16-byte chunks (r*KB/16 of them,
+// KB = bytes per stored element): the chunk dots are summed in the balanced tree the
+// transposed wave reduction uses, so identical rows get bit-identical scores
+// whichever code path computes them. q holds q_hat (r fp32).
+template <int R, int KB>
+__device__ __forceinline__ float row_score_words(const float* q, const u32x4 (&w)[R * KB / 16]) {
+  constexpr int LPR = R * KB / 16;
+  constexpr int VPC = 16 / KB;                 // values per chunk
   float a[LPR];
 #pragma unroll
-  for (int i = 0; i < LPR; ++i) a[i] = dot8_bf16(q + 8 * i, w[i]);
-  if constexpr (LPR == 2) {
+  for (int i = 0; i < LPR; ++i) a[i] = dot_chunk<KB>(q + VPC * i, w[i]);
+  if constexpr (LPR == 1) {
+    return a[0];
+  } else if constexpr (LPR == 2) {
     return a[0] + a[1];
   } else if constexpr (LPR == 4) {
     return (a[0] + a[1]) + (a[2] + a[3]);
@@ -210,12 +251,12 @@ __device__ __forceinline__ float row_score_words(const float* q, const u32x4 (&w
   }
 }
 
-template <int R>
-__device__ __forceinline__ float row_score(const float* q, const uint16_t* rowp) {
-  u32x4 w[R / 8];
+template <int R, int KB>
+__device__ __forceinline__ float row_score(const float* q, const unsigned char* rowp) {
+  u32x4 w[R * KB / 16];
 #pragma unroll
-  for (int i = 0; i < R / 8; ++i) w[i] = ld16(rowp + 8 * i);
-  return row_score_words<R>(q, w);
+  for (int i = 0; i < R * KB / 16; ++i) w[i] = ld16(rowp + 16 * i);
+  return row_score_words<R, KB>(q, w);
 }
 
 }  // namespace sjsa

@@ -45,7 +45,7 @@ Layout make_layout(const sjsa_shape& s, int k);
 
 // Kernel launchers (device pointers; host-validated arguments).
 hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
-                         const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, uint16_t* Kproj,
+                         const float* M, const int32_t* pos, uint16_t* K, uint16_t* V, void* Kproj,
                          hipStream_t st);
 // The new token of a decode step, appended by the prep kernel (one token per sequence).
 struct PrepAppend {
@@ -54,18 +54,18 @@ struct PrepAppend {
   const int32_t* pos = nullptr;      // [B]
   uint16_t* K = nullptr;
   uint16_t* V = nullptr;
-  uint16_t* Kproj = nullptr;
+  unsigned char* Kproj = nullptr;     // bf16 or fp8 elements (SJSA_FLAG_KPROJ_FP8)
 };
 // ap != nullptr: the prep kernel also appends the new token (see PrepAppend).
 hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
-                       const uint16_t* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
+                       const void* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
                        const PrepAppend* ap = nullptr);
-hipError_t launch_score(const sjsa_shape& s, const Layout& L, const uint16_t* kproj, const int32_t* seq_len,
+hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj, const int32_t* seq_len,
                         unsigned char* ws, hipStream_t st);
 // scores == nullptr: select from the scan's candidates in the workspace (recomputing a
 // unit's scores from kproj/qhat when needed); else exact top-k of the given dense scores.
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
-                         const uint16_t* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
+                         const void* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
                          hipStream_t st);
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "lib", "libsjsa.so")
 
 SJSA_FLAG_OUT_F32 = 1
 SJSA_FLAG_WRITE_SCORES = 2
+SJSA_FLAG_KPROJ_FP8 = 4
+KPROJ_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # OCP E4M3 bytes
 SJSA_MAX_K = 1 << 20
 
 
@@ -87,9 +89,29 @@ def _check(status: int):
         raise SjsaError(status, lib().sjsa_status_string(status).decode())
 
 
-def make_shape(batch, n_kv_heads, group, head_dim, rank, capacity, out_f32=False, write_scores=False) -> Shape:
-    flags = (SJSA_FLAG_OUT_F32 if out_f32 else 0) | (SJSA_FLAG_WRITE_SCORES if write_scores else 0)
+def make_shape(batch, n_kv_heads, group, head_dim, rank, capacity, out_f32=False, write_scores=False,
+               kproj_fp8=False) -> Shape:
+    flags = ((SJSA_FLAG_OUT_F32 if out_f32 else 0) | (SJSA_FLAG_WRITE_SCORES if write_scores else 0)
+             | (SJSA_FLAG_KPROJ_FP8 if kproj_fp8 else 0))
     return Shape(batch, n_kv_heads, group, head_dim, rank, flags, capacity)
+
+
+def kproj_is_fp8(Kproj: torch.Tensor) -> bool:
+    """The projected cache is bf16, or FP8 E4M3 given as uint8 / float8_e4m3fn bytes."""
+    if Kproj.dtype == torch.bfloat16:
+        return False
+    if Kproj.dtype in KPROJ_FP8_DTYPES:
+        return True
+    raise TypeError(f"Kproj must be bfloat16, uint8 or float8_e4m3fn (got {Kproj.dtype})")
+
+
+def _need_kproj(Kproj: torch.Tensor, shape=None, fp8=None):
+    """Kproj checks; with fp8 given, its format must match the call's shape flags."""
+    is8 = kproj_is_fp8(Kproj)
+    if fp8 is not None and is8 != bool(fp8):
+        raise TypeError("Kproj's dtype does not match the shape's SJSA_FLAG_KPROJ_FP8 flag")
+    _need(Kproj, "Kproj", Kproj.dtype, shape)
+    return is8
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -114,12 +136,13 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def shape_of(q: torch.Tensor, K: torch.Tensor, M: torch.Tensor, out_f32=False) -> Shape:
+def shape_of(q: torch.Tensor, K: torch.Tensor, M: torch.Tensor, out_f32=False, Kproj=None) -> Shape:
     B, Hkv, cap, d = K.shape
     Hq = q.shape[1]
     if Hq % Hkv:
         raise ValueError("query heads must be a multiple of KV heads")
-    return make_shape(B, Hkv, Hq // Hkv, d, M.shape[1], cap, out_f32)
+    fp8 = Kproj is not None and kproj_is_fp8(Kproj)
+    return make_shape(B, Hkv, Hq // Hkv, d, M.shape[1], cap, out_f32, kproj_fp8=fp8)
 
 
 def workspace_size(shape: Shape, k: int) -> int:
@@ -149,12 +172,12 @@ def append_kv(k_new, v_new, M, pos, K, V, Kproj, stream=None):
     T = k_new.shape[2]
     _need(K, "K", torch.bfloat16)
     _need(V, "V", torch.bfloat16, K.shape)
-    _need(Kproj, "Kproj", torch.bfloat16, (B, Hkv, cap, r))
+    fp8 = _need_kproj(Kproj, (B, Hkv, cap, r))
     _need(k_new, "k_new", torch.bfloat16, (B, Hkv, T, d))
     _need(v_new, "v_new", torch.bfloat16, (B, Hkv, T, d))
     _need(M, "M", torch.float32, (Hkv, r, d))
     _need(pos, "pos", torch.int32, (B,))
-    shape = make_shape(B, Hkv, 1, d, r, cap)
+    shape = make_shape(B, Hkv, 1, d, r, cap, kproj_fp8=fp8)
     _check(lib().sjsa_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), T, _ptr(M), _ptr(pos),
                                 _ptr(K), _ptr(V), _ptr(Kproj), _stream(stream)))
 
@@ -168,7 +191,7 @@ def _step_checks(q, K, V, Kproj, M, seq_len):
     _need(K, "K", torch.bfloat16)
     _need(V, "V", torch.bfloat16, K.shape)
     if Kproj is not None:
-        _need(Kproj, "Kproj", torch.bfloat16, (B, Hkv, cap, r))
+        _need_kproj(Kproj, (B, Hkv, cap, r))
     _need(M, "M", torch.float32, (Hkv, r, d))
     _need(seq_len, "seq_len", torch.int32, (B,))
 
@@ -177,7 +200,7 @@ def decode_step(q, K, V, Kproj, M, seq_len, k, sm_scale=0.0, out=None, idx=None,
                 out_f32=False, stream=None):
     """One sparse decode step. Returns (out [B, H_q, d], idx [B, H_kv, k])."""
     _step_checks(q, K, V, Kproj, M, seq_len)
-    shape = shape_of(q, K, M, out_f32)
+    shape = shape_of(q, K, M, out_f32, Kproj)
     B, Hkv = shape.batch, shape.n_kv_heads
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
@@ -207,7 +230,7 @@ def decode_step_append(k_new, v_new, pos, q, K, V, Kproj, M, seq_len, k, sm_scal
     by decode_step. Returns (out, idx)."""
     _step_checks(q, K, V, Kproj, M, seq_len)
     _append_one_checks(k_new, v_new, pos, K, M)
-    shape = shape_of(q, K, M, out_f32)
+    shape = shape_of(q, K, M, out_f32, Kproj)
     B, Hkv = shape.batch, shape.n_kv_heads
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
@@ -230,9 +253,10 @@ def score(q, Kproj, M, seq_len, k, workspace, write_scores=False, stream=None):
     [B, H_kv, stride] view; otherwise returns None."""
     B, Hkv, cap, r = Kproj.shape
     d = M.shape[2]
-    shape = make_shape(B, Hkv, q.shape[1] // Hkv, d, r, cap, write_scores=write_scores)
+    shape = make_shape(B, Hkv, q.shape[1] // Hkv, d, r, cap, write_scores=write_scores,
+                       kproj_fp8=kproj_is_fp8(Kproj))
     _need(q, "q", torch.bfloat16, (B, shape.group * Hkv, d))
-    _need(Kproj, "Kproj", torch.bfloat16)
+    _need_kproj(Kproj)
     _need(M, "M", torch.float32, (Hkv, r, d))
     _need(seq_len, "seq_len", torch.int32, (B,))
     _check(lib().sjsa_score(ctypes.byref(shape), _ptr(q), _ptr(Kproj), _ptr(M), _ptr(seq_len), int(k),
@@ -244,7 +268,7 @@ def prep(shape: Shape, q, M, Kproj, seq_len, k, workspace, stream=None):
     """Scoring prep only (mean query, projection, candidate threshold for budget k)."""
     _need(q, "q", torch.bfloat16, (shape.batch, shape.n_kv_heads * shape.group, shape.head_dim))
     _need(M, "M", torch.float32, (shape.n_kv_heads, shape.rank, shape.head_dim))
-    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need_kproj(Kproj, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank), bool(shape.flags & SJSA_FLAG_KPROJ_FP8))
     _need(seq_len, "seq_len", torch.int32, (shape.batch,))
     _check(lib().sjsa_prep(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(Kproj), _ptr(seq_len), int(k),
                            _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -256,7 +280,7 @@ def prep_append(shape: Shape, k_new, v_new, pos, q, K, V, M, Kproj, seq_len, k, 
     _need(M, "M", torch.float32, (shape.n_kv_heads, shape.rank, shape.head_dim))
     _need(K, "K", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.head_dim))
     _need(V, "V", torch.bfloat16, K.shape)
-    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need_kproj(Kproj, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank), bool(shape.flags & SJSA_FLAG_KPROJ_FP8))
     _need(seq_len, "seq_len", torch.int32, (shape.batch,))
     _append_one_checks(k_new, v_new, pos, K, M)
     _check(lib().sjsa_prep_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(q), _ptr(K),
@@ -266,7 +290,7 @@ def prep_append(shape: Shape, k_new, v_new, pos, q, K, V, M, Kproj, seq_len, k, 
 
 def scan(shape: Shape, Kproj, seq_len, workspace, stream=None):
     """Score scan only (after prep)."""
-    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need_kproj(Kproj, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank), bool(shape.flags & SJSA_FLAG_KPROJ_FP8))
     _need(seq_len, "seq_len", torch.int32, (shape.batch,))
     _check(lib().sjsa_scan(ctypes.byref(shape), _ptr(Kproj), _ptr(seq_len), _ptr(workspace), workspace.numel(),
                            _stream(stream)))
@@ -277,7 +301,7 @@ def select(shape: Shape, Kproj, seq_len, k, workspace, idx=None, stream=None):
     if idx is None:
         idx = torch.empty((shape.batch, shape.n_kv_heads, int(k)), dtype=torch.int32, device=workspace.device)
     _need(idx, "idx", torch.int32, (shape.batch, shape.n_kv_heads, int(k)))
-    _need(Kproj, "Kproj", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank))
+    _need_kproj(Kproj, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank), bool(shape.flags & SJSA_FLAG_KPROJ_FP8))
     _check(lib().sjsa_select(ctypes.byref(shape), _ptr(Kproj), _ptr(seq_len), int(k), _ptr(idx), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
     return idx
