@@ -208,6 +208,33 @@ def long_batched(seed: int = 3, device="cpu", n_q_sets: int = 1, batch: int = 16
                     name=f"long-batched-b{batch}-n{n}-r32-k4096", n_q_sets=n_q_sets)
 
 
+def gated(batch, n_kv_heads, group, n, unit_size, k_units, *, seed, device="cpu", capacity=None,
+          seq_len=None, name="gated-units") -> Workload:
+    """Gated-logit (SAS-style) decode layer: K, V and q as in rope_gqa, plus one gate
+    score per context unit of unit_size tokens, u ~ N(0,1) fp32, stored as
+    extra["gate_scores"] [B, H_kv, ceil(cap/unit_size)]. seq_len (a list) makes the
+    batch ragged; rows past a sequence's length are zero."""
+    wl = rope_gqa(batch, n_kv_heads, group, n, 16, k_units * unit_size, seed=seed, device=device,
+                  capacity=capacity, name=name)
+    g = _gen(seed + 104729, device)
+    n_u = (wl.capacity + unit_size - 1) // unit_size
+    wl.extra["gate_scores"] = torch.randn(batch, n_kv_heads, n_u, generator=g, device=device)
+    wl.extra["unit_size"] = unit_size
+    wl.extra["k_units"] = k_units
+    wl.M = None
+    if seq_len is not None:
+        wl.seq_len = torch.tensor(seq_len, dtype=torch.int32, device=device)
+        for b, nb in enumerate(seq_len):
+            wl.K[b, :, max(nb, 0):] = 0
+            wl.V[b, :, max(nb, 0):] = 0
+    return wl
+
+
+def gated_config(seed: int = 4, device="cpu") -> Workload:
+    """B=1, 32/8 heads (G=4), d=128, n=32768 in 512 units of 64 tokens, budget 32 units."""
+    return gated(1, 8, 4, 32768, 64, 32, seed=seed, device=device, name="gated-b1-n32768-u64-k32")
+
+
 def new_token(wl: Workload, seed: int, T: int = 1):
     """k_new, v_new [B, H_kv, T, d] bf16 for an append of T tokens."""
     dev = wl.q.device
