@@ -73,6 +73,7 @@ typedef enum sjsa_status {
 /* Largest supported token budget per call, and largest cache capacity. */
 #define SJSA_MAX_K (1 << 20)
 #define SJSA_MAX_CAPACITY ((int64_t)1 << 30)
+#define SJSA_MAX_GATED_UNITS 4096   /* unit budget of sjsa_gated_decode_step */
 
 typedef struct sjsa_shape {
   int32_t batch;      /* B >= 1 */
@@ -205,6 +206,42 @@ int sjsa_topk(const sjsa_shape* shape, const float* scores, int64_t score_stride
  * (host only). */
 size_t sjsa_workspace_scores_offset(const sjsa_shape* shape);
 int64_t sjsa_workspace_score_stride(const sjsa_shape* shape);
+
+/*
+ * Gated-logit sparse decode step. Source: SAS article ("SAS：用门控稀疏注意力把
+ * 上下文排序端到端对齐 LM 损失"), section 2.1 (each unit's gate enters the
+ * attention logits in log form), section 2.2 (b) (normalized softmax gates; the
+ * current block is always kept) and section 2.3 (decode attends only over the
+ * units with the largest gates).
+ * The cache is split into context units of unit_size consecutive positions; unit
+ * i covers [i*unit_size, (i+1)*unit_size). Sequence b has U_b = ceil(n_b/unit_size)
+ * units; the last one, which holds position n_b - 1, is the current unit.
+ *   q [B, H_q, d] bf16; K, V [B, H_kv, cap, d] bf16; seq_len [B] int32
+ *   gate_scores [B, H_kv, gate_stride] fp32: the selector's score u of every unit
+ *     (gate_stride >= ceil(cap/unit_size)); the gates are g = softmax(u) over the
+ *     U_b units of the sequence. Scores should be finite (NaN ranks lowest; the
+ *     output is then unspecified).
+ *   Kept units: every unit when U_b <= k_units, else the current unit plus the
+ *     k_units - 1 other units with the largest scores (equal scores: lower unit).
+ *   idx [B, H_kv, k_units*unit_size]: the kept units' positions below n_b,
+ *     ascending, then -1.
+ *   out [B, H_q, d]: per query head, the softmax over the kept positions j of
+ *     sm_scale * q.k_j + lambda * ln g(unit of j), applied to their V rows
+ *     (bf16, or fp32 with SJSA_FLAG_OUT_F32); zero where n_b = 0.
+ *   shape: rank and SJSA_FLAG_KPROJ_FP8 are ignored (no scoring cache is read).
+ *   1 <= k_units <= SJSA_MAX_GATED_UNITS, unit_size >= 1,
+ *   k_units * unit_size <= SJSA_MAX_K; lambda and sm_scale finite (sm_scale 0
+ *   selects 1/sqrt(d)).
+ * The workspace (caller-owned, sjsa_gated_workspace_size bytes, 256-byte aligned)
+ * holds each position's logit term and the attention partials.
+ * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _K, _WORKSPACE, _ALIGN, _HIP.
+ */
+size_t sjsa_gated_workspace_size(const sjsa_shape* shape, int32_t unit_size, int32_t k_units);
+int sjsa_gated_decode_step(const sjsa_shape* shape, const void* q, const void* K, const void* V,
+                           const float* gate_scores, int64_t gate_stride, const int32_t* seq_len,
+                           int32_t unit_size, int32_t k_units, float lambda, float sm_scale,
+                           void* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Static message for a status code. */
 const char* sjsa_status_string(int status);

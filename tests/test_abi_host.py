@@ -138,3 +138,28 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         sj.decode_step(q, K, K, torch.zeros(1, 1, 64, 16, dtype=torch.bfloat16), M,
                        torch.zeros(1, dtype=torch.int32), 8)
+
+
+def test_gated_validation():
+    L = sj.lib()
+    s = _shape(rank=0)                  # the gated step reads no scoring cache: rank is ignored
+    f = ctypes.c_void_p(FAKE)
+
+    def call(shape=s, unit=64, k_units=32, stride=16, lam=1.0, sm=0.0, ws=1 << 30, gates=f, out=f):
+        return L.sjsa_gated_decode_step(ctypes.byref(shape), f, f, f, gates, stride, f, unit, k_units, lam, sm,
+                                        out, f, f, ws, None)
+
+    assert L.sjsa_gated_workspace_size(ctypes.byref(s), 64, 32) > 0
+    assert L.sjsa_gated_workspace_size(ctypes.byref(s), 64, 0) == 0
+    assert L.sjsa_gated_workspace_size(ctypes.byref(_shape(head_dim=64)), 64, 32) == 0
+    assert call(k_units=0) == -2
+    assert call(k_units=4097) == -2                       # above SJSA_MAX_GATED_UNITS
+    assert call(unit=0) == -2
+    assert call(unit=1 << 12, k_units=512) == -4          # more than SJSA_MAX_K positions
+    assert call(stride=15) == -2                          # ceil(1000 / 64) = 16 units per row
+    assert call(lam=float("inf")) == -2
+    assert call(sm=float("nan")) == -2
+    assert call(ws=1024) == -5
+    assert call(gates=None) == -1
+    assert call(out=ctypes.c_void_p(FAKE + 4)) == -7
+    assert call(shape=_shape(group=3)) == -3

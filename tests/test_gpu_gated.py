@@ -1,0 +1,87 @@
+"""GPU parity of the gated-logit (SAS) decode step against the oracle: the kept
+units' positions exactly, the biased attention output within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import token_level_sparse_kv_amd as sj
+import workloads
+from oracle import jssa, sas
+from tests.gpu_helpers import OUT_TOL_BF16, OUT_TOL_F32, bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, unit, k_units, lam, out_f32=True, tag="", gates=None):
+    u = wl.extra["gate_scores"] if gates is None else gates
+    out, idx = sj.gated_decode_step(wl.q, wl.K, wl.V, u, wl.seq_len, unit, k_units, lam=lam, out_f32=out_f32)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    ix = idx.cpu().numpy()
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    un = u.cpu().numpy()
+    G = wl.group
+    tol = OUT_TOL_F32 if out_f32 else OUT_TOL_BF16
+    scale = jssa.default_sm_scale(128)
+    for b in range(wl.batch):
+        n = min(max(int(wl.seq_len[b]), 0), wl.capacity)
+        for h in range(wl.n_kv_heads):
+            ref_out, ref_idx, _ = sas.gated_decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], un[b, h], n,
+                                                        unit, k_units, lam, scale)
+            assert np.array_equal(ix[b, h], ref_idx), f"{tag} unit ({b},{h}): positions differ"
+            err = np.max(np.abs(o[b, h * G:(h + 1) * G] - ref_out))
+            assert err <= tol, f"{tag} unit ({b},{h}): max |out - oracle| = {err}"
+    return out, idx
+
+
+def test_gated_config_512_units_of_64():
+    say("gated step: B=1, 32/8 heads, n=32768, 512 units of 64, budget 32")
+    wl = workloads.gated_config(device="cuda")
+    for lam, out_f32 in ((1.0, True), (1.0, False), (2.5, True)):
+        _check(wl, 64, 32, lam, out_f32=out_f32, tag=f"config lam={lam}")
+
+
+@pytest.mark.parametrize("G,unit,k_units", [(1, 64, 8), (2, 16, 20), (4, 1, 300), (8, 64, 3)])
+def test_gated_ragged(G, unit, k_units):
+    say(f"gated ragged G={G} unit={unit} k_units={k_units}")
+    seq = [3000, 1, 0, 64 * 9, 2049]
+    wl = workloads.gated(5, 2, G, 3000, unit, k_units, seed=60 + G + unit, device="cuda", capacity=3003,
+                         seq_len=seq)
+    _check(wl, unit, k_units, 1.0, tag=f"ragged G{G} u{unit} k{k_units}")
+
+
+def test_gated_radix_path_many_units_with_ties():
+    # 1500 units per sequence: more than the counting path ranks; integer scores tie often
+    say("gated radix path with ties")
+    wl = workloads.gated(2, 2, 4, 6000, 4, 100, seed=70, device="cuda", seq_len=[6000, 5999])
+    g = torch.randint(-3, 4, wl.extra["gate_scores"].shape, generator=torch.Generator().manual_seed(71))
+    gates = g.float().cuda()
+    _check(wl, 4, 100, 1.0, tag="radix ties", gates=gates)
+    _check(wl, 4, 100, 1.0, tag="radix normal")
+
+
+def test_gated_counting_path_with_ties_and_budget_one():
+    say("gated counting path with ties; budget of one unit")
+    wl = workloads.gated(2, 2, 4, 4000, 8, 40, seed=72, device="cuda", seq_len=[4000, 3333])
+    g = torch.randint(-2, 3, wl.extra["gate_scores"].shape, generator=torch.Generator().manual_seed(73))
+    _check(wl, 8, 40, 1.0, tag="counting ties", gates=g.float().cuda())
+    _check(wl, 8, 1, 1.0, tag="current unit only")
+
+
+def test_gated_lambda_zero_equals_plain_attention_bitwise():
+    say("gated lambda=0 vs attend over the same positions")
+    wl = workloads.gated(2, 2, 4, 5000, 64, 16, seed=74, device="cuda", seq_len=[5000, 4100])
+    out, idx = sj.gated_decode_step(wl.q, wl.K, wl.V, wl.extra["gate_scores"], wl.seq_len, 64, 16, lam=0.0)
+    ref = sj.attend(wl.q, wl.K, wl.V, idx, wl.seq_len, rank=32)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_gated_is_deterministic():
+    say("gated determinism")
+    wl = workloads.gated_config(device="cuda")
+    u = wl.extra["gate_scores"]
+    a = sj.gated_decode_step(wl.q, wl.K, wl.V, u, wl.seq_len, 64, 32)
+    b = sj.gated_decode_step(wl.q, wl.K, wl.V, u, wl.seq_len, 64, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])

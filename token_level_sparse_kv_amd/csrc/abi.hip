@@ -17,12 +17,13 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_shape(const sjsa_shape* s) {
+// with_rank = false: the call reads no scoring cache, so rank is not checked.
+int check_shape(const sjsa_shape* s, bool with_rank = true) {
   if (!s) return SJSA_ERR_NULL;
   if (s->batch < 1 || s->n_kv_heads < 1 || s->capacity < 1 || s->capacity > SJSA_MAX_CAPACITY) return SJSA_ERR_DIMS;
   if ((int64_t)s->batch * s->n_kv_heads > 65535) return SJSA_ERR_DIMS;     // grid.y limit
   if (s->head_dim != HEAD_DIM) return SJSA_ERR_UNSUPPORTED;
-  if (s->rank != 16 && s->rank != 32 && s->rank != 64) return SJSA_ERR_UNSUPPORTED;
+  if (with_rank && s->rank != 16 && s->rank != 32 && s->rank != 64) return SJSA_ERR_UNSUPPORTED;
   if (s->group != 1 && s->group != 2 && s->group != 4 && s->group != 8) return SJSA_ERR_UNSUPPORTED;
   if (s->flags & ~(SJSA_FLAG_OUT_F32 | SJSA_FLAG_WRITE_SCORES | SJSA_FLAG_KPROJ_FP8)) return SJSA_ERR_UNSUPPORTED;
   return SJSA_OK;
@@ -71,9 +72,38 @@ Layout make_layout(const sjsa_shape& s, int k) {
   return L;
 }
 
+Layout make_gated_layout(const sjsa_shape& s, int ktok) {
+  const Layout A = make_layout(s, ktok);      // attention split of a ktok-entry index list
+  Layout L;
+  L.units = A.units;
+  L.nsplit = A.nsplit;
+  L.chunk = A.chunk;
+  size_t off = 0;
+  L.off_bias = off;
+  off = align_up(off + (size_t)L.units * ktok * sizeof(float), WS_ALIGN);
+  L.off_partials = off;
+  const size_t part = L.nsplit > 1 ? (size_t)L.units * L.nsplit * s.group * PART_STRIDE * sizeof(float) : 0;
+  off = align_up(off + part, WS_ALIGN);
+  L.scores_end = L.off_partials;
+  L.total = off;
+  return L;
+}
+
 }  // namespace sjsa
 
 using namespace sjsa;
+
+namespace {
+
+int check_gated(const sjsa_shape* shape, int32_t unit_size, int32_t k_units) {
+  int st = check_shape(shape, false);
+  if (st) return st;
+  if (unit_size < 1 || k_units < 1 || k_units > SJSA_MAX_GATED_UNITS) return SJSA_ERR_DIMS;
+  if ((int64_t)unit_size * k_units > SJSA_MAX_K) return SJSA_ERR_K;
+  return SJSA_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -307,6 +337,37 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
                       resolve_scale(sm_scale), out, ws, s);
+  return status_of(e);
+}
+
+size_t sjsa_gated_workspace_size(const sjsa_shape* shape, int32_t unit_size, int32_t k_units) {
+  if (check_gated(shape, unit_size, k_units) != SJSA_OK) return 0;
+  return make_gated_layout(*shape, unit_size * k_units).total;
+}
+
+int sjsa_gated_decode_step(const sjsa_shape* shape, const void* q, const void* K, const void* V,
+                           const float* gate_scores, int64_t gate_stride, const int32_t* seq_len,
+                           int32_t unit_size, int32_t k_units, float lambda, float sm_scale, void* out,
+                           int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gated(shape, unit_size, k_units);
+  if (st) return st;
+  if (!q || !K || !V || !gate_scores || !seq_len || !out || !idx || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(gate_scores, 4) ||
+      !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(out, 16) || !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  if (gate_stride < (shape->capacity + unit_size - 1) / unit_size) return SJSA_ERR_DIMS;
+  if (!isfinite(sm_scale) || !isfinite(lambda)) return SJSA_ERR_DIMS;
+  const int ktok = unit_size * k_units;
+  const Layout L = make_gated_layout(*shape, ktok);
+  if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  float* bias = reinterpret_cast<float*>(ws + L.off_bias);
+  hipError_t e = launch_gate_select(*shape, gate_scores, gate_stride, seq_len, unit_size, k_units, lambda, idx,
+                                    bias, s);
+  if (e == hipSuccess)
+    e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, ktok, seq_len,
+                      resolve_scale(sm_scale), out, ws, s, bias);
   return status_of(e);
 }
 

@@ -32,13 +32,16 @@ constexpr int ATT_U = 4;             // rows in flight per slot
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.f;  // log2 units a logit may exceed the softmax reference by
 
-template <int G, int U>
+// BIAS: every index entry carries an additive exp2-domain logit term (bias, laid out
+// like idx), as the gated-logit variant needs.
+template <int G, int U, bool BIAS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ seq_len, int n_kv_heads, int64_t cap,
-    int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
+    const int32_t* __restrict__ idx, const float* __restrict__ bias, const int32_t* __restrict__ seq_len,
+    int n_kv_heads, int64_t cap, int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
     void* __restrict__ out, int out_f32) {
   __shared__ int32_t sidx[1024];
+  __shared__ float sbias[BIAS ? 1024 : 1];
   __shared__ uint32_t sq2[G][HEAD_DIM / 2];     // query heads as packed bf16 pairs
   __shared__ float sm_m[SLOTS][G];
   __shared__ float sm_l[SLOTS][G];
@@ -55,6 +58,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   const int first = split * chunk;
   const int cnt = max(0, min(chunk, k - first));
   const int32_t* ids = idx + (size_t)unit * k + first;
+  const float* bss = BIAS ? bias + (size_t)unit * k + first : nullptr;
   const uint16_t* Kb = K + (size_t)unit * cap * HEAD_DIM + t * 8;
   const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + t * 8;
 
@@ -72,12 +76,19 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   // the slot's first batch of rows is requested straight from the index list, before
   // the workgroup stages the list and the queries in LDS
   int32_t j0[U];
+  float b0[U];
   u32x4 kw0[U], vw0[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) j0[u] = slot * U + u < cnt ? ids[slot * U + u] : -1;
+  for (int u = 0; u < U; ++u) {
+    j0[u] = slot * U + u < cnt ? ids[slot * U + u] : -1;
+    b0[u] = (BIAS && slot * U + u < cnt) ? bss[slot * U + u] : 0.f;
+  }
   load_rows(j0, kw0, vw0);
 
-  for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
+  for (int i = tid; i < cnt; i += ATT_THREADS) {
+    sidx[i] = ids[i];
+    if constexpr (BIAS) sbias[i] = bss[i];
+  }
   // query heads kept in LDS as bf16 pairs (read per use: fewer registers, more
   // waves in flight); the exp2-domain scale is applied to each finished dot
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(q + (size_t)unit * G * HEAD_DIM);
@@ -92,7 +103,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   }
   __syncthreads();
 
-  auto consume = [&](const int32_t (&j)[U], const u32x4 (&kw)[U], const u32x4 (&vw)[U]) {
+  auto consume = [&](const int32_t (&j)[U], const float (&bj)[U], const u32x4 (&kw)[U], const u32x4 (&vw)[U]) {
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) ok[u] = j[u] >= 0 && (int64_t)j[u] < n;
@@ -111,7 +122,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         a = dot2_bf16(qv.z, kw[u].z, a);
         a = dot2_bf16(qv.w, kw[u].w, a);
         a = row16_sum(a);
-        z[u][g] = ok[u] ? a * qscale : -INFINITY;
+        z[u][g] = ok[u] ? (BIAS ? fmaf(a, qscale, bj[u]) : a * qscale) : -INFINITY;
       }
     }
     // online softmax with a lazy reference: the running reference m only moves (and
@@ -152,14 +163,18 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     }
   };
 
-  if (slot * U < cnt) consume(j0, kw0, vw0);
+  if (slot * U < cnt) consume(j0, b0, kw0, vw0);
   for (int base = slot * U + SLOTS * U; base < cnt; base += SLOTS * U) {
     int32_t j[U];
+    float bj[U];
     u32x4 kw[U], vw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) j[u] = base + u < cnt ? sidx[base + u] : -1;
+    for (int u = 0; u < U; ++u) {
+      j[u] = base + u < cnt ? sidx[base + u] : -1;
+      bj[u] = (BIAS && base + u < cnt) ? sbias[base + u] : 0.f;
+    }
     load_rows(j, kw, vw);
-    consume(j, kw, vw);
+    consume(j, bj, kw, vw);
   }
 
   // ---- combine the 16 slots of this workgroup
@@ -246,14 +261,20 @@ __global__ __launch_bounds__(HEAD_DIM) void merge_kernel(const float* __restrict
 
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
-                         float sm_scale, void* out, unsigned char* ws, hipStream_t st) {
+                         float sm_scale, void* out, unsigned char* ws, hipStream_t st, const float* bias) {
   float* partials = reinterpret_cast<float*>(ws + L.off_partials);
   const float qscale = sm_scale * LOG2E;
   const int out_f32 = (s.flags & SJSA_FLAG_OUT_F32) ? 1 : 0;
   const dim3 grid((unsigned)L.nsplit, (unsigned)L.units), block(ATT_THREADS);
-#define SJSA_ATT(GG)                                                                              \
-  attend_kernel<GG, ATT_U><<<grid, block, 0, st>>>(q, K, V, idx, seq_len, s.n_kv_heads, s.capacity, k,   \
-                                            L.chunk, L.nsplit, qscale, partials, out, out_f32);   \
+#define SJSA_ATT(GG)                                                                                        \
+  if (bias)                                                                                                 \
+    attend_kernel<GG, ATT_U, true><<<grid, block, 0, st>>>(q, K, V, idx, bias, seq_len, s.n_kv_heads,         \
+                                                           s.capacity, k, L.chunk, L.nsplit, qscale, partials, \
+                                                           out, out_f32);                                      \
+  else                                                                                                      \
+    attend_kernel<GG, ATT_U, false><<<grid, block, 0, st>>>(q, K, V, idx, nullptr, seq_len, s.n_kv_heads,     \
+                                                            s.capacity, k, L.chunk, L.nsplit, qscale, partials,\
+                                                            out, out_f32);                                     \
   if (L.nsplit > 1) merge_kernel<GG><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32)
   switch (s.group) {
     case 1: SJSA_ATT(1); break;

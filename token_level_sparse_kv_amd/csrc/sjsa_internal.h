@@ -38,10 +38,13 @@ struct Layout {
   int64_t ntile_cap = 0;      // scan tiles per unit (capacity / TILE_ROWS, rounded up)
   int64_t cand_stride = 0;    // 4-byte candidate entries per unit (capacity rounded up to TILE_ROWS)
   size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
+  size_t off_bias = 0;        // gated step: per-position logit terms
   size_t scores_end = 0, total = 0;
 };
 
 Layout make_layout(const sjsa_shape& s, int k);
+// Workspace of the gated step: logit terms [units, ktok] fp32, then attention partials.
+Layout make_gated_layout(const sjsa_shape& s, int ktok);
 
 // Kernel launchers (device pointers; host-validated arguments).
 hipError_t launch_append(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
@@ -67,8 +70,14 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj,
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
                          const void* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
                          hipStream_t st);
+// bias != nullptr: one exp2-domain logit term per index entry, laid out like idx.
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
-                         float sm_scale, void* out, unsigned char* ws, hipStream_t st);
+                         float sm_scale, void* out, unsigned char* ws, hipStream_t st,
+                         const float* bias = nullptr);
+// Gated-logit unit selection: idx and bias [B * H_kv, k_units * unit_size].
+hipError_t launch_gate_select(const sjsa_shape& s, const float* gate_scores, int64_t gate_stride,
+                              const int32_t* seq_len, int unit_size, int k_units, float lambda, int32_t* idx,
+                              float* bias, hipStream_t st);
 
 }  // namespace sjsa

@@ -63,6 +63,10 @@ _SIGS = {
                                    _P, _P, ctypes.c_size_t, _P]),
     "sjsa_topk": (ctypes.c_int, [ctypes.POINTER(Shape), _P, ctypes.c_int64, _P, ctypes.c_int32, _P, _P,
                                  ctypes.c_size_t, _P]),
+    "sjsa_gated_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
+    "sjsa_gated_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int64, _P,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                              _P, _P, _P, ctypes.c_size_t, _P]),
     "sjsa_workspace_scores_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "sjsa_workspace_score_stride": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "sjsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -345,3 +349,50 @@ def attend(q, K, V, idx, seq_len, sm_scale=0.0, out=None, workspace=None, out_f3
 
 def default_sm_scale(head_dim: int = 128) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+def gated_shape(q: torch.Tensor, K: torch.Tensor, out_f32=False) -> Shape:
+    B, Hkv, cap, d = K.shape
+    Hq = q.shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    return make_shape(B, Hkv, Hq // Hkv, d, 0, cap, out_f32)
+
+
+def gated_workspace(shape: Shape, unit_size: int, k_units: int, device=None) -> torch.Tensor:
+    n = lib().sjsa_gated_workspace_size(ctypes.byref(shape), int(unit_size), int(k_units))
+    if n == 0:
+        raise SjsaError(-2, "invalid shape, unit size or unit budget for the gated step")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def gated_decode_step(q, K, V, gate_scores, seq_len, unit_size, k_units, lam=1.0, sm_scale=0.0, out=None,
+                      idx=None, workspace=None, out_f32=False, stream=None):
+    """Gated-logit sparse decode step over context units of unit_size tokens: the
+    current unit plus the k_units - 1 units with the largest gates, attention logits
+    biased by lam * ln g. gate_scores [B, H_kv, >= ceil(cap/unit_size)] fp32 (the
+    gates are their softmax over each sequence's units). Returns (out [B, H_q, d],
+    idx [B, H_kv, k_units * unit_size])."""
+    B, Hkv, cap, d = K.shape
+    _need(q, "q", torch.bfloat16, (B, q.shape[1], d))
+    _need(K, "K", torch.bfloat16, (B, Hkv, cap, d))
+    _need(V, "V", torch.bfloat16, (B, Hkv, cap, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    if gate_scores.dim() != 3 or tuple(gate_scores.shape[:2]) != (B, Hkv):
+        raise ValueError("gate_scores must be [B, H_kv, units]")
+    _need(gate_scores, "gate_scores", torch.float32)
+    shape = gated_shape(q, K, out_f32)
+    ktok = int(unit_size) * int(k_units)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hkv, ktok), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, q.shape)
+    _need(idx, "idx", torch.int32, (B, Hkv, ktok))
+    if workspace is None:
+        workspace = gated_workspace(shape, unit_size, k_units, q.device)
+    _check(lib().sjsa_gated_decode_step(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(gate_scores),
+                                        int(gate_scores.shape[2]), _ptr(seq_len), int(unit_size), int(k_units),
+                                        float(lam), float(sm_scale), _ptr(out), _ptr(idx), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
+    return out, idx
