@@ -137,6 +137,48 @@ def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, 
             "hbm_frac_of_peak": round(gbs / peak, 4)}
 
 
+GATED_WORKLOAD = ("gated-logit decode step: batch 1, 32 query / 8 KV heads (G=4), d=128, n=32768 in 512 units of "
+                  "64 tokens, budget 32 units (current unit kept), lambda=1; gate scores ~ N(0,1); 4 input sets "
+                  "rotated so the K/V rows are not cache resident")
+
+
+def gated_variant(sj, workloads, steps, warmup, peak):
+    """The gated-logit (unit-gated) step at its own workload, timed back to back over
+    4 rotating input sets (together larger than the last-level cache)."""
+    import torch
+    sets = [workloads.gated_config(seed=4 + i, device="cuda") for i in range(4)]
+    wl = sets[0]
+    unit, k_units = wl.extra["unit_size"], wl.extra["k_units"]
+    shape = sj.gated_shape(wl.q, wl.K)
+    ws = sj.gated_workspace(shape, unit, k_units)
+    out = torch.empty_like(wl.q)
+    idx = torch.empty(wl.batch, wl.n_kv_heads, unit * k_units, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        w = sets[i % len(sets)]
+        sj.gated_decode_step(w.q, w.K, w.V, w.extra["gate_scores"], w.seq_len, unit, k_units, lam=1.0, out=out,
+                             idx=idx, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    units = wl.batch * wl.n_kv_heads
+    ktok = unit * k_units
+    kv = units * ktok * wl.head_dim * 2 * 2
+    nbytes = (kv + units * (wl.capacity // unit) * 4 + 2 * wl.q.numel() * 2 + units * ktok * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": GATED_WORKLOAD, "value": round(1000.0 / ms, 2), "unit": "steps/s",
+            "us_per_step": round(ms * 1000.0, 2), "algorithmic_bytes_per_step": nbytes, "kv_row_bytes": kv,
+            "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +188,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-fp8-variant", action="store_true", help="skip the FP8 scoring-cache measurement")
+    ap.add_argument("--no-gated-variant", action="store_true", help="skip the gated-logit step measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -264,6 +307,8 @@ def main():
     }
 
     print(f"timed: {ms_per_step * 1000:.1f} us/step, stages (us) {line['stage_us']}", file=sys.stderr, flush=True)
+    if not args.no_gated_variant:
+        line["gated_variant"] = gated_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS)
     if not args.no_fp8_variant:
         line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, args.steps,
                                                 args.warmup, step_bytes, MI355X_HBM_PEAK_GBS)

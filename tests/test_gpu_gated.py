@@ -50,9 +50,9 @@ def test_gated_ragged(G, unit, k_units):
     _check(wl, unit, k_units, 1.0, tag=f"ragged G{G} u{unit} k{k_units}")
 
 
-def test_gated_radix_path_many_units_with_ties():
-    # 1500 units per sequence: more than the counting path ranks; integer scores tie often
-    say("gated radix path with ties")
+def test_gated_many_units_with_ties():
+    # 1500 units per sequence; integer scores tie often, so the boundary key is shared
+    say("gated 1500 units with ties")
     wl = workloads.gated(2, 2, 4, 6000, 4, 100, seed=70, device="cuda", seq_len=[6000, 5999])
     g = torch.randint(-3, 4, wl.extra["gate_scores"].shape, generator=torch.Generator().manual_seed(71))
     gates = g.float().cuda()
@@ -60,11 +60,20 @@ def test_gated_radix_path_many_units_with_ties():
     _check(wl, 4, 100, 1.0, tag="radix normal")
 
 
-def test_gated_counting_path_with_ties_and_budget_one():
-    say("gated counting path with ties; budget of one unit")
+def test_gated_scores_read_from_global():
+    # 10000 single-token units: more scores than the kernel stages in LDS
+    say("gated 10000 units, scores read from global memory")
+    wl = workloads.gated(1, 2, 4, 10000, 1, 500, seed=75, device="cuda", seq_len=[9999])
+    _check(wl, 1, 500, 1.0, tag="unstaged")
+    g = torch.randint(-2, 3, wl.extra["gate_scores"].shape, generator=torch.Generator().manual_seed(76))
+    _check(wl, 1, 500, 1.0, tag="unstaged ties", gates=g.float().cuda())
+
+
+def test_gated_ties_and_budget_one():
+    say("gated ties; budget of one unit")
     wl = workloads.gated(2, 2, 4, 4000, 8, 40, seed=72, device="cuda", seq_len=[4000, 3333])
     g = torch.randint(-2, 3, wl.extra["gate_scores"].shape, generator=torch.Generator().manual_seed(73))
-    _check(wl, 8, 40, 1.0, tag="counting ties", gates=g.float().cuda())
+    _check(wl, 8, 40, 1.0, tag="ties", gates=g.float().cuda())
     _check(wl, 8, 1, 1.0, tag="current unit only")
 
 

@@ -284,8 +284,8 @@ int sjsa_attend(const sjsa_shape* shape, const void* q, const void* K, const voi
   if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
-                      resolve_scale(sm_scale), out, ws, s);
+  const hipError_t e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k,
+                                     seq_len, resolve_scale(sm_scale), out, ws, s);
   return status_of(e);
 }
 

@@ -221,10 +221,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
 // l_s and the unnormalized output acc_s; the merge keeps a running (m, l, acc)
 // and rescales by 2^(m_old - m_new) as each partial comes in (log-sum-exp merge),
 // then out = acc / l.
-template <int G>
+template <int G, int MU>
 __global__ __launch_bounds__(HEAD_DIM) void merge_kernel(const float* __restrict__ partials, int nsplit,
                                                          void* __restrict__ out, int out_f32) {
-  constexpr int MU = 8;
   const int unit = blockIdx.x / G;
   const int g = blockIdx.x - unit * G;
   const int dim = threadIdx.x;
@@ -275,7 +274,10 @@ hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q
     attend_kernel<GG, ATT_U, false><<<grid, block, 0, st>>>(q, K, V, idx, nullptr, seq_len, s.n_kv_heads,     \
                                                             s.capacity, k, L.chunk, L.nsplit, qscale, partials,\
                                                             out, out_f32);                                     \
-  if (L.nsplit > 1) merge_kernel<GG><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32)
+  if (L.nsplit > 8)                                                                                         \
+    merge_kernel<GG, 32><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32); \
+  else if (L.nsplit > 1)                                                                                    \
+    merge_kernel<GG, 8><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32)
   switch (s.group) {
     case 1: SJSA_ATT(1); break;
     case 2: SJSA_ATT(2); break;
