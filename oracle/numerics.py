@@ -97,3 +97,49 @@ def round_to_fp8e4m3(x) -> np.ndarray:
     code = np.where(sub, code_s, code_n) | sign
     code = np.where(nan, 0x7F, code)
     return code.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------- fp16
+# IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits;
+# largest finite 65504, smallest subnormal 2^-24.
+FP16_MAX = 65504.0
+FP16_MIN_QUANTUM_EXP = -24
+
+
+def fp16_to_f32(bits) -> np.ndarray:
+    """Exact decoding of binary16 bit patterns (uint16) to fp32, from the format
+    definition: (-1)^s * 2^(e-15) * 1.f for normals, 2^-14 * 0.f for subnormals."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b & 0x8000, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(f, -24), np.ldexp(1024.0 + f, e - 25))
+    val = np.where(e == 31, np.where(f == 0, np.inf, np.nan), val)
+    return (sign * val).astype(np.float32)
+
+
+def round_to_fp16(x) -> np.ndarray:
+    """Round real values to binary16 in one step, ties to even; values that round
+    above 65504 become infinity (IEEE overflow). Returns uint16 bit patterns.
+    Same method as round_to_bf16 with 11 significant bits and quantum >= 2^-24."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    qexp = np.maximum(e - 11, FP16_MIN_QUANTUM_EXP)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.ldexp(np.rint(np.ldexp(x, -qexp)), qexp)
+    nan = np.isnan(x)
+    r = np.where(nan, 0.0, r)
+    mag = np.abs(r)
+    exp_field = np.zeros(r.shape, dtype=np.int64)
+    frac = np.zeros(r.shape, dtype=np.int64)
+    normal = mag >= 2.0 ** -14
+    _, re = np.frexp(np.where(normal, mag, 1.0))
+    exp_field = np.where(normal, re - 1 + 15, 0)
+    frac = np.where(normal, np.rint(np.ldexp(np.where(normal, mag, 0.0), -(re - 1) + 10)) - 1024,
+                    np.rint(np.ldexp(mag, 24)))
+    over = mag > FP16_MAX
+    bits = (exp_field << 10) | frac.astype(np.int64)
+    bits = np.where(over, 0x7C00, bits)
+    bits = bits | (np.signbit(x).astype(np.int64) << 15)
+    bits = np.where(nan, 0x7E00, bits)
+    return bits.astype(np.uint16)
