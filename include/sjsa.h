@@ -73,7 +73,8 @@ typedef enum sjsa_status {
 /* Largest supported token budget per call, and largest cache capacity. */
 #define SJSA_MAX_K (1 << 20)
 #define SJSA_MAX_CAPACITY ((int64_t)1 << 30)
-#define SJSA_MAX_GATED_UNITS 4096   /* unit budget of sjsa_gated_decode_step */
+#define SJSA_MAX_SELECT_UNITS 4096   /* unit (block) budget of the gated and block-sparse steps */
+#define SJSA_MAX_BLOCK_SIZE 4096     /* positions per key block of the block-sparse step */
 
 typedef struct sjsa_shape {
   int32_t batch;      /* B >= 1 */
@@ -229,7 +230,7 @@ int64_t sjsa_workspace_score_stride(const sjsa_shape* shape);
  *     sm_scale * q.k_j + lambda * ln g(unit of j), applied to their V rows
  *     (bf16, or fp32 with SJSA_FLAG_OUT_F32); zero where n_b = 0.
  *   shape: rank and SJSA_FLAG_KPROJ_FP8 are ignored (no scoring cache is read).
- *   1 <= k_units <= SJSA_MAX_GATED_UNITS, unit_size >= 1,
+ *   1 <= k_units <= SJSA_MAX_SELECT_UNITS, unit_size >= 1,
  *   k_units * unit_size <= SJSA_MAX_K; lambda and sm_scale finite (sm_scale 0
  *   selects 1/sqrt(d)).
  * The workspace (caller-owned, sjsa_gated_workspace_size bytes, 256-byte aligned)
@@ -242,6 +243,64 @@ int sjsa_gated_decode_step(const sjsa_shape* shape, const void* q, const void* K
                            int32_t unit_size, int32_t k_units, float lambda, float sm_scale,
                            void* out, int32_t* idx, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * Block-sparse decode: block keys, selection of whole key blocks, attention over
+ * the kept blocks. Sources: the NSA tutorial page ("稀疏注意力:每个 query 只挑一部分
+ * 历史去读"): a block's summary key exists once the block is complete; a block's
+ * score is the softmax of q . key / sqrt(head_size) over the visible blocks, summed
+ * over the query heads sharing the K/V head, which select together; the current
+ * block, the first block and the local blocks are always selected. The
+ * SpotAttention abstract page ("SpotAttention: Plug-In Block-Sparse Routing for
+ * Pretrained Long-Context Transformers"): the selector's key cache may be INT4.
+ * Block j of a sequence covers positions [j*bs, (j+1)*bs); it is complete once
+ * n_b >= (j+1)*bs. Block keys are parameter-free: the mean of the block's keys
+ * (fp32 sum in position order, divided by bs, rounded to bf16).
+ *   Kc [B, H_kv, floor(cap/bs), d] bf16 block keys, and/or the INT4 form:
+ *   Kq [B, H_kv, floor(cap/bs), d/2] uint8 (two 4-bit two's-complement codes per
+ *   byte, element 2i in the low nibble) with Ks [B, H_kv, floor(cap/bs), d/64] fp16
+ *   scales: per group of 64 elements, scale = fp16(absmax / 7) (saturating at 65504)
+ *   and code = clamp(rint(x / scale), -7, 7) (0 when the scale is 0), x the bf16 key.
+ *   1 <= bs <= SJSA_MAX_BLOCK_SIZE; rank and the Kproj flag of shape are ignored.
+ */
+
+/* Keys of every complete block of each sequence (n_b = seq_len[b]). Kc, or Kq with
+ * Ks, or all three. Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _ALIGN, _HIP. */
+int sjsa_block_keys(const sjsa_shape* shape, int32_t block_size, const void* K, const int32_t* seq_len,
+                    void* Kc, void* Kq, void* Ks, void* stream);
+
+/* Append n_new tokens per (b, h) at slots pos[b] .. pos[b]+n_new-1 (K and V rows as
+ * in sjsa_append_kv, slots outside [0, cap) skipped), then write the keys of the
+ * blocks these rows complete (reading the blocks' earlier rows from K).
+ * Errors: as sjsa_block_keys, and _DIMS for n_new < 1. */
+int sjsa_block_append(const sjsa_shape* shape, int32_t block_size, const void* k_new, const void* v_new,
+                      int32_t n_new, const int32_t* pos, void* K, void* V, void* Kc, void* Kq, void* Ks,
+                      void* stream);
+
+/* Workspace bytes of sjsa_block_decode_step; 0 if the arguments are invalid. */
+size_t sjsa_block_workspace_size(const sjsa_shape* shape, int32_t block_size, int32_t k_blocks);
+
+/*
+ * One block-sparse decode step. Scores the complete blocks with the bf16 keys Kc
+ * (or, when Kc is NULL, with the INT4 keys Kq, Ks), keeps the forced blocks (the
+ * first n_init blocks, and the n_local blocks ending with the current block, the
+ * one holding position n_b - 1) and the highest-scoring other complete blocks
+ * until k_blocks are kept (equal scores: lower block; every block when a sequence
+ * has at most k_blocks), then runs exact softmax attention of every query head
+ * over the kept blocks' positions, K and V read in place.
+ *   q [B, H_q, d] bf16; K, V [B, H_kv, cap, d] bf16; seq_len [B] int32
+ *   idx [B, H_kv, k_blocks*bs]: kept positions below n_b, ascending, then -1
+ *   out [B, H_q, d] (bf16, or fp32 with SJSA_FLAG_OUT_F32); zero where n_b = 0
+ *   sm_scale scales both the block logits and the attention (0 selects 1/sqrt(d))
+ *   1 <= k_blocks <= SJSA_MAX_SELECT_UNITS, k_blocks*bs <= SJSA_MAX_K,
+ *   n_init, n_local >= 0 with n_init + n_local <= k_blocks.
+ * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _K, _WORKSPACE, _ALIGN, _HIP.
+ */
+int sjsa_block_decode_step(const sjsa_shape* shape, int32_t block_size, const void* q, const void* K,
+                           const void* V, const void* Kc, const void* Kq, const void* Ks,
+                           const int32_t* seq_len, int32_t k_blocks, int32_t n_init, int32_t n_local,
+                           float sm_scale, void* out, int32_t* idx, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Static message for a status code. */
 const char* sjsa_status_string(int status);

@@ -70,7 +70,8 @@ def block_keys(K_bits: np.ndarray, n: int, block: int) -> np.ndarray:
     if m == 0:
         return np.zeros((0, K_bits.shape[1]), dtype=np.uint16)
     k = bf16_to_f32(K_bits[:m * block]).astype(np.float64).reshape(m, block, -1)
-    return round_to_bf16(k.sum(axis=1) / block)       # fp64 sum of 64 bf16 values is exact
+    # the fp64 sum is exact while the block mixes magnitudes less than 2^44 apart
+    return round_to_bf16(k.sum(axis=1) / block)
 
 
 def int4_quantize(kc_bits: np.ndarray):
@@ -141,6 +142,7 @@ def select_blocks(s: np.ndarray, n: int, block: int, k_blocks: int, n_init: int,
     """Kept blocks, ascending: the forced ones, then complete blocks by descending
     score (ties: lower block) until k_blocks are kept; all blocks if there are at
     most k_blocks."""
+    assert n_init + n_local <= k_blocks, "the forced blocks must fit the budget"
     nb = total_blocks(n, block)
     if nb <= k_blocks:
         return np.arange(nb, dtype=np.int64)

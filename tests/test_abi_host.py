@@ -153,7 +153,7 @@ def test_gated_validation():
     assert L.sjsa_gated_workspace_size(ctypes.byref(s), 64, 0) == 0
     assert L.sjsa_gated_workspace_size(ctypes.byref(_shape(head_dim=64)), 64, 32) == 0
     assert call(k_units=0) == -2
-    assert call(k_units=4097) == -2                       # above SJSA_MAX_GATED_UNITS
+    assert call(k_units=4097) == -2                       # above SJSA_MAX_SELECT_UNITS
     assert call(unit=0) == -2
     assert call(unit=1 << 12, k_units=512) == -4          # more than SJSA_MAX_K positions
     assert call(stride=15) == -2                          # ceil(1000 / 64) = 16 units per row
@@ -163,3 +163,33 @@ def test_gated_validation():
     assert call(gates=None) == -1
     assert call(out=ctypes.c_void_p(FAKE + 4)) == -7
     assert call(shape=_shape(group=3)) == -3
+
+
+def test_block_validation():
+    L = sj.lib()
+    s = _shape(rank=0)
+    f = ctypes.c_void_p(FAKE)
+
+    def step(shape=s, bs=64, kb=16, n_init=1, n_local=2, sm=0.0, ws=1 << 30, Kc=f, Kq=None, Ks=None, out=f):
+        return L.sjsa_block_decode_step(ctypes.byref(shape), bs, f, f, f, Kc, Kq, Ks, f, kb, n_init, n_local, sm, out,
+                                        f, f, ws, None)
+
+    assert L.sjsa_block_workspace_size(ctypes.byref(s), 64, 16) > 0
+    assert L.sjsa_block_workspace_size(ctypes.byref(s), 0, 16) == 0
+    assert L.sjsa_block_workspace_size(ctypes.byref(s), 64, 0) == 0
+    assert step(bs=0) == -2 and step(bs=4097) == -2
+    assert step(kb=0) == -2 and step(kb=4097) == -2
+    assert step(bs=4096, kb=257) == -4                   # more than SJSA_MAX_K positions
+    assert step(n_init=-1) == -2 and step(n_local=-1) == -2
+    assert step(kb=4, n_init=2, n_local=3) == -2         # forced blocks beyond the budget
+    assert step(Kc=None) == -1                           # neither bf16 keys nor the INT4 pair
+    assert step(Kc=None, Kq=f) == -1
+    assert step(Kc=None, Kq=f, Ks=ctypes.c_void_p(FAKE + 1)) == -7
+    assert step(sm=float("inf")) == -2
+    assert step(ws=1024) == -5
+    assert step(out=ctypes.c_void_p(FAKE + 8)) == -7
+    assert step(shape=_shape(head_dim=96)) == -3
+    assert L.sjsa_block_keys(ctypes.byref(s), 64, f, f, None, f, None, None) == -1     # Kq without Ks
+    assert L.sjsa_block_keys(ctypes.byref(s), 64, f, None, f, None, None, None) == -1  # no seq_len
+    assert L.sjsa_block_append(ctypes.byref(s), 64, f, f, 0, f, f, f, f, None, None, None) == -2
+    assert L.sjsa_block_append(ctypes.byref(s), 64, f, f, 1, None, f, f, f, None, None, None) == -1

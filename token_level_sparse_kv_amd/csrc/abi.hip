@@ -89,16 +89,47 @@ Layout make_gated_layout(const sjsa_shape& s, int ktok) {
   return L;
 }
 
+BlockLayout make_block_layout(const sjsa_shape& s, int block_size, int k_blocks) {
+  BlockLayout B;
+  const int ktok = block_size * k_blocks;
+  const Layout A = make_layout(s, ktok);
+  B.nblk_cap = s.capacity / block_size;
+  B.zstride = (int64_t)align_up((size_t)B.nblk_cap, 64);
+  B.ntile = (int)((B.nblk_cap + 63) / 64);
+  const size_t units = (size_t)A.units;
+  size_t off = 0;
+  B.off_z = off;
+  off = align_up(off + units * s.group * B.zstride * sizeof(float), WS_ALIGN);
+  B.off_ms = off;
+  off = align_up(off + units * B.ntile * s.group * 2 * sizeof(float), WS_ALIGN);
+  B.att.units = A.units;
+  B.att.nsplit = A.nsplit;
+  B.att.chunk = A.chunk;
+  B.att.off_partials = off;
+  const size_t part = A.nsplit > 1 ? units * A.nsplit * s.group * PART_STRIDE * sizeof(float) : 0;
+  off = align_up(off + part, WS_ALIGN);
+  B.att.total = off;
+  B.total = off;
+  return B;
+}
+
 }  // namespace sjsa
 
 using namespace sjsa;
 
 namespace {
 
+int check_blocks(const sjsa_shape* shape, int32_t block_size) {
+  int st = check_shape(shape, false);
+  if (st) return st;
+  if (block_size < 1 || block_size > SJSA_MAX_BLOCK_SIZE) return SJSA_ERR_DIMS;
+  return SJSA_OK;
+}
+
 int check_gated(const sjsa_shape* shape, int32_t unit_size, int32_t k_units) {
   int st = check_shape(shape, false);
   if (st) return st;
-  if (unit_size < 1 || k_units < 1 || k_units > SJSA_MAX_GATED_UNITS) return SJSA_ERR_DIMS;
+  if (unit_size < 1 || k_units < 1 || k_units > SJSA_MAX_SELECT_UNITS) return SJSA_ERR_DIMS;
   if ((int64_t)unit_size * k_units > SJSA_MAX_K) return SJSA_ERR_K;
   return SJSA_OK;
 }
@@ -368,6 +399,72 @@ int sjsa_gated_decode_step(const sjsa_shape* shape, const void* q, const void* K
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, ktok, seq_len,
                       resolve_scale(sm_scale), out, ws, s, bias);
+  return status_of(e);
+}
+
+int sjsa_block_keys(const sjsa_shape* shape, int32_t block_size, const void* K, const int32_t* seq_len, void* Kc,
+                    void* Kq, void* Ks, void* stream) {
+  int st = check_blocks(shape, block_size);
+  if (st) return st;
+  if (!K || !seq_len || (!Kc && !(Kq && Ks)) || (!Kq != !Ks)) return SJSA_ERR_NULL;
+  if (!aligned(K, 16) || !aligned(seq_len, 4) || !aligned(Kc, 16) || !aligned(Kq, 4) || !aligned(Ks, 2))
+    return SJSA_ERR_ALIGN;
+  return status_of(launch_block_keys(*shape, block_size, (const uint16_t*)K, seq_len, nullptr, 0, (uint16_t*)Kc,
+                                     (unsigned char*)Kq, (uint16_t*)Ks, (hipStream_t)stream));
+}
+
+int sjsa_block_append(const sjsa_shape* shape, int32_t block_size, const void* k_new, const void* v_new,
+                      int32_t n_new, const int32_t* pos, void* K, void* V, void* Kc, void* Kq, void* Ks,
+                      void* stream) {
+  int st = check_blocks(shape, block_size);
+  if (st) return st;
+  if (!k_new || !v_new || !pos || !K || !V || (!Kc && !(Kq && Ks)) || (!Kq != !Ks)) return SJSA_ERR_NULL;
+  if (n_new < 1) return SJSA_ERR_DIMS;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(pos, 4) ||
+      !aligned(Kc, 16) || !aligned(Kq, 4) || !aligned(Ks, 2))
+    return SJSA_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_kv_rows(*shape, (const uint16_t*)k_new, (const uint16_t*)v_new, n_new, pos, (uint16_t*)K,
+                                (uint16_t*)V, s);
+  if (e == hipSuccess)
+    e = launch_block_keys(*shape, block_size, (const uint16_t*)K, nullptr, pos, n_new, (uint16_t*)Kc,
+                          (unsigned char*)Kq, (uint16_t*)Ks, s);
+  return status_of(e);
+}
+
+size_t sjsa_block_workspace_size(const sjsa_shape* shape, int32_t block_size, int32_t k_blocks) {
+  if (check_blocks(shape, block_size) != SJSA_OK) return 0;
+  if (k_blocks < 1 || k_blocks > SJSA_MAX_SELECT_UNITS || (int64_t)k_blocks * block_size > SJSA_MAX_K) return 0;
+  return make_block_layout(*shape, block_size, k_blocks).total;
+}
+
+int sjsa_block_decode_step(const sjsa_shape* shape, int32_t block_size, const void* q, const void* K, const void* V,
+                           const void* Kc, const void* Kq, const void* Ks, const int32_t* seq_len, int32_t k_blocks,
+                           int32_t n_init, int32_t n_local, float sm_scale, void* out, int32_t* idx,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_blocks(shape, block_size);
+  if (st) return st;
+  if (k_blocks < 1 || k_blocks > SJSA_MAX_SELECT_UNITS) return SJSA_ERR_DIMS;
+  if ((int64_t)k_blocks * block_size > SJSA_MAX_K) return SJSA_ERR_K;
+  if (n_init < 0 || n_local < 0 || (int64_t)n_init + n_local > k_blocks) return SJSA_ERR_DIMS;
+  if (!q || !K || !V || !seq_len || !out || !idx || !workspace || (!Kc && !(Kq && Ks))) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Kc, 16) || !aligned(Kq, 4) ||
+      !aligned(Ks, 2) || !aligned(seq_len, 4) || !aligned(idx, 4) || !aligned(out, 16) ||
+      !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  if (!isfinite(sm_scale)) return SJSA_ERR_DIMS;
+  const BlockLayout L = make_block_layout(*shape, block_size, k_blocks);
+  if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const float scale = resolve_scale(sm_scale);
+  const int ktok = k_blocks * block_size;
+  hipError_t e = launch_block_select(*shape, L, block_size, (const uint16_t*)q, (const uint16_t*)Kc,
+                                     Kc ? nullptr : (const unsigned char*)Kq, Kc ? nullptr : (const uint16_t*)Ks,
+                                     seq_len, k_blocks, n_init, n_local, scale, idx, ws, s);
+  if (e == hipSuccess)
+    e = launch_attend(*shape, L.att, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, ktok, seq_len,
+                      scale, out, ws, s);
   return status_of(e);
 }
 

@@ -75,6 +75,28 @@ hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
                          float sm_scale, void* out, unsigned char* ws, hipStream_t st,
                          const float* bias = nullptr);
+// Block-sparse step: workspace of the block logits and the tiles' softmax partials,
+// then the attention partials (att).
+struct BlockLayout {
+  Layout att;                 // attention split and partials for k_blocks * block_size entries
+  int64_t nblk_cap = 0;       // block keys per (b, h): capacity / block_size
+  int64_t zstride = 0;        // floats per (unit, head) row of block logits
+  int ntile = 0;              // scoring tiles per unit
+  size_t off_z = 0, off_ms = 0, total = 0;
+};
+BlockLayout make_block_layout(const sjsa_shape& s, int block_size, int k_blocks);
+hipError_t launch_kv_rows(const sjsa_shape& s, const uint16_t* k_new, const uint16_t* v_new, int n_new,
+                          const int32_t* pos, uint16_t* K, uint16_t* V, hipStream_t st);
+// pos == nullptr: keys of every complete block of each sequence; else of the blocks
+// completed by the rows [pos_b, pos_b + n_new) just written. Kc / Kq+Ks may be null.
+hipError_t launch_block_keys(const sjsa_shape& s, int bs, const uint16_t* K, const int32_t* seq_len,
+                             const int32_t* pos, int n_new, uint16_t* Kc, unsigned char* Kq, uint16_t* Ks,
+                             hipStream_t st);
+// Kc != nullptr: bf16 block keys; else INT4 codes Kq and fp16 scales Ks.
+hipError_t launch_block_select(const sjsa_shape& s, const BlockLayout& L, int bs, const uint16_t* q,
+                               const uint16_t* Kc, const unsigned char* Kq, const uint16_t* Ks,
+                               const int32_t* seq_len, int k_blocks, int n_init, int n_local, float sm_scale,
+                               int32_t* idx, unsigned char* ws, hipStream_t st);
 // Gated-logit unit selection: idx and bias [B * H_kv, k_units * unit_size].
 hipError_t launch_gate_select(const sjsa_shape& s, const float* gate_scores, int64_t gate_stride,
                               const int32_t* seq_len, int unit_size, int k_units, float lambda, int32_t* idx,

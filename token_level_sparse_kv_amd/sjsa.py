@@ -67,6 +67,13 @@ _SIGS = {
     "sjsa_gated_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int64, _P,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                                               _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_block_keys": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "sjsa_block_append": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                         _P, _P, _P, _P]),
+    "sjsa_block_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
+    "sjsa_block_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P,
+                                              _P, ctypes.c_size_t, _P]),
     "sjsa_workspace_scores_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "sjsa_workspace_score_stride": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "sjsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -395,4 +402,91 @@ def gated_decode_step(q, K, V, gate_scores, seq_len, unit_size, k_units, lam=1.0
                                         int(gate_scores.shape[2]), _ptr(seq_len), int(unit_size), int(k_units),
                                         float(lam), float(sm_scale), _ptr(out), _ptr(idx), _ptr(workspace),
                                         workspace.numel(), _stream(stream)))
+    return out, idx
+
+
+def block_cache(K: torch.Tensor, block_size: int, int4: bool = False, bf16: bool = True):
+    """Empty block-key caches for K [B, H_kv, cap, d]: (Kc bf16 or None, Kq uint8 or None,
+    Ks fp16 or None), floor(cap / block_size) blocks per (b, h)."""
+    B, Hkv, cap, d = K.shape
+    nb = cap // int(block_size)
+    Kc = torch.zeros(B, Hkv, nb, d, dtype=torch.bfloat16, device=K.device) if bf16 else None
+    Kq = torch.zeros(B, Hkv, nb, d // 2, dtype=torch.uint8, device=K.device) if int4 else None
+    Ks = torch.zeros(B, Hkv, nb, d // 64, dtype=torch.float16, device=K.device) if int4 else None
+    return Kc, Kq, Ks
+
+
+def _block_cache_checks(K, block_size, Kc, Kq, Ks):
+    B, Hkv, cap, d = K.shape
+    nb = cap // int(block_size)
+    if Kc is None and (Kq is None or Ks is None):
+        raise ValueError("give the bf16 block keys Kc, or the INT4 pair Kq and Ks")
+    if (Kq is None) != (Ks is None):
+        raise ValueError("Kq and Ks go together")
+    if Kc is not None:
+        _need(Kc, "Kc", torch.bfloat16, (B, Hkv, nb, d))
+    if Kq is not None:
+        _need(Kq, "Kq", torch.uint8, (B, Hkv, nb, d // 2))
+        _need(Ks, "Ks", torch.float16, (B, Hkv, nb, d // 64))
+
+
+def block_keys(K, seq_len, block_size, Kc=None, Kq=None, Ks=None, stream=None):
+    """Keys of every complete block (mean of its keys, bf16; and/or the INT4 form)."""
+    B, Hkv, cap, d = K.shape
+    _need(K, "K", torch.bfloat16, (B, Hkv, cap, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    _block_cache_checks(K, block_size, Kc, Kq, Ks)
+    shape = make_shape(B, Hkv, 1, d, 0, cap)
+    _check(lib().sjsa_block_keys(ctypes.byref(shape), int(block_size), _ptr(K), _ptr(seq_len), _ptr(Kc), _ptr(Kq),
+                                 _ptr(Ks), _stream(stream)))
+
+
+def block_append(k_new, v_new, pos, K, V, block_size, Kc=None, Kq=None, Ks=None, stream=None):
+    """Append T tokens per (b, h) at slots pos[b].. and write the keys of the blocks they complete."""
+    B, Hkv, cap, d = K.shape
+    T = k_new.shape[2]
+    _need(K, "K", torch.bfloat16, (B, Hkv, cap, d))
+    _need(V, "V", torch.bfloat16, (B, Hkv, cap, d))
+    _need(k_new, "k_new", torch.bfloat16, (B, Hkv, T, d))
+    _need(v_new, "v_new", torch.bfloat16, (B, Hkv, T, d))
+    _need(pos, "pos", torch.int32, (B,))
+    _block_cache_checks(K, block_size, Kc, Kq, Ks)
+    shape = make_shape(B, Hkv, 1, d, 0, cap)
+    _check(lib().sjsa_block_append(ctypes.byref(shape), int(block_size), _ptr(k_new), _ptr(v_new), int(T), _ptr(pos),
+                                   _ptr(K), _ptr(V), _ptr(Kc), _ptr(Kq), _ptr(Ks), _stream(stream)))
+
+
+def block_workspace(shape: Shape, block_size: int, k_blocks: int, device=None) -> torch.Tensor:
+    n = lib().sjsa_block_workspace_size(ctypes.byref(shape), int(block_size), int(k_blocks))
+    if n == 0:
+        raise SjsaError(-2, "invalid shape, block size or block budget for the block-sparse step")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def block_decode_step(q, K, V, seq_len, block_size, k_blocks, Kc=None, Kq=None, Ks=None, n_init=1, n_local=2,
+                      sm_scale=0.0, out=None, idx=None, workspace=None, out_f32=False, stream=None):
+    """Block-sparse decode step: block scores from the bf16 keys Kc (or the INT4 keys
+    Kq, Ks when Kc is None), forced first/local blocks plus the best others up to
+    k_blocks, attention over their positions. Returns (out [B, H_q, d],
+    idx [B, H_kv, k_blocks * block_size])."""
+    B, Hkv, cap, d = K.shape
+    _need(q, "q", torch.bfloat16, (B, q.shape[1], d))
+    _need(K, "K", torch.bfloat16, (B, Hkv, cap, d))
+    _need(V, "V", torch.bfloat16, (B, Hkv, cap, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    _block_cache_checks(K, block_size, Kc, Kq, Ks)
+    shape = gated_shape(q, K, out_f32)
+    ktok = int(block_size) * int(k_blocks)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hkv, ktok), dtype=torch.int32, device=q.device)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, q.shape)
+    _need(idx, "idx", torch.int32, (B, Hkv, ktok))
+    if workspace is None:
+        workspace = block_workspace(shape, block_size, k_blocks, q.device)
+    _check(lib().sjsa_block_decode_step(ctypes.byref(shape), int(block_size), _ptr(q), _ptr(K), _ptr(V), _ptr(Kc),
+                                        _ptr(Kq), _ptr(Ks), _ptr(seq_len), int(k_blocks), int(n_init), int(n_local),
+                                        float(sm_scale), _ptr(out), _ptr(idx), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)))
     return out, idx

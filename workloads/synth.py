@@ -235,6 +235,29 @@ def gated_config(seed: int = 4, device="cpu") -> Workload:
     return gated(1, 8, 4, 32768, 64, 32, seed=seed, device=device, name="gated-b1-n32768-u64-k32")
 
 
+def blocks(batch, n_kv_heads, group, n, block_size, k_blocks, *, seed, device="cpu", capacity=None,
+           seq_len=None, name="block-sparse") -> Workload:
+    """Block-sparse decode layer: K, V and q as in rope_gqa (no scoring basis);
+    extra["block_size"], extra["k_blocks"]. seq_len (a list) makes the batch ragged;
+    rows past a sequence's length are zero."""
+    wl = rope_gqa(batch, n_kv_heads, group, n, 16, k_blocks * block_size, seed=seed, device=device,
+                  capacity=capacity, name=name)
+    wl.M = None
+    wl.extra["block_size"] = block_size
+    wl.extra["k_blocks"] = k_blocks
+    if seq_len is not None:
+        wl.seq_len = torch.tensor(seq_len, dtype=torch.int32, device=device)
+        for b, nb in enumerate(seq_len):
+            wl.K[b, :, max(nb, 0):] = 0
+            wl.V[b, :, max(nb, 0):] = 0
+    return wl
+
+
+def block_config(seed: int = 5, device="cpu") -> Workload:
+    """B=4, 64/8 heads (G=8), d=128, n=65536 in 1024 blocks of 64, 16 blocks kept."""
+    return blocks(4, 8, 8, 65536, 64, 16, seed=seed, device=device, name="blocks-b4-g8-n65536-bs64-k16")
+
+
 def new_token(wl: Workload, seed: int, T: int = 1):
     """k_new, v_new [B, H_kv, T, d] bf16 for an append of T tokens."""
     dev = wl.q.device
