@@ -179,6 +179,57 @@ def gated_variant(sj, workloads, steps, warmup, peak):
             "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
 
 
+BLOCK_WORKLOAD = ("block-sparse decode step: batch 4, 64 query / 8 KV heads (G=8), d=128, n=65536 in 1024 blocks "
+                  "of 64, 16 blocks kept (first block and the two local blocks forced); mean block keys; K/V with "
+                  "RoPE; 4 input sets rotated so the K/V rows are not cache resident")
+
+
+def block_variant(sj, workloads, steps, warmup, peak, int4):
+    """The block-sparse step at its own workload (bf16 or INT4 block keys), timed back
+    to back over 4 rotating input sets."""
+    import torch
+    sets = []
+    for i in range(4):
+        w = workloads.block_config(seed=5 + i, device="cuda")
+        bsz = w.extra["block_size"]
+        w.extra["keys"] = sj.block_cache(w.K, bsz, int4=int4, bf16=not int4)
+        sj.block_keys(w.K, w.seq_len, bsz, *w.extra["keys"])
+        sets.append(w)
+    wl = sets[0]
+    bsz, k_blocks = wl.extra["block_size"], wl.extra["k_blocks"]
+    shape = sj.gated_shape(wl.q, wl.K)
+    ws = sj.block_workspace(shape, bsz, k_blocks)
+    out = torch.empty_like(wl.q)
+    idx = torch.empty(wl.batch, wl.n_kv_heads, bsz * k_blocks, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        w = sets[i % len(sets)]
+        Kc, Kq, Ks = w.extra["keys"]
+        sj.block_decode_step(w.q, w.K, w.V, w.seq_len, bsz, k_blocks, Kc, Kq, Ks, 1, 2, out=out, idx=idx,
+                             workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    units = wl.batch * wl.n_kv_heads
+    nblk = wl.capacity // bsz
+    key_bytes = units * nblk * (wl.head_dim // 2 + 2 * (wl.head_dim // 64) if int4 else wl.head_dim * 2)
+    kv = units * k_blocks * bsz * wl.head_dim * 2 * 2
+    nbytes = key_bytes + kv + 2 * wl.q.numel() * 2 + units * k_blocks * bsz * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": BLOCK_WORKLOAD, "block_keys": "int4" if int4 else "bf16", "value": round(1000.0 / ms, 2),
+            "unit": "steps/s", "us_per_step": round(ms * 1000.0, 2), "algorithmic_bytes_per_step": nbytes,
+            "block_key_bytes": key_bytes, "kv_row_bytes": kv, "hbm_gbs": round(gbs, 1),
+            "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +240,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-fp8-variant", action="store_true", help="skip the FP8 scoring-cache measurement")
     ap.add_argument("--no-gated-variant", action="store_true", help="skip the gated-logit step measurement")
+    ap.add_argument("--no-block-variant", action="store_true", help="skip the block-sparse step measurements")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -309,6 +361,10 @@ def main():
     print(f"timed: {ms_per_step * 1000:.1f} us/step, stages (us) {line['stage_us']}", file=sys.stderr, flush=True)
     if not args.no_gated_variant:
         line["gated_variant"] = gated_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS)
+    if not args.no_block_variant:
+        line["block_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS, False)
+        line["block_int4_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS,
+                                                   True)
     if not args.no_fp8_variant:
         line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, args.steps,
                                                 args.warmup, step_bytes, MI355X_HBM_PEAK_GBS)
