@@ -86,3 +86,28 @@ def subspace_overlap(Ma: np.ndarray, Mb: np.ndarray) -> float:
     orthonormal r x d bases: ||Ma Mb^T||_F^2 / r (1 when the subspaces coincide)."""
     C = np.asarray(Ma, dtype=np.float64) @ np.asarray(Mb, dtype=np.float64).T
     return float((C * C).sum() / Ma.shape[0])
+
+
+def accumulate_moments(q_heads_bits: np.ndarray, keys_bits: np.ndarray):
+    """Sums of outer products over calibration positions, the quantities a prefill
+    accumulates (section "校准:一次前向 + 一次特征分解": one dense prefill per
+    calibration sequence accumulates the second moments of the group-mean query and
+    of the key, per layer and KV head):
+        S_Q = sum_n q_bar_n q_bar_n^T,   S_K = sum_n k_n k_n^T   (fp64, exact sums of
+    the fp32 / bf16 values). q_bar_n is the decode step's group-mean query: the fp32
+    sum of the G bf16 heads in head order divided by G in fp32. Dividing by the
+    sample count gives G_Q and G_K; the trace normalization cancels it.
+    q_heads_bits [N, G, d], keys_bits [N, d] bf16 bits."""
+    from .jssa import mean_query
+    from .numerics import bf16_to_f32
+    qh = np.asarray(q_heads_bits)
+    qbar = np.zeros((qh.shape[0], qh.shape[2]))
+    for i in range(qh.shape[0]):
+        qbar[i] = mean_query(qh[i])
+    k = bf16_to_f32(keys_bits).astype(np.float64)
+    return qbar.T @ qbar, k.T @ k
+
+
+def basis_from_sums(SQ: np.ndarray, SK: np.ndarray, r: int):
+    """M* and the descending eigenvalues of G_hatQ + G_hatK from accumulated sums."""
+    return closed_form_basis(trace_normalize(SQ), trace_normalize(SK), r)

@@ -93,3 +93,36 @@ def test_tiny_single_head_calibration():
     P = calib.projector(M)
     for c in wl.extra["outlier_channels"].tolist():
         assert P[c, c] > 0.95
+
+
+def test_accumulated_sums_brute_force_and_invariants():
+    # the sums equal an explicit loop of outer products of the decode step's mean
+    # queries (pinned in the step tests) and of the keys; they are symmetric PSD with
+    # trace = sum of squared norms; splitting the samples adds the sums
+    from oracle import jssa
+    from oracle.numerics import bf16_to_f32, round_to_bf16
+    rng = np.random.default_rng(9)
+    qh = round_to_bf16(rng.standard_normal((40, 4, 16)))
+    ks = round_to_bf16(rng.standard_normal((40, 16)))
+    SQ, SK = calib.accumulate_moments(qh, ks)
+    bq = np.zeros((16, 16))
+    bk = np.zeros((16, 16))
+    for i in range(40):
+        qb = jssa.mean_query(qh[i]).astype(np.float64)
+        kv = bf16_to_f32(ks[i]).astype(np.float64)
+        for a in range(16):
+            for b in range(16):
+                bq[a, b] += qb[a] * qb[b]
+                bk[a, b] += kv[a] * kv[b]
+    assert np.allclose(SQ, bq, rtol=1e-13, atol=1e-13) and np.allclose(SK, bk, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(SQ, SQ.T) and np.min(np.linalg.eigvalsh(SK)) > -1e-9
+    assert abs(np.trace(SK) - (bf16_to_f32(ks).astype(np.float64) ** 2).sum()) < 1e-9
+    a = calib.accumulate_moments(qh[:13], ks[:13])
+    b = calib.accumulate_moments(qh[13:], ks[13:])
+    assert np.allclose(a[0] + b[0], SQ, rtol=1e-13) and np.allclose(a[1] + b[1], SK, rtol=1e-13)
+    # the basis from sums equals the basis from means (the normalization cancels N)
+    M1, w1 = calib.basis_from_sums(SQ, SK, 5)
+    GQ, GK = calib.second_moments(np.stack([jssa.mean_query(qh[i]) for i in range(40)]),
+                                  bf16_to_f32(ks).astype(np.float64))
+    M2, w2 = calib.closed_form_basis(calib.trace_normalize(GQ), calib.trace_normalize(GK), 5)
+    assert np.allclose(w1, w2, atol=1e-12) and calib.subspace_overlap(M1, M2) > 1 - 1e-10
