@@ -302,6 +302,41 @@ int sjsa_block_decode_step(const sjsa_shape* shape, int32_t block_size, const vo
                            float sm_scale, void* out, int32_t* idx, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * Calibration of the scoring basis. Source: JSSA article, section 校准:一次前向 +
+ * 一次特征分解 (one dense prefill per calibration sequence accumulates, per layer
+ * and KV head, the second moments of the group-mean query and of the key; then one
+ * eigendecomposition per layer and KV head), section 迹归一化 (unit-trace
+ * normalization of each moment) and section 闭式谱解 (basis rows = top-r
+ * eigenvectors of the sum of the normalized moments).
+ *
+ * sjsa_calib_accumulate adds one prefill's sums to fp64 accumulators (device):
+ *   q [B, H_q, T, d] bf16 (the prefill's queries), k [B, H_kv, T, d] bf16 (its keys)
+ *   SQ[h] += sum over (b, t) of q_bar q_bar^T, q_bar = the decode step's group-mean
+ *            query (fp32 sum of the G heads in head order, divided by G)
+ *   SK[h] += sum over (b, t) of k k^T          (SQ, SK: [H_kv, d, d] fp64, d = 128)
+ * Products are summed in fp32 over at most 256 positions, then in fp64, in a fixed
+ * order (deterministic). Only batch, n_kv_heads, group and head_dim of shape are
+ * used. The workspace holds per-workgroup fp64 partials
+ * (sjsa_calib_workspace_size bytes, 8-byte aligned).
+ * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _WORKSPACE, _ALIGN, _HIP.
+ */
+size_t sjsa_calib_workspace_size(const sjsa_shape* shape, int64_t n_tokens);
+int sjsa_calib_accumulate(const sjsa_shape* shape, const void* q, const void* k, int64_t n_tokens,
+                          double* SQ, double* SK, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host (no GPU work): the basis of every KV head from accumulated sums (host
+ * memory). A = SQ/tr(SQ) + SK/tr(SK) (symmetrized; the sample count cancels), its
+ * eigendecomposition by cyclic Jacobi rotations in fp64, and M[h] = the eigenvectors
+ * of the r largest eigenvalues as rows (descending; each row's largest-magnitude
+ * component made positive), written as fp32 [H_kv, r, d]. eigenvalues (optional,
+ * [H_kv, d] fp64) receives all eigenvalues in descending order.
+ * Errors: SJSA_ERR_NULL, _DIMS (r outside 1..d, or a zero or non-finite trace).
+ */
+int sjsa_calib_basis(const double* SQ, const double* SK, int32_t n_kv_heads, int32_t d, int32_t r, float* M,
+                     double* eigenvalues);
+
 /* Static message for a status code. */
 const char* sjsa_status_string(int status);
 

@@ -19,7 +19,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsjsa.so")
 OBJDIR = os.path.join(ROOT, "_build", "sjsa")
 
-SOURCES = ["abi.hip", "append.hip", "score.hip", "select.hip", "attend.hip", "gated.hip", "blocks.hip"]
+SOURCES = ["abi.hip", "append.hip", "score.hip", "select.hip", "attend.hip", "gated.hip", "blocks.hip", "calib.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -74,6 +74,10 @@ _SIGS = {
     "sjsa_block_decode_step": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P,
                                               _P, ctypes.c_size_t, _P]),
+    "sjsa_calib_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int64]),
+    "sjsa_calib_accumulate": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, ctypes.c_int64, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
+    "sjsa_calib_basis": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "sjsa_workspace_scores_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "sjsa_workspace_score_stride": (ctypes.c_int64, [ctypes.POINTER(Shape)]),
     "sjsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -490,3 +494,35 @@ def block_decode_step(q, K, V, seq_len, block_size, k_blocks, Kc=None, Kq=None, 
                                         float(sm_scale), _ptr(out), _ptr(idx), _ptr(workspace), workspace.numel(),
                                         _stream(stream)))
     return out, idx
+
+
+def calib_accumulate(q, k, SQ, SK, workspace=None, stream=None):
+    """Add one prefill's second-moment sums to the fp64 accumulators SQ, SK [H_kv, d, d]
+    (device): q [B, H_q, T, d], k [B, H_kv, T, d] bf16."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16, (B, Hq, T, d))
+    _need(k, "k", torch.bfloat16, (B, Hkv, T, d))
+    _need(SQ, "SQ", torch.float64, (Hkv, d, d))
+    _need(SK, "SK", torch.float64, (Hkv, d, d))
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    shape = make_shape(B, Hkv, Hq // Hkv, d, 0, 1)
+    n = lib().sjsa_calib_workspace_size(ctypes.byref(shape), int(T))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().sjsa_calib_accumulate(ctypes.byref(shape), _ptr(q), _ptr(k), int(T), _ptr(SQ), _ptr(SK),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def calib_basis(SQ, SK, r):
+    """Host: the basis M [H_kv, r, d] fp32 and the eigenvalues [H_kv, d] (descending) of
+    SQ/tr(SQ) + SK/tr(SK), from accumulated sums given as host arrays [H_kv, d, d]."""
+    import numpy as np
+    sq = np.ascontiguousarray(SQ.cpu().numpy() if isinstance(SQ, torch.Tensor) else SQ, dtype=np.float64)
+    sk = np.ascontiguousarray(SK.cpu().numpy() if isinstance(SK, torch.Tensor) else SK, dtype=np.float64)
+    H, d, _ = sq.shape
+    M = np.empty((H, int(r), d), dtype=np.float32)
+    w = np.empty((H, d), dtype=np.float64)
+    _check(lib().sjsa_calib_basis(sq.ctypes.data, sk.ctypes.data, H, d, int(r), M.ctypes.data, w.ctypes.data))
+    return M, w
