@@ -230,6 +230,41 @@ def block_variant(sj, workloads, steps, warmup, peak, int4):
             "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
 
 
+CALIB_WORKLOAD = ("calibration accumulation: one 131072-token prefill, 32 query / 8 KV heads (G=4), d=128; "
+                  "second-moment sums of the group-mean query and of the key per KV head")
+FP32_PEAK_TFLOPS = 157.3
+
+
+def calib_variant(sj, reps, warmup):
+    """Second-moment accumulation over one prefill of 131072 tokens (the pages'
+    calibration sequence length), timed over repeated calls."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    T, Hkv, G = 131072, 8, 4
+    q = torch.randn(1, Hkv * G, T, 128, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, Hkv, T, 128, generator=g, device="cuda").to(torch.bfloat16)
+    SQ = torch.zeros(Hkv, 128, 128, dtype=torch.float64, device="cuda")
+    SK = torch.zeros_like(SQ)
+    ws = sj.calib_workspace(q, k)
+    for _ in range(warmup):
+        sj.calib_accumulate(q, k, SQ, SK, workspace=ws)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        sj.calib_accumulate(q, k, SQ, SK, workspace=ws)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    flops = 2 * Hkv * T * 128 * 128 * 2            # both moment matrices, multiply + add per element
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": CALIB_WORKLOAD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_prefill": round(ms, 4), "bound": "alu", "achieved_tflops": round(tf, 2),
+            "peak_tflops": FP32_PEAK_TFLOPS, "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+            "input_bytes": q.numel() * 2 + k.numel() * 2}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +276,7 @@ def main():
     ap.add_argument("--no-fp8-variant", action="store_true", help="skip the FP8 scoring-cache measurement")
     ap.add_argument("--no-gated-variant", action="store_true", help="skip the gated-logit step measurement")
     ap.add_argument("--no-block-variant", action="store_true", help="skip the block-sparse step measurements")
+    ap.add_argument("--no-calib-variant", action="store_true", help="skip the calibration accumulation measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -365,6 +401,8 @@ def main():
         line["block_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS, False)
         line["block_int4_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS,
                                                    True)
+    if not args.no_calib_variant:
+        line["calib_variant"] = calib_variant(sj, max(2, args.steps // 20), 1)
     if not args.no_fp8_variant:
         line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, args.steps,
                                                 args.warmup, step_bytes, MI355X_HBM_PEAK_GBS)

@@ -4,5 +4,5 @@ from .sjsa import (SjsaError, Shape, make_shape, shape_of, workspace_size, alloc
                    scores_view, append_kv, decode_step, decode_step_append, score, prep, prep_append, scan,
                    select, topk, attend, gated_decode_step, gated_workspace, gated_shape,
                    block_cache, block_keys, block_append, block_workspace, block_decode_step,
-                   calib_accumulate, calib_basis, lib, LIB_PATH,
+                   calib_accumulate, calib_workspace, calib_basis, lib, LIB_PATH,
                    SJSA_FLAG_OUT_F32, SJSA_FLAG_KPROJ_FP8, SJSA_MAX_K, kproj_is_fp8)

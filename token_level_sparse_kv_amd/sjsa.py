@@ -496,6 +496,17 @@ def block_decode_step(q, K, V, seq_len, block_size, k_blocks, Kc=None, Kq=None, 
     return out, idx
 
 
+def calib_workspace(q, k) -> torch.Tensor:
+    """Workspace for calib_accumulate with these q [B, H_q, T, d] and k [B, H_kv, T, d]."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    shape = make_shape(B, Hkv, Hq // Hkv, d, 0, 1)
+    n = lib().sjsa_calib_workspace_size(ctypes.byref(shape), int(T))
+    if n == 0:
+        raise SjsaError(-2, "invalid shape for the calibration accumulation")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def calib_accumulate(q, k, SQ, SK, workspace=None, stream=None):
     """Add one prefill's second-moment sums to the fp64 accumulators SQ, SK [H_kv, d, d]
     (device): q [B, H_q, T, d], k [B, H_kv, T, d] bf16."""
@@ -508,9 +519,8 @@ def calib_accumulate(q, k, SQ, SK, workspace=None, stream=None):
     if Hq % Hkv:
         raise ValueError("query heads must be a multiple of KV heads")
     shape = make_shape(B, Hkv, Hq // Hkv, d, 0, 1)
-    n = lib().sjsa_calib_workspace_size(ctypes.byref(shape), int(T))
     if workspace is None:
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        workspace = calib_workspace(q, k)
     _check(lib().sjsa_calib_accumulate(ctypes.byref(shape), _ptr(q), _ptr(k), int(T), _ptr(SQ), _ptr(SK),
                                        _ptr(workspace), workspace.numel(), _stream(stream)))
 
