@@ -95,7 +95,23 @@ def cpu_baseline(host, units, k, scale, gpu_out, gpu_idx):
     return dt, workers, ok, worst
 
 
-def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, warmup, step_bytes, peak):
+def oracle_timing(jobs):
+    """Wall time of the oracle jobs (callables) on a thread pool, and the thread count."""
+    workers = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(lambda f: f(), jobs))
+    return time.perf_counter() - t0, workers, res
+
+
+def _bits(t):
+    import numpy as np
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, warmup, step_bytes, peak,
+                cpu=False):
     """The same step over an FP8 E4M3 scoring cache (one byte per element), timed the
     same way. Reported beside the bf16 figure, which stays the headline."""
     import numpy as np
@@ -132,9 +148,26 @@ def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, 
     ms = start.elapsed_time(end) / steps
     tb = step_bytes(B, Hkv, G, d, r, n, k, kb=1)
     gbs = tb["total"] / (ms * 1e-3) / 1e9
-    return {"kproj_dtype": "fp8_e4m3", "value": round(1000.0 / ms, 2), "unit": "steps/s",
-            "ms_per_step": round(ms, 5), "algorithmic_bytes_per_step": tb["total"], "hbm_gbs": round(gbs, 1),
-            "hbm_frac_of_peak": round(gbs / peak, 4)}
+    res = {"kproj_dtype": "fp8_e4m3", "value": round(1000.0 / ms, 2), "unit": "steps/s",
+           "ms_per_step": round(ms, 5), "algorithmic_bytes_per_step": tb["total"], "hbm_gbs": round(gbs, 1),
+           "hbm_frac_of_peak": round(gbs / peak, 4)}
+    if cpu:
+        from oracle import jssa
+        units = [(b, h) for b in range(0, B, 4) for h in range(0, Hkv, 2)]       # 16 of 128
+        q = _bits(q_sets[0])
+        Mh = M.cpu().numpy()
+        scale = jssa.default_sm_scale(d)
+        jobs = []
+        for b, h in units:
+            Kb, Vb, Pb = _bits(K[b, h]), _bits(V[b, h]), Kp8[b, h].cpu().numpy()
+            jobs.append(lambda b=b, h=h, Kb=Kb, Vb=Vb, Pb=Pb: jssa.decode_unit(
+                q[b, h * G:(h + 1) * G], Kb, Vb, Pb, Mh[h], n, k, scale, "fp8"))
+        dt, workers, _ = oracle_timing(jobs)
+        scale_up = B * Hkv / len(units)
+        res["cpu_baseline"] = {"value": round(1.0 / (dt * scale_up), 4), "unit": "steps/s", "cores": workers,
+                               "kind": "oracle", "sample": f"{len(units)} of {B * Hkv} units of one step, wall "
+                                                           f"time scaled by {scale_up:g}"}
+    return res
 
 
 GATED_WORKLOAD = ("gated-logit decode step: batch 1, 32 query / 8 KV heads (G=4), d=128, n=32768 in 512 units of "
@@ -142,7 +175,7 @@ GATED_WORKLOAD = ("gated-logit decode step: batch 1, 32 query / 8 KV heads (G=4)
                   "rotated so the K/V rows are not cache resident")
 
 
-def gated_variant(sj, workloads, steps, warmup, peak):
+def gated_variant(sj, workloads, steps, warmup, peak, cpu=False):
     """The gated-logit (unit-gated) step at its own workload, timed back to back over
     4 rotating input sets (together larger than the last-level cache)."""
     import torch
@@ -174,9 +207,24 @@ def gated_variant(sj, workloads, steps, warmup, peak):
     kv = units * ktok * wl.head_dim * 2 * 2
     nbytes = (kv + units * (wl.capacity // unit) * 4 + 2 * wl.q.numel() * 2 + units * ktok * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": GATED_WORKLOAD, "value": round(1000.0 / ms, 2), "unit": "steps/s",
-            "us_per_step": round(ms * 1000.0, 2), "algorithmic_bytes_per_step": nbytes, "kv_row_bytes": kv,
-            "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
+    res = {"workload": GATED_WORKLOAD, "value": round(1000.0 / ms, 2), "unit": "steps/s",
+           "us_per_step": round(ms * 1000.0, 2), "algorithmic_bytes_per_step": nbytes, "kv_row_bytes": kv,
+           "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
+    if cpu:
+        from oracle import jssa, sas
+        q = _bits(wl.q)
+        u = wl.extra["gate_scores"].cpu().numpy()
+        G = wl.group
+        n = int(wl.seq_len[0])
+        jobs = []
+        for h in range(wl.n_kv_heads):
+            Kb, Vb = _bits(wl.K[0, h]), _bits(wl.V[0, h])
+            jobs.append(lambda h=h, Kb=Kb, Vb=Vb: sas.gated_decode_unit(
+                q[0, h * G:(h + 1) * G], Kb, Vb, u[0, h], n, unit, k_units, 1.0, jssa.default_sm_scale(128)))
+        dt, workers, _ = oracle_timing(jobs)
+        res["cpu_baseline"] = {"value": round(1.0 / dt, 2), "unit": "steps/s", "cores": workers, "kind": "oracle",
+                               "sample": "all 8 (sequence, KV head) units of one step"}
+    return res
 
 
 BLOCK_WORKLOAD = ("block-sparse decode step: batch 4, 64 query / 8 KV heads (G=8), d=128, n=65536 in 1024 blocks "
@@ -184,7 +232,7 @@ BLOCK_WORKLOAD = ("block-sparse decode step: batch 4, 64 query / 8 KV heads (G=8
                   "RoPE; 4 input sets rotated so the K/V rows are not cache resident")
 
 
-def block_variant(sj, workloads, steps, warmup, peak, int4):
+def block_variant(sj, workloads, steps, warmup, peak, int4, cpu=False):
     """The block-sparse step at its own workload (bf16 or INT4 block keys), timed back
     to back over 4 rotating input sets."""
     import torch
@@ -224,10 +272,36 @@ def block_variant(sj, workloads, steps, warmup, peak, int4):
     kv = units * k_blocks * bsz * wl.head_dim * 2 * 2
     nbytes = key_bytes + kv + 2 * wl.q.numel() * 2 + units * k_blocks * bsz * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": BLOCK_WORKLOAD, "block_keys": "int4" if int4 else "bf16", "value": round(1000.0 / ms, 2),
-            "unit": "steps/s", "us_per_step": round(ms * 1000.0, 2), "algorithmic_bytes_per_step": nbytes,
-            "block_key_bytes": key_bytes, "kv_row_bytes": kv, "hbm_gbs": round(gbs, 1),
-            "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
+    res = {"workload": BLOCK_WORKLOAD, "block_keys": "int4" if int4 else "bf16", "value": round(1000.0 / ms, 2),
+           "unit": "steps/s", "us_per_step": round(ms * 1000.0, 2), "algorithmic_bytes_per_step": nbytes,
+           "block_key_bytes": key_bytes, "kv_row_bytes": kv, "hbm_gbs": round(gbs, 1),
+           "hbm_frac_of_peak": round(gbs / peak, 4), "bound": "latency"}
+    if cpu:
+        from oracle import blocksparse, jssa
+        from oracle.numerics import bf16_to_f32
+        q = _bits(wl.q)
+        G = wl.group
+        n = int(wl.seq_len[0])
+        m = n // bsz
+        Kc, Kq, Ks = wl.extra["keys"]
+        units = [(b, h) for b in range(wl.batch) for h in (0, 5)]                 # 8 of 32
+        jobs = []
+        for b, h in units:
+            Kb, Vb = _bits(wl.K[b, h]), _bits(wl.V[b, h])
+            if int4:
+                kcv = blocksparse.int4_dequantize(blocksparse.unpack_int4(Kq[b, h, :m].cpu().numpy()),
+                                                  _bits(Ks[b, h, :m]))
+            else:
+                kcv = bf16_to_f32(_bits(Kc[b, h, :m]))
+            jobs.append(lambda b=b, h=h, Kb=Kb, Vb=Vb, kcv=kcv: blocksparse.decode_unit(
+                q[b, h * G:(h + 1) * G], Kb, Vb, kcv, n, bsz, k_blocks, 1, 2, jssa.default_sm_scale(128)))
+        dt, workers, _ = oracle_timing(jobs)
+        units_total = wl.batch * wl.n_kv_heads
+        scale_up = units_total / len(units)
+        res["cpu_baseline"] = {"value": round(1.0 / (dt * scale_up), 3), "unit": "steps/s", "cores": workers,
+                               "kind": "oracle", "sample": f"{len(units)} of {units_total} units of one step, "
+                                                           f"wall time scaled by {scale_up:g}"}
+    return res
 
 
 CALIB_WORKLOAD = ("calibration accumulation: one 131072-token prefill, 32 query / 8 KV heads (G=4), d=128; "
@@ -235,7 +309,7 @@ CALIB_WORKLOAD = ("calibration accumulation: one 131072-token prefill, 32 query 
 FP32_PEAK_TFLOPS = 157.3
 
 
-def calib_variant(sj, reps, warmup):
+def calib_variant(sj, reps, warmup, cpu=False):
     """Second-moment accumulation over one prefill of 131072 tokens (the pages'
     calibration sequence length), timed over repeated calls."""
     import torch
@@ -259,10 +333,25 @@ def calib_variant(sj, reps, warmup):
     ms = start.elapsed_time(end) / reps
     flops = 2 * Hkv * T * 128 * 128 * 2            # both moment matrices, multiply + add per element
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": CALIB_WORKLOAD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_prefill": round(ms, 4), "bound": "alu", "achieved_tflops": round(tf, 2),
-            "peak_tflops": FP32_PEAK_TFLOPS, "frac": round(tf / FP32_PEAK_TFLOPS, 4),
-            "input_bytes": q.numel() * 2 + k.numel() * 2}
+    res = {"workload": CALIB_WORKLOAD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+           "ms_per_prefill": round(ms, 4), "bound": "alu", "achieved_tflops": round(tf, 2),
+           "peak_tflops": FP32_PEAK_TFLOPS, "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+           "input_bytes": q.numel() * 2 + k.numel() * 2}
+    if cpu:
+        from oracle import calib
+        P = 4096                                    # positions per sampled KV head
+        heads = [0, 3, 6, 7]
+        jobs = []
+        for h in heads:
+            qh = _bits(q[0, h * G:(h + 1) * G, :P]).transpose(1, 0, 2).copy()      # [P, G, d]
+            kh = _bits(k[0, h, :P])
+            jobs.append(lambda qh=qh, kh=kh: calib.accumulate_moments(qh, kh))
+        dt, workers, _ = oracle_timing(jobs)
+        sampled = P * len(heads)
+        res["cpu_baseline"] = {"value": round(sampled / Hkv / dt, 1), "unit": "tokens/s", "cores": workers,
+                               "kind": "oracle", "sample": f"{P} positions of {len(heads)} of {Hkv} KV heads; "
+                                                           f"tokens/s = positions per KV head / wall time"}
+    return res
 
 
 def main():
@@ -396,16 +485,19 @@ def main():
 
     print(f"timed: {ms_per_step * 1000:.1f} us/step, stages (us) {line['stage_us']}", file=sys.stderr, flush=True)
     if not args.no_gated_variant:
-        line["gated_variant"] = gated_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS)
+        line["gated_variant"] = gated_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS,
+                                              cpu=not args.no_cpu_baseline)
     if not args.no_block_variant:
-        line["block_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS, False)
+        line["block_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS, False,
+                                              cpu=not args.no_cpu_baseline)
         line["block_int4_variant"] = block_variant(sj, workloads, args.steps, args.warmup, MI355X_HBM_PEAK_GBS,
-                                                   True)
+                                                   True, cpu=not args.no_cpu_baseline)
     if not args.no_calib_variant:
-        line["calib_variant"] = calib_variant(sj, max(2, args.steps // 20), 1)
+        line["calib_variant"] = calib_variant(sj, max(2, args.steps // 20), 1, cpu=not args.no_cpu_baseline)
     if not args.no_fp8_variant:
         line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, args.steps,
-                                                args.warmup, step_bytes, MI355X_HBM_PEAK_GBS)
+                                                args.warmup, step_bytes, MI355X_HBM_PEAK_GBS,
+                                                cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         rng = np.random.default_rng(3)
         all_units = [(b, h) for b in range(B) for h in range(Hkv)]
