@@ -306,7 +306,11 @@ def block_variant(sj, workloads, steps, warmup, peak, int4, cpu=False):
 
 CALIB_WORKLOAD = ("calibration accumulation: one 131072-token prefill, 32 query / 8 KV heads (G=4), d=128; "
                   "second-moment sums of the group-mean query and of the key per KV head")
-FP32_PEAK_TFLOPS = 157.3
+# fp32 FMA peak for non-packed instructions: 256 CUs x 64 FMA lanes per clock x 2 flops x
+# 2.4 GHz. The published 157.3 TFLOP/s counts packed FP32 (two FMAs per lane per
+# instruction), which this build does not emit.
+FP32_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+FP32_PACKED_PEAK_TFLOPS = 157.3
 
 
 def calib_variant(sj, reps, warmup, cpu=False):
@@ -335,7 +339,8 @@ def calib_variant(sj, reps, warmup, cpu=False):
     tf = flops / (ms * 1e-3) / 1e12
     res = {"workload": CALIB_WORKLOAD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
            "ms_per_prefill": round(ms, 4), "bound": "alu", "achieved_tflops": round(tf, 2),
-           "peak_tflops": FP32_PEAK_TFLOPS, "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+           "peak_tflops": round(FP32_PEAK_TFLOPS, 2), "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+           "packed_fp32_peak_tflops": FP32_PACKED_PEAK_TFLOPS,
            "input_bytes": q.numel() * 2 + k.numel() * 2}
     if cpu:
         from oracle import calib
