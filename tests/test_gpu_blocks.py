@@ -157,3 +157,17 @@ def test_block_step_many_blocks_scores_from_global():
     keys = _keys(wl, 4, int4=True)
     _check_step(wl, 4, 50, keys, tag="many bf16")
     _check_step(wl, 4, 50, keys, tag="many int4", int4=True)
+
+
+def test_block_step_largest_budget_and_clamped_lengths():
+    # the largest block budget (4096 blocks of one position: every key its own block),
+    # a capacity that is not a multiple of the block size, lengths above the capacity
+    say("block step: 4096-block budget; capacity not a multiple of bs; seq_len above capacity")
+    wl = workloads.blocks(2, 1, 4, 9000, 1, 4096, seed=88, device="cuda", capacity=9000)
+    wl.seq_len = torch.tensor([20000, 7777], dtype=torch.int32, device="cuda")
+    keys = _keys(wl, 1, int4=True)
+    _check_step(wl, 1, 4096, keys, tag="budget 4096")
+    wl2 = workloads.blocks(2, 2, 2, 1000, 48, 6, seed=89, device="cuda", capacity=1001, seq_len=[1001, 999])
+    keys2 = _keys(wl2, 48, int4=True)
+    _check_step(wl2, 48, 6, keys2, tag="bs 48 cap 1001")
+    _check_step(wl2, 48, 6, keys2, tag="bs 48 cap 1001 int4", int4=True)

@@ -94,3 +94,14 @@ def test_gated_is_deterministic():
     b = sj.gated_decode_step(wl.q, wl.K, wl.V, u, wl.seq_len, 64, 32)
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+def test_gated_largest_unit_budget_and_clamped_lengths():
+    # the largest unit budget the library takes (4096 units), single-token units, and
+    # sequence lengths beyond the capacity (clamped to it)
+    say("gated: 4096-unit budget; seq_len above capacity")
+    wl = workloads.gated(2, 1, 4, 9000, 1, 4096, seed=77, device="cuda", capacity=9000)
+    wl.seq_len = torch.tensor([12000, 5000], dtype=torch.int32, device="cuda")
+    _check(wl, 1, 4096, 1.0, tag="budget 4096")
+    wl2 = workloads.gated(1, 2, 2, 3000, 64, 4096, seed=78, device="cuda")     # every unit fits the budget
+    _check(wl2, 64, 4096, 0.5, tag="all units kept")
