@@ -171,3 +171,25 @@ def test_block_step_largest_budget_and_clamped_lengths():
     keys2 = _keys(wl2, 48, int4=True)
     _check_step(wl2, 48, 6, keys2, tag="bs 48 cap 1001")
     _check_step(wl2, 48, 6, keys2, tag="bs 48 cap 1001 int4", int4=True)
+
+
+def test_block_toy_by_hand_on_gpu():
+    from tests import golden_variants as gv
+    from tests.util import from_bits
+    say("block step: hand-worked toy (bf16 and INT4 keys)")
+    g = gv.load("block_toy")
+    q = from_bits(gv.padded_bits(g["q_heads"]))[None].cuda()
+    K = from_bits(gv.padded_bits(g["K"]))[None, None].cuda()
+    V = from_bits(gv.padded_bits(g["V"]))[None, None].cuda()
+    sl = torch.tensor([g["n"]], dtype=torch.int32, device="cuda")
+    bsz = g["block_size"]
+    Kc, Kq, Ks = sj.block_cache(K, bsz, int4=True)
+    sj.block_keys(K, sl, bsz, Kc, Kq, Ks)
+    for keys in ((Kc, None, None), (None, Kq, Ks)):
+        out, idx = sj.block_decode_step(q, K, V, sl, bsz, g["k_blocks"], *keys, g["n_init"], g["n_local"],
+                                        sm_scale=1.0, out_f32=True)
+        torch.cuda.synchronize()
+        assert list(idx.cpu().numpy()[0, 0]) == g["idx"]
+        o = out.cpu().numpy()[0]
+        assert np.max(np.abs(o[:, :4] - gv.matrix(g["out"]))) < 1e-5
+        assert np.all(o[:, 4:] == 0)

@@ -105,3 +105,23 @@ def test_gated_largest_unit_budget_and_clamped_lengths():
     _check(wl, 1, 4096, 1.0, tag="budget 4096")
     wl2 = workloads.gated(1, 2, 2, 3000, 64, 4096, seed=78, device="cuda")     # every unit fits the budget
     _check(wl2, 64, 4096, 0.5, tag="all units kept")
+
+
+def test_gated_toy_by_hand_on_gpu():
+    from tests import golden_variants as gv
+    from tests.util import from_bits
+    say("gated: hand-worked toy")
+    g = gv.load("gated_toy")
+    q = from_bits(gv.padded_bits(g["q_heads"]))[None].cuda()
+    K = from_bits(gv.padded_bits(g["K"]))[None, None].cuda()
+    V = from_bits(gv.padded_bits(g["V"]))[None, None].cuda()
+    u = torch.tensor([[[gv.value(x) for x in g["u"]]]], dtype=torch.float32, device="cuda")
+    sl = torch.tensor([g["n"]], dtype=torch.int32, device="cuda")
+    for c in g["cases"]:
+        out, idx = sj.gated_decode_step(q, K, V, u, sl, g["unit_size"], g["k_units"], lam=c["lambda"], sm_scale=1.0,
+                                        out_f32=True)
+        torch.cuda.synchronize()
+        assert list(idx.cpu().numpy()[0, 0]) == g["idx"]
+        o = out.cpu().numpy()[0]
+        assert np.max(np.abs(o[:, :4] - gv.matrix(c["out"]))) < 1e-5
+        assert np.all(o[:, 4:] == 0)
