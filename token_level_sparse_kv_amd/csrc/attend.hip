@@ -7,7 +7,8 @@
 // each indexed read is a full burst (section 不规则索引本身不是障碍): here a
 // 256-byte row is read by 16 lanes with 16 bytes each.
 //
-// grid = (nsplit, B * H_kv), 256 threads = 16 row slots of 16 lanes. A workgroup
+// grid = (nsplit, B * H_kv), 256 threads = 16 row slots of 16 lanes (G = 8 without
+// logit terms uses the MFMA form below instead). A workgroup
 // handles `chunk` consecutive entries of its unit's index list; each slot walks
 // its share of rows, U rows at a time (nontemporal loads: every row is read once),
 // computing the G logits per row (lane t holds head dims 8t..8t+7, dotted as bf16
@@ -216,6 +217,211 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
+// MFMA form of the same computation, used for G = 8 (v_mfma_f32_16x16x16_bf16; lane
+// l of a wave holds A[l%16][4*(l/16)+v], B[4*(l/16)+v][l%16] and D[4*(l/16)+v][l%16],
+// v = 0..3). With 8 heads the per-row dot products and reductions of the vector form
+// need about 210 VGPRs (2 waves per SIMD); here the 16-wide tiles are half used and
+// the kernel keeps 4 waves per SIMD.
+// grid = (nsplit, B * H_kv), 256 threads = 4 waves; wave w takes groups w, w+4, ...
+// of 16 consecutive entries of the workgroup's chunk. Per group:
+//  * S = K Q^T (16 keys x 16 columns, the first G columns being the query heads) in
+//    8 steps over d; lane l loads 4 x 16 bytes of key row l%16, which directly form
+//    its A operands once d is ordered so that step s, k-row 4q+v covers dim
+//    32(s/2) + 8q + 4(s%2) + v; the queries are laid out the same way as B;
+//  * softmax bookkeeping per head on the D layout (the 4 keys of a lane, then
+//    across the 4 lane rows), with the lazily moved reference as above;
+//  * O += P V: D's layout already is P's A layout (head l%16, keys 4(l/16)+v); V is
+//    staged through a per-wave LDS tile and read back as key columns; O columns
+//    are dims in the order dim(t, c) = 32(t/2) + 2c + (t%2) for tile t, column c.
+template <int G>
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attend_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ seq_len, int n_kv_heads, int64_t cap,
+    int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
+    void* __restrict__ out, int out_f32) {
+  static_assert(G <= 16, "the query heads fill at most the 16 MFMA columns");
+  constexpr int NW = ATT_THREADS / 64;
+  constexpr int KG = 16;                    // keys per MFMA group
+  constexpr int PITCH = HEAD_DIM + 8;       // LDS V row pitch in bf16 (272 bytes: conflict-free column reads)
+  __shared__ int32_t sidx[1024];
+  __shared__ uint16_t sv[NW][KG * PITCH];
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_o[NW][G][HEAD_DIM];
+
+  const int unit = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = unit / n_kv_heads;
+  const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, q4 = lane >> 4;  // A/B/D row-in-16 and 4-row group of this lane
+
+  const int first = split * chunk;
+  const int cnt = max(0, min(chunk, k - first));
+  const int32_t* ids = idx + (size_t)unit * k + first;
+  for (int i = tid; i < cnt; i += ATT_THREADS) sidx[i] = ids[i];
+
+  // B operands of S = K Q^T: column r is query head r (zero past G)
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  s16x4 qb[8];
+  {
+    const uint16_t* qh = q + ((size_t)unit * G + min(r, G - 1)) * HEAD_DIM;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint2 w = *reinterpret_cast<const uint2*>(qh + 32 * (s / 2) + 8 * q4 + 4 * (s % 2));
+      const u32x2 x = {r < G ? w.x : 0u, r < G ? w.y : 0u};
+      qb[s] = __builtin_bit_cast(s16x4, x);
+    }
+  }
+  f32x4 O[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;          // per head r (identical in the 4 lane rows)
+  __syncthreads();
+
+  const uint16_t* Kb = K + (size_t)unit * cap * HEAD_DIM + 8 * q4;
+  const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + 8 * q4;
+  uint16_t* tile = sv[wave];
+  for (int e0 = wave * KG; e0 < cnt; e0 += NW * KG) {
+    // key row r of the group: 4 x 16 bytes each of K and V (unconditional loads; an
+    // invalid entry reads row 0 and gets zero weight)
+    const int32_t jr = e0 + r < cnt ? sidx[e0 + r] : -1;
+    const int64_t row = (jr >= 0 && (int64_t)jr < cap) ? jr : 0;
+    u32x4 kc[4], vc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kc[c] = ld16_stream(Kb + (size_t)row * HEAD_DIM + 32 * c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vc[c] = ld16_stream(Vb + (size_t)row * HEAD_DIM + 32 * c);
+    bool ok[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = e0 + 4 * q4 + v;
+      const int32_t j = e < cnt ? sidx[e] : -1;
+      ok[v] = j >= 0 && (int64_t)j < n && r < G;
+    }
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 kw = kc[s / 2];
+      const u32x2 h = (s % 2) ? u32x2{kw.z, kw.w} : u32x2{kw.x, kw.y};
+      S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, h), qb[s], S, 0, 0, 0);
+    }
+    // V rows into the wave's LDS tile (row r, dims 32c + 8q4 ..)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(tile + r * PITCH + 32 * c + 8 * q4) = vc[c];
+
+    // softmax bookkeeping for head r over the group's keys 4q4+v
+    float z[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      z[v] = ok[v] ? S[v] * qscale : -INFINITY;
+      mx = fmaxf(mx, z[v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool raise = mx > m + RESCALE_SLACK;
+    if (__ballot(raise) != 0ull) {          // some head's reference moves: rescale
+      const float sc = raise ? exp2f(m - mx) : 1.f;
+      if (raise) m = mx;
+      lsum *= sc;
+      // O rows are heads 4q4+v; head h's factor is in lane h
+      float f[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int qq = 0; qq < (G + 3) / 4; ++qq) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (q4 == qq) f[v] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 4 * qq + v));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) O[t][v] *= f[v];
+      }
+    }
+    // the weights enter the PV product as bf16 pairs hi + lo (hi = bf16(p), lo =
+    // bf16(p - hi)), which keeps them to about 16 significant bits
+    const float ref = m == -INFINITY ? 0.f : m;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float pv = exp2f(z[v] - ref);
+      lsum += pv;
+      ph[v] = f32_to_bf16_rne(pv);
+      pl[v] = f32_to_bf16_rne(pv - __uint_as_float(ph[v] << 16));
+    }
+    const s16x4 pa_hi = __builtin_bit_cast(s16x4, u32x2{ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)});
+    const s16x4 pa_lo = __builtin_bit_cast(s16x4, u32x2{pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)});
+
+    // the tile's writes are wave-private: order them before the column reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) w[v] = *reinterpret_cast<const uint32_t*>(tile + (4 * q4 + v) * PITCH + 32 * t2 + 2 * r);
+      const u32x2 lo = {(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
+      const u32x2 hi = {(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+      const s16x4 vlo = __builtin_bit_cast(s16x4, lo), vhi = __builtin_bit_cast(s16x4, hi);
+      O[2 * t2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, vlo, O[2 * t2], 0, 0, 0);
+      O[2 * t2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, vlo, O[2 * t2], 0, 0, 0);
+      O[2 * t2 + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, vhi, O[2 * t2 + 1], 0, 0, 0);
+      O[2 * t2 + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, vhi, O[2 * t2 + 1], 0, 0, 0);
+    }
+    // the next group rewrites the tile only after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+
+  // ---- combine the waves of this workgroup
+  if (q4 == 0 && r < G) { sm_m[wave][r] = m; sm_l[wave][r] = lsum; }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * q4 + v;
+      if (h < G) sm_o[wave][h][32 * (t / 2) + 2 * r + (t % 2)] = O[t][v];
+    }
+  }
+  __syncthreads();
+
+  const bool direct = nsplit == 1;
+  float* part = partials + ((size_t)unit * nsplit + split) * G * PART_STRIDE;
+  for (int o = tid; o < G * HEAD_DIM; o += ATT_THREADS) {
+    const int g = o / HEAD_DIM, dim = o - g * HEAD_DIM;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NW; ++s) M = fmaxf(M, sm_m[s][g]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < NW; ++s) {
+        const float ms = sm_m[s][g];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f(ms - M);
+        L = fmaf(sm_l[s][g], w, L);
+        A = fmaf(sm_o[s][g][dim], w, A);
+      }
+    }
+    if (direct) {
+      const float res = L > 0.f ? A / L : 0.f;
+      const size_t oi = ((size_t)unit * G + g) * HEAD_DIM + dim;
+      if (out_f32) reinterpret_cast<float*>(out)[oi] = res;
+      else reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(res);
+    } else {
+      part[g * PART_STRIDE + dim] = A;
+      if (dim == 0) { part[g * PART_STRIDE + HEAD_DIM] = M; part[g * PART_STRIDE + HEAD_DIM + 1] = L; }
+    }
+  }
+}
+
 // Combine the nsplit partials of one (unit, query head) in split order; one thread
 // per output dim. Partial s holds the running maximum m_s (exp2 domain), the sum
 // l_s and the unnormalized output acc_s; the merge keeps a running (m, l, acc)
@@ -258,34 +464,47 @@ __global__ __launch_bounds__(HEAD_DIM) void merge_kernel(const float* __restrict
 
 }  // namespace
 
+namespace {
+
+template <int G>
+void launch_attend_g(const Layout& L, const uint16_t* q, const uint16_t* K, const uint16_t* V, const int32_t* idx,
+                     const float* bias, int k, const int32_t* seq_len, int n_kv_heads, int64_t cap, float qscale,
+                     float* partials, void* out, int out_f32, hipStream_t st) {
+  const dim3 grid((unsigned)L.nsplit, (unsigned)L.units), block(ATT_THREADS);
+  if (bias) {
+    attend_kernel<G, ATT_U, true><<<grid, block, 0, st>>>(q, K, V, idx, bias, seq_len, n_kv_heads, cap, k, L.chunk,
+                                                          L.nsplit, qscale, partials, out, out_f32);
+  } else if constexpr (G == 8) {
+    attend_mfma_kernel<G><<<grid, block, 0, st>>>(q, K, V, idx, seq_len, n_kv_heads, cap, k, L.chunk, L.nsplit,
+                                                  qscale, partials, out, out_f32);
+  } else {
+    attend_kernel<G, ATT_U, false><<<grid, block, 0, st>>>(q, K, V, idx, nullptr, seq_len, n_kv_heads, cap, k,
+                                                           L.chunk, L.nsplit, qscale, partials, out, out_f32);
+  }
+  const dim3 mgrid((unsigned)(L.units * G));
+  if (L.nsplit > 8) merge_kernel<G, 32><<<mgrid, dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32);
+  else if (L.nsplit > 1) merge_kernel<G, 8><<<mgrid, dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32);
+}
+
+}  // namespace
+
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
                          float sm_scale, void* out, unsigned char* ws, hipStream_t st, const float* bias) {
   float* partials = reinterpret_cast<float*>(ws + L.off_partials);
   const float qscale = sm_scale * LOG2E;
   const int out_f32 = (s.flags & SJSA_FLAG_OUT_F32) ? 1 : 0;
-  const dim3 grid((unsigned)L.nsplit, (unsigned)L.units), block(ATT_THREADS);
-#define SJSA_ATT(GG)                                                                                        \
-  if (bias)                                                                                                 \
-    attend_kernel<GG, ATT_U, true><<<grid, block, 0, st>>>(q, K, V, idx, bias, seq_len, s.n_kv_heads,         \
-                                                           s.capacity, k, L.chunk, L.nsplit, qscale, partials, \
-                                                           out, out_f32);                                      \
-  else                                                                                                      \
-    attend_kernel<GG, ATT_U, false><<<grid, block, 0, st>>>(q, K, V, idx, nullptr, seq_len, s.n_kv_heads,     \
-                                                            s.capacity, k, L.chunk, L.nsplit, qscale, partials,\
-                                                            out, out_f32);                                     \
-  if (L.nsplit > 8)                                                                                         \
-    merge_kernel<GG, 32><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32); \
-  else if (L.nsplit > 1)                                                                                    \
-    merge_kernel<GG, 8><<<dim3((unsigned)(L.units * GG)), dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32)
   switch (s.group) {
-    case 1: SJSA_ATT(1); break;
-    case 2: SJSA_ATT(2); break;
-    case 4: SJSA_ATT(4); break;
-    case 8: SJSA_ATT(8); break;
+    case 1: launch_attend_g<1>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
+                               out_f32, st); break;
+    case 2: launch_attend_g<2>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
+                               out_f32, st); break;
+    case 4: launch_attend_g<4>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
+                               out_f32, st); break;
+    case 8: launch_attend_g<8>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
+                               out_f32, st); break;
     default: return hipErrorInvalidValue;
   }
-#undef SJSA_ATT
   return hipGetLastError();
 }
 
