@@ -13,9 +13,10 @@
 //     sum in row order, divided by the block size, rounded to bf16); optionally also
 //     its INT4 form: per group of 64 elements, scale = fp16(absmax / 7) and codes
 //     clamp(rint(x / scale), -7, 7), two codes per byte (low nibble first);
-//   * block_score_kernel: per (sequence, KV head) and 64 blocks, the exp2-domain
+//   * block_score_mfma_kernel: per (sequence, KV head) and 64 blocks, the exp2-domain
 //     logits z[g][j] = sm_scale * log2(e) * q_g . key_j of every query head over the
-//     complete blocks, plus each tile's per-head (max, sum of 2^(z - max));
+//     complete blocks (an MFMA product), plus each tile's per-head (max, sum of
+//     2^(z - max));
 //   * block_select_kernel: merges the tiles' (max, sum) into each head's softmax,
 //     scores s_j = sum_g 2^(z[g][j] - max_g) / sum_g, keeps the forced blocks plus
 //     the best others (unit_select.h) and writes the kept blocks' positions; the
@@ -27,9 +28,10 @@ namespace {
 
 constexpr float BLK_LOG2E = 1.4426950408889634f;
 constexpr int BLK_TILE = 64;              // blocks per scoring workgroup
-constexpr int BLK_SLOTS = 16;             // 16-lane row slots per scoring workgroup
 constexpr int BLK_LDS_SCORES = 8192;      // block scores staged in LDS up to this many blocks
 constexpr int INT4_GROUP = 64;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Copy of new K and V rows into the caches (rows outside [0, cap) are skipped).
 __global__ __launch_bounds__(256) void kv_rows_kernel(const uint16_t* __restrict__ k_new,
@@ -94,75 +96,98 @@ __global__ __launch_bounds__(HEAD_DIM) void block_keys_kernel(
   }
 }
 
-// grid = (ceil(nblk_cap / BLK_TILE), B * H_kv), 256 threads = 16 slots of 16 lanes;
-// lane t of a slot holds dimensions 8t .. 8t+7 of a block key. INT4: the key is
-// codes (4 bytes per lane) times its group's scale.
+// grid = (ceil(nblk_cap / BLK_TILE), B * H_kv), 256 threads. The logits of a tile
+// are a matrix product, Z = Q Kc^T per 16 blocks, on v_mfma_f32_16x16x16_bf16 (16
+// heads, zero past G, by 16 blocks; bf16 products are exact, sums in fp32); wave w of
+// the workgroup takes the tile's w-th group of 16 blocks. Lane l feeds head l % 16 (A) and block l % 16 (B) with contraction
+// indices 4*(l/16)..+3 of each of 8 chunks, and receives heads 4*(l/16)..+3 of block
+// l % 16 (D). The contraction order is a permutation of the dimensions chosen so a
+// lane reads whole runs of its block's key: 32 consecutive dimensions (64 bytes) of a
+// bf16 key, or two runs of 16 (8 bytes of codes each), one per INT4 scale group,
+// whose partial products are accumulated and scaled separately.
 template <int G, bool INT4>
-__global__ __launch_bounds__(256) void block_score_kernel(
+__global__ __launch_bounds__(256) void block_score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const unsigned char* __restrict__ Kq,
     const uint16_t* __restrict__ Ks, const int32_t* __restrict__ seq_len, int n_kv_heads, int64_t cap, int bs,
     int64_t nblk_cap, float qscale, float* __restrict__ z, int64_t zstride, float* __restrict__ ms,
     int ntile) {
-  __shared__ float sq[G][HEAD_DIM];
-  __shared__ float smax[BLK_SLOTS][G];
-  __shared__ float ssum[BLK_SLOTS][G];
+  static_assert(BLK_TILE == 4 * 16, "four waves of 16 blocks per tile");
+  __shared__ float wmax[4][G], wsum[4][G];
   const int unit = blockIdx.y;
   const int b = unit / n_kv_heads;
   const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
   const int64_t m = n / bs;                     // complete blocks
-  const int tid = threadIdx.x, slot = tid >> 4, t = tid & 15;
-  const int64_t j0 = (int64_t)blockIdx.x * BLK_TILE;
-  for (int i = tid; i < G * HEAD_DIM; i += 256)
-    sq[i / HEAD_DIM][i % HEAD_DIM] = __uint_as_float((uint32_t)q[(size_t)unit * G * HEAD_DIM + i] << 16);
-  __syncthreads();
-  float mx[G], sm[G];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gq = lane >> 4, col = lane & 15;
+  const int64_t blk = (int64_t)blockIdx.x * BLK_TILE + wave * 16 + col;
+  const bool ok = blk < m;
+  const size_t row = (size_t)unit * nblk_cap + (ok ? blk : 0);
+
+  auto dim_of = [&](int c, int v) { return INT4 ? 64 * (c >> 2) + 16 * gq + 4 * (c & 3) + v : 32 * gq + 4 * c + v; };
+  s16x4 a[8];
+  const uint16_t* qh = q + ((size_t)unit * G + (col < G ? col : 0)) * HEAD_DIM;
 #pragma unroll
-  for (int g = 0; g < G; ++g) { mx[g] = -INFINITY; sm[g] = 0.f; }
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-  for (int r = 0; r < BLK_TILE / BLK_SLOTS; ++r) {
-    const int64_t j = j0 + r * BLK_SLOTS + slot;
-    const bool ok = j < m;
-    const size_t row = (size_t)unit * nblk_cap + (ok ? j : 0);
-    float kv[8];
-    if (INT4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(Kq + row * (HEAD_DIM / 2) + t * 4);
-      const float scale = (float)__builtin_bit_cast(_Float16, Ks[row * (HEAD_DIM / INT4_GROUP) + t / 8]);
+    for (int v = 0; v < 4; ++v) a[c][v] = col < G ? (short)qh[dim_of(c, v)] : (short)0;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!INT4) {
+    u32x4 w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int code = ((int)(w << (28 - 4 * e))) >> 28;      // sign-extended nibble e
-        kv[e] = (float)code * scale;
-      }
-    } else {
-      const u32x4 w = ld16(Kc + row * HEAD_DIM + t * 8);
-      kv[0] = bf_lo(w.x); kv[1] = bf_hi(w.x); kv[2] = bf_lo(w.y); kv[3] = bf_hi(w.y);
-      kv[4] = bf_lo(w.z); kv[5] = bf_hi(w.z); kv[6] = bf_lo(w.w); kv[7] = bf_hi(w.w);
+    for (int i = 0; i < 4; ++i) w[i] = ld16(Kc + row * HEAD_DIM + 32 * gq + 8 * i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 x = w[c >> 1];
+      const uint32_t lo = (c & 1) ? x.z : x.x, hi = (c & 1) ? x.w : x.y;
+      s16x4 bv;
+      bv[0] = (short)(lo & 0xffffu); bv[1] = (short)(lo >> 16); bv[2] = (short)(hi & 0xffffu); bv[3] = (short)(hi >> 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[c], bv, acc, 0, 0, 0);
     }
+  } else {
+    const unsigned char* cr = Kq + row * (HEAD_DIM / 2);
+    const uint2 p0 = *reinterpret_cast<const uint2*>(cr + 8 * gq);          // dims 16gq .. 16gq+15
+    const uint2 p1 = *reinterpret_cast<const uint2*>(cr + 32 + 8 * gq);     // dims 64+16gq ..
+    const uint16_t sc0 = Ks[row * (HEAD_DIM / INT4_GROUP)], sc1 = Ks[row * (HEAD_DIM / INT4_GROUP) + 1];
+    f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float a = 0.f;
+    for (int c = 0; c < 8; ++c) {
+      const uint2 p = c < 4 ? p0 : p1;
+      const uint32_t word = ((c & 3) < 2) ? p.x : p.y;
+      s16x4 bv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a = fmaf(sq[g][t * 8 + e], kv[e], a);
-      a = row16_sum(a) * qscale;
-      if (ok) {
-        if (t == g) z[((size_t)unit * G + g) * zstride + j] = a;
-        const float nm = fmaxf(mx[g], a);
-        sm[g] = sm[g] * exp2f(mx[g] - nm) + exp2f(a - nm);
-        mx[g] = nm;
+      for (int v = 0; v < 4; ++v) {
+        const int nib = 4 * (c & 1) + v;                              // nibble within the 32-bit word
+        const int code = ((int)(word << (28 - 4 * nib))) >> 28;      // sign-extended
+        bv[v] = (short)(__float_as_uint((float)code) >> 16);          // small integers are exact in bf16
       }
+      if (c < 4) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[c], bv, acc, 0, 0, 0);
+      else acc1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[c], bv, acc1, 0, 0, 0);
     }
+    const float s0 = (float)__builtin_bit_cast(_Float16, sc0), s1 = (float)__builtin_bit_cast(_Float16, sc1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = acc[v] * s0 + acc1[v] * s1;
   }
-  if (t == 0) {
+  // logits of heads 4*gq + v for this lane's block; each head's (max, sum) over the
+  // wave's 16 blocks by row reductions (a DPP row is the 16 blocks of one head group)
 #pragma unroll
-    for (int g = 0; g < G; ++g) { smax[slot][g] = mx[g]; ssum[slot][g] = sm[g]; }
+  for (int v = 0; v < 4; ++v) {
+    const int h = 4 * gq + v;
+    const float zz = ok ? acc[v] * qscale : -INFINITY;
+    if (h < G && ok) z[((size_t)unit * G + h) * zstride + blk] = zz;
+    const float mx = row16_max(zz);
+    const float e = mx == -INFINITY ? 0.f : exp2f(zz - mx);
+    const float sm = row16_sum(e);
+    if (col == 0 && h < G) { wmax[wave][h] = mx; wsum[wave][h] = sm; }
   }
   __syncthreads();
   if (tid < G) {
     float M = -INFINITY;
-    for (int s = 0; s < BLK_SLOTS; ++s) M = fmaxf(M, smax[s][tid]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wmax[w][tid]);
     float S = 0.f;
     if (M != -INFINITY)
-      for (int s = 0; s < BLK_SLOTS; ++s)
-        if (smax[s][tid] != -INFINITY) S += ssum[s][tid] * exp2f(smax[s][tid] - M);
+      for (int w = 0; w < 4; ++w)
+        if (wmax[w][tid] != -INFINITY) S += wsum[w][tid] * exp2f(wmax[w][tid] - M);
     float* o = ms + (((size_t)unit * ntile + blockIdx.x) * G + tid) * 2;
     o[0] = M;
     o[1] = S;
@@ -261,11 +286,13 @@ hipError_t launch_block_select(const sjsa_shape& s, const BlockLayout& L, int bs
     const dim3 grid((unsigned)L.ntile, (unsigned)units);
 #define SJSA_BSCORE(GG)                                                                                          \
   if (Kc)                                                                                                        \
-    block_score_kernel<GG, false><<<grid, dim3(256), 0, st>>>(q, Kc, Kq, Ks, seq_len, s.n_kv_heads, s.capacity,   \
-                                                               bs, L.nblk_cap, qscale, z, L.zstride, ms, L.ntile); \
+    block_score_mfma_kernel<GG, false><<<grid, dim3(256), 0, st>>>(q, Kc, Kq, Ks, seq_len, s.n_kv_heads,         \
+                                                                    s.capacity, bs, L.nblk_cap, qscale, z,        \
+                                                                    L.zstride, ms, L.ntile);                      \
   else                                                                                                           \
-    block_score_kernel<GG, true><<<grid, dim3(256), 0, st>>>(q, Kc, Kq, Ks, seq_len, s.n_kv_heads, s.capacity,    \
-                                                              bs, L.nblk_cap, qscale, z, L.zstride, ms, L.ntile)
+    block_score_mfma_kernel<GG, true><<<grid, dim3(256), 0, st>>>(q, Kc, Kq, Ks, seq_len, s.n_kv_heads,          \
+                                                                   s.capacity, bs, L.nblk_cap, qscale, z,         \
+                                                                   L.zstride, ms, L.ntile)
     switch (s.group) {
       case 1: SJSA_BSCORE(1); break;
       case 2: SJSA_BSCORE(2); break;
