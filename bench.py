@@ -2,11 +2,12 @@
 """Benchmark one sparse decode step of the 128K batched-decode workload on one MI355X.
 
 A step is the whole hot path on one batch: append the current token (K, V and its
-projected scoring row, done by the prep kernel), scoring prep, the full-context
-score scan, per-KV-head top-k, and gather-free attention with the split merge. Inputs are resident in HBM
+projected scoring row), scoring prep and the full-context score scan (one launch:
+the prep workgroups hand q_hat and the threshold to the scan workgroups), per-KV-head
+top-k, and gather-free attention with the split merge. Inputs are resident in HBM
 before timing starts. Throughput comes from steps run back to back between one
 pair of events; a second timed pass brackets every stage with HIP events on the
-stream the kernels run on, which gives the scan kernel's own duration.
+stream the kernels run on, which gives the prep + scan kernel's own duration.
 
 Prints one JSON line. Default: --gpus 1 --steps 200 --warmup 20.
 """
@@ -27,8 +28,9 @@ if ROOT not in sys.path:
 WORKLOAD = ("long-batched decode step: batch 16, 32 query / 8 KV heads (G=4), d=128, n=131072 cached tokens "
             "per sequence, scoring rank r=32, budget k=4096; bf16 K/V with RoPE (base 500000) and 1% heavy "
             "hitters (key x4), random orthonormal basis per KV head, 8 query sets cycled")
-PMC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_long_batched_pmc.json")
-SCAN_SOURCES = [os.path.join(ROOT, "token_level_sparse_kv_amd", "csrc", f) for f in ("score.hip", "sjsa_device.h")]
+PMC_FILE = os.path.join(ROOT, "profiles", "prep_scan_kernel_long_batched_pmc.json")
+SCAN_SOURCES = [os.path.join(ROOT, "token_level_sparse_kv_amd", "csrc", f)
+                for f in ("score.hip", "sjsa_device.h", "key_proj.h")]
 
 
 def source_hash(paths):
@@ -51,8 +53,8 @@ def copy_calibration(nbytes: int, reps: int):
 
 
 def traffic_from_profile(scan_bytes_per_launch):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
-    taken on the current scan kernel source; else None."""
+    """HBM bytes per prep + scan launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
     try:
         with open(PMC_FILE) as f:
             p = json.load(f)
@@ -131,8 +133,7 @@ def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, 
 
     def step(i):
         q = q_sets[i % q_sets.shape[0]]
-        sj.prep_append(shape, k_new, v_new, pos_new, q, K, V, M, Kp8, seq_len, k, ws)
-        sj.scan(shape, Kp8, seq_len, ws)
+        sj.prep_scan(shape, q, M, Kp8, seq_len, k, ws, k_new=k_new, v_new=v_new, pos=pos_new, K=K, V=V)
         sj.select(shape, Kp8, seq_len, k, ws, idx=idx)
         sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
 
@@ -411,23 +412,20 @@ def main():
     t_setup = time.time() - t_setup
 
     def step(i, ev=None):
-        # the stage calls of sjsa_decode_step_append: the prep kernel appends the new
-        # token (K, V and projected rows), then scan, select, attend + merge
+        # the stage calls of sjsa_decode_step_append: one launch appends the new token
+        # (K, V and projected rows), preps and scans; then select, attend + merge
         q = q_sets[i % q_sets.shape[0]]
         if ev is not None:
             ev[0].record()
-        sj.prep_append(shape, k_new, v_new, pos_new, q, K, V, M, Kp, seq_len, k, ws)
+        sj.prep_scan(shape, q, M, Kp, seq_len, k, ws, k_new=k_new, v_new=v_new, pos=pos_new, K=K, V=V)
         if ev is not None:
             ev[1].record()
-        sj.scan(shape, Kp, seq_len, ws)
-        if ev is not None:
-            ev[2].record()
         sj.select(shape, Kp, seq_len, k, ws, idx=idx)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
         sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
@@ -448,18 +446,19 @@ def main():
     # stages, all on the stream the kernels run on (torch's current stream); each
     # interval also holds the launch latency of its first kernel, so these figures
     # slightly overstate the kernels' own durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    names = ["append+prep", "scan", "select", "attend"]
+    names = ["append+prep+scan", "select", "attend"]
     stage_ms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, nm in enumerate(names)}
 
     tb = step_bytes(B, Hkv, G, d, r, n, k)
     gbs = tb["total"] / (ms_per_step * 1e-3) / 1e9
-    scan_bytes = tb["scan_kproj"]
-    scan_gbs = scan_bytes / (stage_ms["scan"] * 1e-3) / 1e9
+    # the prep + scan launch moves the projected cache, q, M and the appended rows
+    scan_bytes = tb["scan_kproj"] + tb["q"] + tb["M"] + tb["append"]
+    scan_gbs = scan_bytes / (stage_ms["append+prep+scan"] * 1e-3) / 1e9
     traffic = traffic_from_profile(scan_bytes)
 
     line = {
@@ -481,7 +480,8 @@ def main():
         "hbm_frac_of_peak": round(gbs / MI355X_HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": tb["total"],
         "stage_us": {kk: round(v * 1000.0, 2) for kk, v in stage_ms.items()},
-        "roofline": {"kernel": "score scan (score_kernel<32,2>)", "bound": "hbm", "achieved": round(scan_gbs, 1),
+        "roofline": {"kernel": "prep + score scan (prep_scan_kernel<32,2,true>)", "bound": "hbm",
+                     "achieved": round(scan_gbs, 1), "bytes_per_launch": scan_bytes,
                      "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / MI355X_HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},

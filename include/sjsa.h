@@ -35,7 +35,9 @@
  *     failed check returns a negative status and enqueues nothing. A launch
  *     failure reported by the HIP runtime returns SJSA_ERR_HIP.
  *   - Calls that share a workspace must not overlap (use one stream or order
- *     them); the library keeps no global mutable state.
+ *     them). The library's only global mutable state is a launch counter that
+ *     tags what the prep workgroups of a fused launch hand to its scan
+ *     workgroups, and that hand-over's wait limit (see sjsa_prep_scan).
  *   - Results are deterministic: identical inputs give bit-identical outputs.
  */
 #ifndef SJSA_H
@@ -176,6 +178,29 @@ int sjsa_prep_append(const sjsa_shape* shape, const void* k_new, const void* v_n
                      void* stream);
 int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, void* workspace,
               size_t workspace_bytes, void* stream);
+/* Stages 1+2 as the decode steps run them: sjsa_prep (or, with k_new non-NULL,
+ * sjsa_prep_append with k_new, v_new, pos, K, V as there) and sjsa_scan in one
+ * launch, whose scan workgroups take q_hat, the threshold and the appended row
+ * from the prep workgroups as soon as each is published (a workgroup that waits
+ * more than about 200 us marks its tile unusable and sjsa_select then handles
+ * that unit exactly). Results are those of the separate calls. It must be
+ * followed by sjsa_select on the same workspace before the next call of this
+ * function there (the workspace carries each unit's step count between calls,
+ * which sjsa_select advances; it needs no initialisation). With
+ * SJSA_FLAG_WRITE_SCORES it makes the two separate launches.
+ * Errors: as sjsa_prep_append (K, V, Kproj and pos are checked only when k_new is
+ * non-NULL). */
+int sjsa_prep_scan(const sjsa_shape* shape, const void* q, const float* M, void* Kproj,
+                   const int32_t* seq_len, int32_t k, const void* k_new, const void* v_new,
+                   const int32_t* pos, void* K, void* V, void* workspace, size_t workspace_bytes,
+                   void* stream);
+/* The longest a scan workgroup of sjsa_prep_scan (and of the decode steps, which
+ * use it) waits for what its unit's prep publishes, in microseconds, for launches
+ * made after the call (default 200; negative values count as 0). Past the limit
+ * the tile is marked unusable and sjsa_select recomputes the unit exactly, so
+ * results never depend on it; 0 exercises that path. Returns the previous limit.
+ * Process-wide; safe to call from any thread. */
+int32_t sjsa_set_fused_wait_us(int32_t microseconds);
 
 /* Stage 3: top-k per (b, h) from what sjsa_score left in the workspace -> idx
  * [B, H_kv, k] (Kproj is read again only for a unit whose sampled threshold

@@ -1,7 +1,8 @@
 """MI355X-native JSSA token-level sparse decode: hand-written HIP kernels for
 gfx950 behind the C ABI in include/sjsa.h, with a thin ctypes binding."""
 from .sjsa import (SjsaError, Shape, make_shape, shape_of, workspace_size, alloc_workspace,  # noqa: F401
-                   scores_view, append_kv, decode_step, decode_step_append, score, prep, prep_append, scan,
+                   scores_view, append_kv, decode_step, decode_step_append, score, prep, prep_append, scan, prep_scan,
+                   set_fused_wait_us,
                    select, topk, attend, gated_decode_step, gated_workspace, gated_shape,
                    block_cache, block_keys, block_append, block_workspace, block_decode_step,
                    calib_accumulate, calib_workspace, calib_basis, lib, LIB_PATH,

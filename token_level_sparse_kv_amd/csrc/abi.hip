@@ -58,6 +58,10 @@ Layout make_layout(const sjsa_shape& s, int k) {
   off = align_up(off + (size_t)L.units * QHAT_STRIDE * sizeof(float), WS_ALIGN);
   L.off_tlow = off;
   off = align_up(off + (size_t)L.units * 2 * sizeof(uint32_t), WS_ALIGN);
+  L.off_epoch = off;
+  off = align_up(off + (size_t)L.units * sizeof(uint32_t), WS_ALIGN);
+  L.off_sync = off;
+  off = align_up(off + (size_t)L.units * SYNC_WORDS * sizeof(uint64_t), WS_ALIGN);
   L.off_counts = off;
   off = align_up(off + (size_t)L.units * L.ntile_cap * sizeof(uint64_t), WS_ALIGN);
   L.off_cand = off;
@@ -271,6 +275,27 @@ int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len
                                 (hipStream_t)stream));
 }
 
+int sjsa_prep_scan(const sjsa_shape* shape, const void* q, const float* M, void* Kproj, const int32_t* seq_len,
+                   int32_t k, const void* k_new, const void* v_new, const int32_t* pos, void* K, void* V,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (k_new && (st = check_append_one(k_new, v_new, pos, K, V, Kproj))) return st;
+  if (!q || !M || !Kproj || !seq_len || !workspace) return SJSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(M, 16) || !aligned(Kproj, 16) || !aligned(seq_len, 4) ||
+      !aligned(workspace, WS_ALIGN))
+    return SJSA_ERR_ALIGN;
+  if (k_new && (!aligned(K, 16) || !aligned(V, 16))) return SJSA_ERR_ALIGN;
+  const Layout L = make_layout(*shape, k);
+  if (workspace_bytes < L.scores_end) return SJSA_ERR_WORKSPACE;
+  const PrepAppend ap = make_append(k_new, v_new, pos, K, V, Kproj);
+  return status_of(launch_prep_scan(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k,
+                                    (unsigned char*)workspace, (hipStream_t)stream, k_new ? &ap : nullptr));
+}
+
+int32_t sjsa_set_fused_wait_us(int32_t microseconds) { return set_fused_wait_us(microseconds); }
+
 int sjsa_select(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, int32_t k, int32_t* idx,
                 void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
@@ -335,8 +360,7 @@ int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, cons
   if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s);
-  if (e == hipSuccess) e = launch_score(*shape, L, (const void*)Kproj, seq_len, ws, s);
+  hipError_t e = launch_prep_scan(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s);
   if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const void*)Kproj, seq_len, k, idx, ws, s);
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
@@ -362,8 +386,7 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const PrepAppend ap = make_append(k_new, v_new, pos, K, V, Kproj);
-  hipError_t e = launch_prep(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s, &ap);
-  if (e == hipSuccess) e = launch_score(*shape, L, (const void*)Kproj, seq_len, ws, s);
+  hipError_t e = launch_prep_scan(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k, ws, s, &ap);
   if (e == hipSuccess) e = launch_select(*shape, L, nullptr, 0, (const void*)Kproj, seq_len, k, idx, ws, s);
   if (e == hipSuccess)
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,

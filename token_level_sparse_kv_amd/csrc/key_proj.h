@@ -35,9 +35,14 @@ struct KeyProj {
   // element i of a projected row in the cache format: bf16 (KB = 2, nearest even) or
   // OCP FP8 E4M3 (KB = 1, nearest even, saturating)
   template <int KB>
+  __device__ static uint32_t encode(float v) {
+    if constexpr (KB == 2) return f32_to_bf16_rne(v);
+    else return f32_to_fp8_sat(v);
+  }
+  template <int KB>
   __device__ static void store(unsigned char* row, int i, float v) {
-    if constexpr (KB == 2) reinterpret_cast<uint16_t*>(row)[i] = (uint16_t)f32_to_bf16_rne(v);
-    else row[i] = (unsigned char)f32_to_fp8_sat(v);
+    if constexpr (KB == 2) reinterpret_cast<uint16_t*>(row)[i] = (uint16_t)encode<KB>(v);
+    else row[i] = (unsigned char)encode<KB>(v);
   }
   // combined dot (valid in the lane with t % TPO == 0); every lane of the wave calls
   __device__ static float dot(const f32x4 (&mv)[CH / 4], const u32x4 (&kv)[CH / 8]) {

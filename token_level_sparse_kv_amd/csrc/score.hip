@@ -7,34 +7,107 @@
 // becomes sparse. Section 组件级拆解 names the stages: scoring prep, candidate
 // scoring, top-k selection, sparse attention.
 //
-// prep_kernel  (one workgroup per (b, h)): q_bar in fp32 (sum in head order, then
-//              divide by G), q_hat = M_h q_bar (fp32), and the unit's candidate
-//              threshold, placed from the scores of evenly spaced sample rows.
-// score_kernel (grid = tiles x units): streams Kproj rows with 128-bit coalesced
-//              loads, each lane holding 8 of a row's r values; the partial dots of
-//              the r/8 lanes of a row are reduced with DPP lane moves in a
-//              transposed pattern, so that after the reduction each lane owns the
-//              full score of one row. Rows whose score key reaches the threshold
-//              are kept as candidates for the top-k stage (and, on request, every
-//              score is stored).
+// prep  (one workgroup per (b, h)): q_bar in fp32 (sum in head order, then divide
+//       by G), q_hat = M_h q_bar (fp32), and the unit's candidate threshold, placed
+//       from the scores of evenly spaced sample rows.
+// scan  (one workgroup per 4096-row tile of a unit): streams Kproj rows with
+//       128-bit coalesced loads, each lane holding 8 of a row's r values; the
+//       partial dots of the r/8 lanes of a row are reduced with DPP lane moves in a
+//       transposed pattern, so that after the reduction each lane owns the full
+//       score of one row. Rows whose score key reaches the threshold are kept as
+//       candidates for the top-k stage (and, on request, every score is stored).
+//
+// The two run as separate kernels (prep_kernel, score_kernel) or as one
+// (prep_scan_kernel): its first B*H_kv workgroups do the prep of one unit each and
+// publish q_hat, the threshold and the appended token's projected row as tagged
+// 64-bit words; the scan workgroups read q_hat as soon as it is published, stream
+// and score their whole tile, and only then need the threshold, so the prep runs
+// under the scan's memory stream instead of before it.
+#include <atomic>
+
 #include "key_proj.h"
 
 namespace sjsa {
 namespace {
 
-constexpr int PREP_THREADS = 512;
-constexpr int PREP_WAVES = PREP_THREADS / 64;
 constexpr int SCORE_THREADS = 256;
 constexpr int SCORE_WAVES = SCORE_THREADS / 64;
 constexpr int GROUP_ROWS = 64;       // rows covered by r/8 wave-wide 16-byte loads
-// rows scored by the prep kernel to place the threshold: more samples give a tighter
-// threshold (fewer candidates) but cost the prep kernel about as much time as the
-// later stages save (measured with 4096 at the 128K batch-16 shape)
-template <int R>
-constexpr int samples_for() { return 2048; }
+constexpr int SCORE_UNROLL = 2;      // groups per segment
+constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
+constexpr int STASH = TILE_ROWS / SCORE_WAVES;    // keys of one wave's rows of a tile
+// rows scored by the prep to place the threshold: more samples give a tighter
+// threshold (fewer candidates) but cost the prep about as much time as the later
+// stages save (measured with 4096 at the 128K batch-16 shape)
+constexpr int PREP_SAMPLES = 2048;
+constexpr int PREP_PASS = 1;         // sample batches per load pass (bounds the registers)
 constexpr int PREP_BINS = 4096;      // linear score bins of the threshold histogram
+constexpr uint32_t TAG_MULT = 0x9E3779B1u;
+// A scan wave waits at most this long for a published word (microseconds; 200 by
+// default, far above a prep's duration); past it the tile reports TILE_OVERFLOW and
+// the selection recomputes the unit exactly. The device's real-time counter runs at
+// 100 MHz.
+std::atomic<int32_t> g_wait_us{200};
+constexpr uint64_t TICKS_PER_US = 100;
 
-// Block-wide (PREP_THREADS) inclusive scan of one u32 per thread; the block total
+static_assert(SEG_ROWS == GROUP_ROWS * SCORE_UNROLL, "one wave iteration covers one segment");
+static_assert(SEGS_PER_TILE <= 64, "one wave scans the segment counts");
+
+// Tag of the words one launch publishes for a unit: the step count of the unit on
+// this workspace (advanced by the selection) and a per-launch number from the host,
+// so words left by an earlier launch never carry the current tag.
+__device__ __forceinline__ uint32_t launch_tag(const uint32_t* epoch, int unit, uint32_t nonce) {
+  return (epoch[unit] + 1u) * TAG_MULT + nonce;
+}
+
+__device__ __forceinline__ void publish(uint64_t* w, uint32_t tag, uint32_t v) {
+  __hip_atomic_store(w, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-wide wait for tagged words: lane l < nw reads w[l] until every one of them
+// carries `tag` (its value then goes to v) or `deadline` passes (returns false; the
+// outcome is uniform over the wave).
+__device__ __forceinline__ bool poll_words(const uint64_t* w, int nw, uint32_t tag, uint64_t deadline,
+                                           uint32_t& v) {
+  const int lane = threadIdx.x & 63;
+  for (;;) {
+    const uint64_t x = lane < nw ? __hip_atomic_load(w + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : (uint64_t)tag << 32;
+    if (!__any((uint32_t)(x >> 32) != tag)) {
+      v = (uint32_t)x;
+      return true;
+    }
+    if (__builtin_readsteadycounter() > deadline) return false;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+struct PrepShared {
+  uint32_t hist[PREP_BINS];
+  uint32_t qraw[8][64];      // the G query rows (bf16 pairs)
+  float qh[64];
+  float red[2 * SCORE_WAVES];
+  uint32_t scan[SCORE_WAVES];
+  uint32_t misc[4];
+  uint32_t row[32];          // the appended token's projected row
+};
+
+struct ScanShared {
+  uint32_t stash[SCORE_WAVES][STASH];   // a wave's keys, then its candidates (compacted in place)
+  uint32_t segcnt[SEGS_PER_TILE];
+  uint32_t segoff[SEGS_PER_TILE + 1];
+  uint32_t sstart[SEGS_PER_TILE];
+  uint32_t overflow[SCORE_WAVES];
+  uint32_t wmax[SCORE_WAVES];
+  alignas(16) uint32_t words[SCORE_WAVES][64];  // published words, as each wave read them
+};
+
+union ScoreShared {
+  PrepShared p;
+  ScanShared s;
+};
+
+// Block-wide (SCORE_THREADS) inclusive scan of one u32 per thread; the block total
 // goes to *total. Two barriers.
 __device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -43,7 +116,7 @@ __device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < PREP_WAVES; ++w) {
+  for (int w = 0; w < SCORE_WAVES; ++w) {
     const uint32_t t = scan_lds[w];
     before += w < wave ? t : 0u;
     tot += t;
@@ -62,117 +135,138 @@ __device__ __forceinline__ int64_t sample_row(int s, int64_t n) {
   return 2 * (((int64_t)(s >> 1) * n) / NS) + (s & 1);
 }
 
-// One workgroup per (b, h).
+struct PrepArgs {
+  const uint16_t* q;
+  const float* M;
+  const unsigned char* kproj;
+  const int32_t* seq_len;
+  int k;
+  float* qhat;
+  uint32_t* tlow;
+  int n_kv_heads;
+  int group;
+  int64_t cap;
+};
+
+// Prep of one unit (b, h), 256 threads.
 //  * q_bar in fp32 (sum in head order, then divide by G) and q_hat = M_h q_bar: output
 //    i is split over 16 lanes of 8 channels each (fp32 partial dots, DPP row sum).
-//  * Threshold for the scan: the scores of NS rows (NS = samples_for<R>(), evenly
-//    spaced pairs of adjacent rows; all rows when n <= NS) are binned linearly
-//    between their least and greatest finite value (+inf in the top bin, -inf and
-//    NaN left out); the bin that holds the sample of rank m (see below) is found,
-//    and the least key in it becomes the unit's candidate threshold, so at least m
-//    samples reach it. The exact top k is among
-//    the rows that reach it unless the sample misjudges the distribution, a case the
-//    select stage detects and handles exactly: the threshold only decides how much
-//    work the select stage does, never its result.
-//  * mode: 1 when k >= n (every position is selected and the scan has no work).
-// The sample rows are loaded first, so their latency overlaps the q_hat work.
-//
-// With APPEND the workgroup first appends its unit's new token (decode: one token
-// per sequence at slot pos[b]): threads 256..287 copy its K and V rows and threads
-// 0..255 write its projected row with the KeyProj layout (bit-identical to the
-// append kernel). A sample that lands on that slot may read the row before or
-// after the write; either way only the threshold moves, never the result.
-template <int R, int KB, bool APPEND>
-__global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ M, const unsigned char* kproj,
-    const int32_t* __restrict__ seq_len, int k, float* __restrict__ qhat, uint32_t* __restrict__ tlow,
-    int n_kv_heads, int group, int64_t cap, PrepAppend ap) {
+//  * Threshold for the scan: the scores of NS rows (evenly spaced pairs of adjacent
+//    rows; all rows when n <= NS) are binned linearly between their least and
+//    greatest finite value (+inf in the top bin, -inf and NaN left out); the bin
+//    that holds the sample of rank m (see below) is found, and the least key in it
+//    becomes the unit's candidate threshold, so at least m samples reach it. The
+//    exact top k is among the rows that reach it unless the sample misjudges the
+//    distribution, a case the select stage detects and handles exactly: the
+//    threshold only decides how much work the select stage does, never its result.
+//  * tlow[2u + 1] = 1 when k >= n (every position is selected; the scan has no work).
+// With APPEND the unit's new token (decode: one token per sequence at slot pos[b]) is
+// appended first: threads 0..31 copy its K and V rows and all threads compute its
+// projected row with the KeyProj layout (bit-identical to the append kernel). A sample
+// that lands on that slot may read the row before or after the write; either way only
+// the threshold moves, never the result.
+// PUBLISH: q_hat, the appended row and the threshold are also published as tagged
+// words (sync) for the scan workgroups of the same launch.
+template <int R, int KB, bool APPEND, bool PUBLISH>
+__device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepArgs& a, const PrepAppend& ap,
+                                          uint64_t* sync, uint32_t tag) {
   constexpr int LPR = R * KB / 16;                    // 16-byte words per Kproj row
   constexpr int VPC = 16 / KB;                        // values per 16-byte word
   constexpr int RPL = 64 / LPR;                       // samples per wave-wide load
-  constexpr int NS = samples_for<R>();
-  constexpr int BATCHES = NS / PREP_THREADS;          // 64-sample batches per wave (= samples per lane)
-  constexpr int OUTS = (R * 16 + PREP_THREADS - 1) / PREP_THREADS;   // q_hat outputs per thread
-  __shared__ float sqh[R];
-  __shared__ uint32_t shist[PREP_BINS];
-  __shared__ float sred[2 * PREP_WAVES];
-  __shared__ uint32_t sscan[PREP_WAVES];
-  __shared__ uint32_t smisc[4];
-  const int unit = blockIdx.x;
-  const int b = unit / n_kv_heads;
-  const int h = unit - b * n_kv_heads;
+  constexpr int NS = PREP_SAMPLES;
+  constexpr int BATCHES = NS / SCORE_THREADS;         // 64-sample batches per wave (= samples per lane)
+  constexpr int OUTS = R * 16 / SCORE_THREADS;        // q_hat outputs per thread
+  constexpr int RW = R * KB / 4;                      // 32-bit words of a projected row
+  static_assert(BATCHES % PREP_PASS == 0 && R * 16 % SCORE_THREADS == 0, "prep work divides evenly");
+  const int b = unit / a.n_kv_heads;
+  const int h = unit - b * a.n_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t* sw = sync + (size_t)unit * SYNC_WORDS;
 
-  using KP = KeyProj<R>;
-  static_assert(KP::THREADS + 32 <= PREP_THREADS, "projection and row copies fit the workgroup");
-  f32x4 amv[KP::CH / 4];
-  u32x4 akv[KP::CH / 8];
-  int64_t apos = -1;
-  if constexpr (APPEND) {
-    apos = ap.pos[b];
-    const uint16_t* krow = ap.k_new + (size_t)unit * HEAD_DIM;
-    if (tid < KP::THREADS) {
-      KP::load_basis(M + (size_t)h * R * HEAD_DIM, tid, amv);
-      KP::load_key(krow, tid, akv);
-    } else if (tid < KP::THREADS + 32 && apos >= 0 && apos < cap) {
-      const int part = tid & 15;
-      const bool is_v = (tid - KP::THREADS) >= 16;
-      const u32x4 x = ld16((is_v ? ap.v_new : ap.k_new) + (size_t)unit * HEAD_DIM + part * 8);
-      *reinterpret_cast<u32x4*>((is_v ? ap.V : ap.K) + ((size_t)unit * cap + apos) * HEAD_DIM + part * 8) = x;
+  // the query rows: thread (g, part) of the first 128 loads 16 bytes of head g (heads
+  // past G repeat the last; they are never read)
+  const int part = tid & 15;
+  u32x4 qw = {0u, 0u, 0u, 0u};
+  if (tid < 128) qw = ld16(a.q + ((size_t)unit * a.group + min(tid >> 4, a.group - 1)) * HEAD_DIM + part * 8);
+  // this thread's slices of the basis rows of its q_hat outputs (loaded up front where
+  // the registers allow, so that q_hat, which the scan workgroups wait for, follows
+  // the first barrier at once)
+  constexpr bool EARLY_M = OUTS <= 2;
+  auto m_slice = [&](int o) {
+    return reinterpret_cast<const f32x4*>(a.M + ((size_t)h * R + tid / 16 + o * (SCORE_THREADS / 16)) * HEAD_DIM +
+                                          part * 8);
+  };
+  f32x4 mq[EARLY_M ? OUTS : 1][2];
+  if constexpr (EARLY_M) {
+#pragma unroll
+    for (int o = 0; o < OUTS; ++o) {
+      mq[o][0] = m_slice(o)[0];
+      mq[o][1] = m_slice(o)[1];
     }
   }
 
-  const int64_t n = min((int64_t)max(seq_len[b], 0), cap);
-  const int64_t kk = min((int64_t)k, n);
-  const bool sampling = kk < n;                       // uniform over the workgroup
-  const int S = (int)min((int64_t)NS, n);
-
-  // sample s sits in row pos(s) (evenly spaced); wave-wide loads as in the scan: in
-  // batch t a wave covers samples sb .. sb + 63 (sb = 64 * (wave + t * PREP_WAVES)),
-  // load i reading 16 bytes (lane column p) of sample sb + i * RPL + rs, so the LPR
-  // lanes of a sample read its row contiguously
-  const int p = lane % LPR, rs = lane / LPR;
-  u32x4 w[BATCHES][LPR];
-  if (sampling) {
-    const unsigned char* base = kproj + (size_t)unit * cap * R * KB + p * 16;
-#pragma unroll
-    for (int t = 0; t < BATCHES; ++t) {
-#pragma unroll
-      for (int i = 0; i < LPR; ++i) {
-        const int sidx = min(64 * (wave + t * PREP_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
-        const int64_t pos = sample_row<NS>(sidx, n);
-        w[t][i] = ld16_stream(base + pos * R * KB);
+  if constexpr (APPEND) {
+    using KP = KeyProj<R>;
+    static_assert(KP::THREADS == SCORE_THREADS, "one projection output per lane group");
+    const int64_t apos = ap.pos[b];
+    const bool in_range = apos >= 0 && apos < a.cap;
+    f32x4 amv[KP::CH / 4];
+    u32x4 akv[KP::CH / 8];
+    KP::load_basis(a.M + (size_t)h * R * HEAD_DIM, tid, amv);
+    KP::load_key(ap.k_new + (size_t)unit * HEAD_DIM, tid, akv);
+    if (tid < 32 && in_range) {
+      const int cp = tid & 15;
+      const bool is_v = tid >= 16;
+      const u32x4 x = ld16((is_v ? ap.v_new : ap.k_new) + (size_t)unit * HEAD_DIM + cp * 8);
+      *reinterpret_cast<u32x4*>((is_v ? ap.V : ap.K) + ((size_t)unit * a.cap + apos) * HEAD_DIM + cp * 8) = x;
+    }
+    const float acc = KP::dot(amv, akv);             // whole waves: the DPP combine needs them
+    if (tid % KP::TPO == 0) {
+      const int i = tid / KP::TPO;
+      const uint32_t bits = KP::template encode<KB>(acc);
+      if (in_range) {
+        unsigned char* row = ap.Kproj + ((size_t)unit * a.cap + apos) * R * KB;
+        if constexpr (KB == 2) reinterpret_cast<uint16_t*>(row)[i] = (uint16_t)bits;
+        else row[i] = (unsigned char)bits;
+      }
+      if constexpr (PUBLISH) {
+        if constexpr (KB == 2) reinterpret_cast<uint16_t*>(sh.row)[i] = (uint16_t)bits;
+        else reinterpret_cast<unsigned char*>(sh.row)[i] = (unsigned char)bits;
       }
     }
+  }
+  if (tid < 128) {
+    sh.qraw[tid >> 4][part * 4 + 0] = qw.x;
+    sh.qraw[tid >> 4][part * 4 + 1] = qw.y;
+    sh.qraw[tid >> 4][part * 4 + 2] = qw.z;
+    sh.qraw[tid >> 4][part * 4 + 3] = qw.w;
+  }
+  for (int i = tid; i < PREP_BINS; i += SCORE_THREADS) sh.hist[i] = 0u;
+  if (tid == 0) sh.misc[0] = 0xffffffffu;
+  __syncthreads();
+  if constexpr (APPEND && PUBLISH) {
+    if (tid < RW) publish(sw + SYNC_ROW + tid, tag, sh.row[tid]);
   }
 
   // q_bar for channels 8*part .. 8*part + 7 (every lane of a 16-lane row computes it)
-  const int part = tid & 15;
   float qbar[8];
-  {
-    const uint16_t* qg = q + (size_t)unit * group * HEAD_DIM + part * 8;
-    u32x4 qw[8];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) qw[g] = ld16(qg + (size_t)min(g, group - 1) * HEAD_DIM);
+  for (int c = 0; c < 8; ++c) qbar[c] = 0.f;
+  for (int g = 0; g < a.group; ++g) {
+    const uint32_t* w = &sh.qraw[g][part * 4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qbar[c] = 0.f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      if (g < group) {
-        qbar[0] += bf_lo(qw[g].x); qbar[1] += bf_hi(qw[g].x);
-        qbar[2] += bf_lo(qw[g].y); qbar[3] += bf_hi(qw[g].y);
-        qbar[4] += bf_lo(qw[g].z); qbar[5] += bf_hi(qw[g].z);
-        qbar[6] += bf_lo(qw[g].w); qbar[7] += bf_hi(qw[g].w);
-      }
+    for (int c = 0; c < 4; ++c) {
+      qbar[2 * c] += bf_lo(w[c]);
+      qbar[2 * c + 1] += bf_hi(w[c]);
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qbar[c] = qbar[c] / (float)group;
   }
 #pragma unroll
+  for (int c = 0; c < 8; ++c) qbar[c] = qbar[c] / (float)a.group;
+#pragma unroll
   for (int o = 0; o < OUTS; ++o) {
-    const int i = tid / 16 + o * (PREP_THREADS / 16);
-    const f32x4* m4 = reinterpret_cast<const f32x4*>(M + ((size_t)h * R + min(i, R - 1)) * HEAD_DIM + part * 8);
-    const f32x4 m0 = m4[0], m1 = m4[1];
+    const int i = tid / 16 + o * (SCORE_THREADS / 16);
+    const f32x4 m0 = EARLY_M ? mq[EARLY_M ? o : 0][0] : m_slice(o)[0];
+    const f32x4 m1 = EARLY_M ? mq[EARLY_M ? o : 0][1] : m_slice(o)[1];
     float acc = m0.x * qbar[0];
     acc = fmaf(m0.y, qbar[1], acc);
     acc = fmaf(m0.z, qbar[2], acc);
@@ -182,66 +276,86 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     acc = fmaf(m1.z, qbar[6], acc);
     acc = fmaf(m1.w, qbar[7], acc);
     acc = row16_sum(acc);
-    if (part == 0 && i < R) {
-      qhat[(size_t)unit * QHAT_STRIDE + i] = acc;
-      sqh[i] = acc;
+    if (part == 0) {
+      a.qhat[(size_t)unit * QHAT_STRIDE + i] = acc;
+      sh.qh[i] = acc;
+      if constexpr (PUBLISH) publish(sw + i, tag, __float_as_uint(acc));
     }
-  }
-  if constexpr (APPEND) {
-    if (tid < KP::THREADS) {                          // whole waves: the DPP combine needs them
-      const float acc = KP::dot(amv, akv);
-      if (tid % KP::TPO == 0 && apos >= 0 && apos < cap)
-        KP::template store<KB>(ap.Kproj + ((size_t)unit * cap + apos) * R * KB, tid / KP::TPO, acc);
-    }
-  }
-  for (int i = tid; i < PREP_BINS; i += PREP_THREADS) shist[i] = 0u;
-  if (tid == 0) smisc[0] = 0xffffffffu;
-  __syncthreads();
-  if (!sampling) {        // take every position (also n = 0): no threshold needed
-    if (tid == 0) { tlow[unit * 2] = 0u; tlow[unit * 2 + 1] = 1u; }
-    return;
   }
 
-  // lane (rs, p) scores its VPC columns of the LPR rows of a batch; the transposed
-  // reduction leaves it the score of sample sb + p * RPL + rs
+  const int64_t n = min((int64_t)max(a.seq_len[b], 0), a.cap);
+  const int64_t kk = min((int64_t)a.k, n);
+  if (!(kk < n)) {        // take every position (also n = 0): no threshold needed
+    if (tid == 0) {
+      a.tlow[unit * 2] = 0u;
+      a.tlow[unit * 2 + 1] = 1u;
+      if constexpr (PUBLISH) publish(sw + SYNC_THR, tag, 0u);
+    }
+    return;
+  }
+  __syncthreads();                                    // sh.qh complete
+  const int S = (int)min((int64_t)NS, n);
+
+  // sample s sits in row pos(s) (evenly spaced); wave-wide loads as in the scan: in
+  // batch t a wave covers samples sb .. sb + 63 (sb = 64 * (wave + t * waves)), load
+  // i reading 16 bytes (lane column p) of sample sb + i * RPL + rs, so the LPR lanes
+  // of a sample read its row contiguously; the lane is left the score of sample
+  // sb + p * RPL + rs by the transposed reduction
+  const int p = lane % LPR, rs = lane / LPR;
   float qh[VPC];
 #pragma unroll
-  for (int e = 0; e < VPC; ++e) qh[e] = sqh[p * VPC + e];
+  for (int e = 0; e < VPC; ++e) qh[e] = sh.qh[p * VPC + e];
+  const unsigned char* base = a.kproj + (size_t)unit * a.cap * R * KB + p * 16;
   float sc[BATCHES];
-  int sid[BATCHES];
   float lo = __builtin_inff(), hi = -__builtin_inff();
 #pragma unroll
-  for (int t = 0; t < BATCHES; ++t) {
-    float a[LPR];
+  for (int t0 = 0; t0 < BATCHES; t0 += PREP_PASS) {
+    u32x4 w[PREP_PASS][LPR];
 #pragma unroll
-    for (int i = 0; i < LPR; ++i) a[i] = dot_chunk<KB>(qh, w[t][i]);
-    sc[t] = transpose_reduce<LPR>(a, p);
-    sid[t] = 64 * (wave + t * PREP_WAVES) + p * RPL + rs;
-    if (sid[t] < S && __builtin_isfinite(sc[t])) {
-      lo = fminf(lo, sc[t]);
-      hi = fmaxf(hi, sc[t]);
+    for (int t = 0; t < PREP_PASS; ++t) {
+#pragma unroll
+      for (int i = 0; i < LPR; ++i) {
+        const int sidx = min(64 * (wave + (t0 + t) * SCORE_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
+        w[t][i] = ld16_stream(base + sample_row<NS>(sidx, n) * R * KB);
+      }
     }
+#pragma unroll
+    for (int t = 0; t < PREP_PASS; ++t) {
+      float d[LPR];
+#pragma unroll
+      for (int i = 0; i < LPR; ++i) d[i] = dot_chunk<KB>(qh, w[t][i]);
+      const float s = transpose_reduce<LPR>(d, p);
+      sc[t0 + t] = s;
+      const int sid = 64 * (wave + (t0 + t) * SCORE_WAVES) + p * RPL + rs;
+      if (sid < S && __builtin_isfinite(s)) {
+        lo = fminf(lo, s);
+        hi = fmaxf(hi, s);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);                // one pass of loads in flight at a time
   }
   lo = wave_min_f32(lo);
   hi = wave_max_f32(hi);
-  if (lane == 0) { sred[wave] = lo; sred[PREP_WAVES + wave] = hi; }
+  if (lane == 0) { sh.red[wave] = lo; sh.red[SCORE_WAVES + wave] = hi; }
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < PREP_WAVES; ++v) {
-    lo = fminf(lo, sred[v]);
-    hi = fmaxf(hi, sred[PREP_WAVES + v]);
+  for (int v = 0; v < SCORE_WAVES; ++v) {
+    lo = fminf(lo, sh.red[v]);
+    hi = fmaxf(hi, sh.red[SCORE_WAVES + v]);
   }
   const float scale = hi > lo ? (float)PREP_BINS / (hi - lo) : 0.f;
-  int bin[BATCHES];
+  // bin of sample t of this lane (-1: not binned)
+  auto bin_of = [&](int t) {
+    const float x = sc[t];
+    const int sid = 64 * (wave + t * SCORE_WAVES) + p * RPL + rs;
+    if (sid >= S || x != x || x == -__builtin_inff()) return -1;
+    const float f = (x - lo) * scale;                         // +inf -> top bin
+    return f > 0.f ? (int)fminf(f, (float)(PREP_BINS - 1)) : 0;
+  };
 #pragma unroll
   for (int t = 0; t < BATCHES; ++t) {
-    const float x = sc[t];
-    bin[t] = -1;
-    if (sid[t] < S && !(x != x) && x != -__builtin_inff()) {
-      const float f = (x - lo) * scale;                       // +inf -> top bin; NaN -> bin 0
-      bin[t] = f > 0.f ? (int)fminf(f, (float)(PREP_BINS - 1)) : 0;
-      atomicAdd(&shist[bin[t]], 1u);
-    }
+    const int bt = bin_of(t);
+    if (bt >= 0) atomicAdd(&sh.hist[bt], 1u);
   }
   __syncthreads();
   // the number of samples at or above the true k-th key is Binomial(S, kk/n): taking
@@ -251,83 +365,97 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
   const double mu = (double)S * pk;
   int64_t m = (int64_t)ceil(mu + 5.0 * sqrt(mu * (1.0 - pk)) + 4.0);
   m = m < 1 ? 1 : (m > S ? S : m);
-  constexpr int BPT = PREP_BINS / PREP_THREADS;
+  constexpr int BPT = PREP_BINS / SCORE_THREADS;
   const int b0 = tid * BPT;
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) local += shist[b0 + i];
+  for (int i = 0; i < BPT; ++i) local += sh.hist[b0 + i];
   uint32_t total;
-  const uint32_t inc = prep_block_scan(local, sscan, &total);
+  const uint32_t inc = prep_block_scan(local, sh.scan, &total);
   uint32_t above = total - inc;                 // samples in bins above this thread's bins
   const uint32_t mm = (uint32_t)m;
   if (above < mm && mm <= above + local) {
     for (int i = BPT - 1; i >= 0; --i) {
-      const uint32_t c = shist[b0 + i];
-      if (above + c >= mm) { smisc[1] = (uint32_t)(b0 + i); break; }
+      const uint32_t c = sh.hist[b0 + i];
+      if (above + c >= mm) { sh.misc[1] = (uint32_t)(b0 + i); break; }
       above += c;
     }
   }
   __syncthreads();
   if (total >= mm) {
-    const int bsel = (int)smisc[1];
+    const int bsel = (int)sh.misc[1];
 #pragma unroll
     for (int t = 0; t < BATCHES; ++t)
-      if (bin[t] == bsel) atomicMin(&smisc[0], score_key(sc[t]));
+      if (bin_of(t) == bsel) atomicMin(&sh.misc[0], score_key(sc[t]));
   }
   __syncthreads();
   // fewer than m binned samples (most scores NaN or -inf): every row is a candidate
-  if (tid == 0) { tlow[unit * 2] = total >= mm ? smisc[0] : 0u; tlow[unit * 2 + 1] = 0u; }
+  if (tid == 0) {
+    const uint32_t thr = total >= mm ? sh.misc[0] : 0u;
+    a.tlow[unit * 2] = thr;
+    a.tlow[unit * 2 + 1] = 0u;
+    if constexpr (PUBLISH) publish(sw + SYNC_THR, tag, thr);
+  }
 }
 
-// grid = (ceil(cap / TILE_ROWS), B * H_kv). A segment is the SEG_ROWS = 128 rows
-// one wave covers in one iteration (UNROLL groups of 64); the waves of a workgroup
-// take the tile's segments in turn (wave w: segments w, w + 4, ...), so the
-// workgroup streams one contiguous region. Loads are 128-bit and coalesced, each
-// lane holding 8 of a row's r values; the partial dots of the r/8 lanes of a row
-// are reduced with DPP lane moves in a transposed pattern, after which lane (rs, p)
-// owns the score of group row p*RPL + rs.
+struct ScanArgs {
+  const unsigned char* kproj;
+  const float* qhat;
+  const uint32_t* tlow;
+  const int32_t* seq_len;
+  int k;
+  float* scores;
+  uint32_t* cand;
+  uint64_t* counts;
+  int n_kv_heads;
+  int64_t cap;
+  int64_t stride;
+  int64_t ntile_cap;
+  int64_t cand_stride;
+};
+
+// Scan of tile `tile` (rows [tile*TILE_ROWS, +TILE_ROWS)) of one unit, 256 threads.
+// A segment is the SEG_ROWS = 128 rows one wave covers in one iteration
+// (SCORE_UNROLL groups of 64); the waves take the tile's segments in turn (wave w:
+// segments w, w + 4, ...), so the workgroup streams one contiguous region. Loads are
+// 128-bit and coalesced, each lane holding 8 of a row's r values; the partial dots of
+// the r/8 lanes of a row are reduced with DPP lane moves in a transposed pattern,
+// after which lane (rs, p) owns the score of group row p*RPL + rs.
 //
-// Rows whose key reaches the unit's threshold are candidates, kept as 32-bit entries
-// (the key's top 20 bits, the row's offset in its tile; see cand_entry) in position
-// order: with a ballot of the flags in lane order, the number of
-// flagged rows before a row is the popcount of the ballot under a per-lane mask of
+// Each wave first scores all its rows into a private LDS stash (one key per row);
+// then it takes the threshold and keeps the rows whose key reaches it as candidates,
+// 32-bit entries (the key's top 20 bits, the row's offset in its tile; see
+// cand_entry) in position order: with a ballot of the flags in lane order, the number
+// of flagged rows before a row is the popcount of the ballot under a per-lane mask of
 // the lanes that hold earlier rows (earlier lane columns, and this column above this
-// lane). Each wave packs the candidates of its segments back to back into a
-// wave-private LDS stage and records each segment's count. At the end the
-// workgroup writes the tile's candidates, in position order, to its region of the
-// candidate buffer (entries [x*TILE_ROWS, ...) for tile x), and to counts[x] their
-// number (low word; TILE_OVERFLOW when a wave had more than CAND_STAGE) and their
-// greatest key (high word; 0 when there are none); writes in the
-// middle of the stream cost far more HBM time than their size. With WRITE_DENSE
-// every score is also stored.
-template <int R, int KB, int UNROLL, bool WRITE_DENSE>
-__global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
-    const unsigned char* __restrict__ kproj, const float* __restrict__ qhat, const uint32_t* __restrict__ tlow,
-    const int32_t* __restrict__ seq_len, float* __restrict__ scores, uint32_t* __restrict__ cand,
-    uint64_t* __restrict__ counts, int n_kv_heads, int64_t cap, int64_t stride, int64_t ntile_cap,
-    int64_t cand_stride) {
+// lane). The candidates are compacted in place over the stash (a segment's entries
+// land no later than its own keys, which are read first). At the end the workgroup
+// writes the tile's candidates, in position order, to its region of the candidate
+// buffer (entries [x*TILE_ROWS, ...) for tile x), and to counts[x] their number (low
+// word; TILE_OVERFLOW when a published word did not arrive in time) and their
+// greatest key (high word; 0 when there are none); writes in the middle of the
+// stream cost far more HBM time than their size. With WRITE_DENSE every score is
+// also stored.
+// POLL: q_hat and the threshold come from the unit's prep in the same launch (tagged
+// words); apos (may be null) gives the slot of each sequence's appended token, whose
+// projected row is taken from the published words rather than from memory.
+template <int R, int KB, bool WRITE_DENSE, bool POLL>
+__device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, const ScanArgs& a,
+                                          const uint64_t* sync, uint32_t tag, const int32_t* apos_b,
+                                          uint64_t wait_ticks) {
+  static_assert(!(WRITE_DENSE && POLL), "dense scores come from the two-launch form");
   constexpr int LPR = R * KB / 16;      // lanes per Kproj row (16 bytes each)
   constexpr int VPC = 16 / KB;          // values per 16-byte word
   constexpr int RPL = 64 / LPR;         // rows per wave-wide load
-  static_assert(GROUP_ROWS * UNROLL == SEG_ROWS, "one wave iteration covers one segment");
-  static_assert(TILE_ROWS / SEG_ROWS <= 64, "one wave scans the segment counts");
-  constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
-  __shared__ uint32_t stage[SCORE_WAVES][CAND_STAGE];
-  __shared__ uint32_t segcnt[SEGS_PER_TILE];
-  __shared__ uint32_t segoff[SEGS_PER_TILE + 1];
-  __shared__ uint32_t sstart[SEGS_PER_TILE];
-  __shared__ uint32_t overflow[SCORE_WAVES];
-  __shared__ uint32_t wmax[SCORE_WAVES];
-  const int unit = blockIdx.y;
-  const int b = unit / n_kv_heads;
-  const int n = (int)min((int64_t)max(seq_len[b], 0), cap);      // cap < 2^30
+  constexpr int RW = R * KB / 4;        // 32-bit words of a projected row
+  const int b = unit / a.n_kv_heads;
+  const int n = (int)min((int64_t)max(a.seq_len[b], 0), a.cap);      // cap < 2^30
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int seg0 = blockIdx.x * SEGS_PER_TILE;
+  const int seg0 = tile * SEGS_PER_TILE;
   if (seg0 * SEG_ROWS >= n) return;            // the whole tile lies past the end
-  const bool take_all = tlow[unit * 2 + 1] != 0u;
+  const bool take_all = POLL ? a.k >= n : a.tlow[unit * 2 + 1] != 0u;
   if (take_all && !WRITE_DENSE) return;
-  const uint32_t tkey = tlow[unit * 2];
   const int p = lane % LPR;
   const int rs = lane / LPR;
   // lanes holding rows before this lane's row p*RPL + rs
@@ -336,118 +464,274 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
   for (int i = 0; i < RPL; ++i) col0 |= 1ull << (i * LPR);
   const uint64_t earlier = col0 * ((1ull << p) - 1) | ((col0 << p) & ((1ull << (LPR * rs)) - 1));
 
+  const uint64_t* sw = sync + (size_t)unit * SYNC_WORDS;
+  uint64_t deadline = 0;
+  int apos = -1;
   float qh[VPC];
+  if constexpr (POLL) {
+    deadline = __builtin_readsteadycounter() + wait_ticks;
+    if (apos_b) {
+      const int64_t ap = apos_b[b];
+      if (ap >= (int64_t)tile * TILE_ROWS && ap < (int64_t)(tile + 1) * TILE_ROWS && ap < a.cap) apos = (int)ap;
+    }
+  } else {
 #pragma unroll
-  for (int e = 0; e < VPC; ++e) qh[e] = qhat[(size_t)unit * QHAT_STRIDE + p * VPC + e];
+    for (int e = 0; e < VPC; ++e) qh[e] = a.qhat[(size_t)unit * QHAT_STRIDE + p * VPC + e];
+  }
 
-  const unsigned char* base = kproj + (size_t)unit * cap * R * KB + p * 16;
-  float* srow = scores + (size_t)unit * stride;
+  const unsigned char* base = a.kproj + (size_t)unit * a.cap * R * KB + p * 16;
+  float* srow = a.scores + (size_t)unit * a.stride;
+  uint32_t* stash = sh.stash[wave];
   const int last = n - 1;
+  bool ok = true;                          // published words arrived
+  // loads of the segment starting at row g0: rows past the end are clamped to the last
+  // valid row (never reported), so every load is unconditional and the whole batch
+  // stays in flight
+  auto load_seg = [&](int g0, u32x4 (&w)[SCORE_UNROLL][LPR]) {
+#pragma unroll
+    for (int u = 0; u < SCORE_UNROLL; ++u) {
+#pragma unroll
+      for (int i = 0; i < LPR; ++i)
+        w[u][i] = ld16_stream(base + (size_t)min(g0 + u * GROUP_ROWS + i * RPL + rs, last) * R * KB);
+    }
+  };
+  // scores of the segment into stash slot `slot` (its keys, one per row)
+  auto score_seg = [&](int g0, int slot, const u32x4 (&w)[SCORE_UNROLL][LPR]) {
+#pragma unroll
+    for (int u = 0; u < SCORE_UNROLL; ++u) {
+      float d[LPR];
+#pragma unroll
+      for (int i = 0; i < LPR; ++i) d[i] = dot_chunk<KB>(qh, w[u][i]);
+      const float s = transpose_reduce<LPR>(d, p);
+      if (WRITE_DENSE) {
+        const int row = g0 + u * GROUP_ROWS + p * RPL + rs;
+        if (row < n) srow[row] = s;
+      }
+      stash[SEG_ROWS * slot + GROUP_ROWS * u + lane] = score_key(s);
+    }
+  };
+  int nseg = 0;
+  int j = wave;
+  if constexpr (POLL) {
+    // first segment: q_hat is polled while its loads are in flight
+    const int g0 = (seg0 + j) * SEG_ROWS;
+    if (g0 < n) {
+      u32x4 w[SCORE_UNROLL][LPR];
+      load_seg(g0, w);
+      uint32_t v;
+      ok = poll_words(sw, R, tag, deadline, v);
+      if (ok) {
+        if (lane < R) sh.words[wave][lane] = v;
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) qh[e] = __uint_as_float(sh.words[wave][p * VPC + e]);
+        score_seg(g0, 0, w);
+        nseg = 1;
+        j += SCORE_WAVES;
+      }
+    }
+  }
+  if (ok) {
+    for (; j < SEGS_PER_TILE; j += SCORE_WAVES, ++nseg) {
+      const int g0 = (seg0 + j) * SEG_ROWS;
+      if (g0 >= n) break;
+      u32x4 w[SCORE_UNROLL][LPR];
+      load_seg(g0, w);
+      score_seg(g0, nseg, w);
+    }
+  }
+
+  if constexpr (POLL) {
+    // the appended token's row (if it falls in a segment this wave scored): its key
+    // from the published bytes, not from memory, which the prep may not have written
+    // yet. The chunk dots of lanes 0..LPR-1 are added in the balanced tree of the
+    // transposed reduction, so the key is the one the scan would have computed.
+    const int ja = apos - seg0 * SEG_ROWS;               // row offset in the tile (< 0: none)
+    const int jseg = ja >> 7;                            // segment of the tile (SEG_ROWS = 128)
+    if (ok && ja >= 0 && apos < n && (jseg & (SCORE_WAVES - 1)) == wave) {
+      uint32_t v;
+      ok = poll_words(sw + SYNC_ROW, RW, tag, deadline, v);
+      if (ok) {
+        if (lane < RW) sh.words[wave][lane] = v;
+        const u32x4 chunk = *reinterpret_cast<const u32x4*>(&sh.words[wave][4 * p]);
+        float x = dot_chunk<KB>(qh, chunk);
+        if constexpr (LPR >= 2) x += dpp<DPP_QUAD_XOR1>(x);
+        if constexpr (LPR >= 4) x += dpp<DPP_QUAD_XOR2>(x);
+        if constexpr (LPR >= 8) x += swz_xor4(x);
+        const int r_in = ja & (SEG_ROWS - 1);            // row in its segment
+        const int u = r_in / GROUP_ROWS, rg = r_in % GROUP_ROWS;
+        const int owner = (rg % RPL) * LPR + rg / RPL;   // the lane whose score is that row's
+        if (lane == 0) stash[SEG_ROWS * (jseg / SCORE_WAVES) + GROUP_ROWS * u + owner] = score_key(x);
+      }
+    }
+  }
+  uint32_t tkey = 0;
+  if (ok && !take_all && nseg > 0) {
+    if constexpr (POLL) {
+      ok = poll_words(sw + SYNC_THR, 1, tag, deadline, tkey);
+      tkey = readlane_u32(tkey, 0);
+    } else {
+      tkey = a.tlow[unit * 2];
+    }
+  }
   uint32_t wcount = 0;                     // candidates of this wave so far
   uint32_t kmax = 0;                       // greatest candidate key seen by this lane
-
-  int j = wave;
-  for (; j < SEGS_PER_TILE; j += SCORE_WAVES) {
-    const int g0 = (seg0 + j) * SEG_ROWS;
-    if (g0 >= n) break;
-    u32x4 w[UNROLL][LPR];
+  int filtered = 0;
+  if (ok && !take_all) {
+    for (; filtered < nseg; ++filtered) {
+      const int j = wave + filtered * SCORE_WAVES;
+      const int g0 = (seg0 + j) * SEG_ROWS;
+      uint32_t key[SCORE_UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
+      for (int u = 0; u < SCORE_UNROLL; ++u) key[u] = stash[SEG_ROWS * filtered + GROUP_ROWS * u + lane];
+      uint32_t count = 0;
 #pragma unroll
-      for (int i = 0; i < LPR; ++i) {
-        // rows past the end are clamped to the last valid row (never reported), so
-        // every load is unconditional and the whole batch stays in flight
-        const int row = min(g0 + u * GROUP_ROWS + i * RPL + rs, last);
-        w[u][i] = ld16_stream(base + (size_t)row * R * KB);
+      for (int u = 0; u < SCORE_UNROLL; ++u) {
+        const int row = g0 + u * GROUP_ROWS + p * RPL + rs;
+        const bool c = row < n && key[u] >= tkey;
+        const uint64_t m = __ballot(c);
+        if (c) {
+          stash[wcount + count + (uint32_t)__popcll(m & earlier)] = cand_entry(key[u], row);
+          kmax = max(kmax, key[u]);
+        }
+        count += (uint32_t)__popcll(m);
       }
+      if (lane == 0) sh.segcnt[j] = count;
+      wcount += count;
     }
-    uint32_t count = 0;
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      float a[LPR];
-#pragma unroll
-      for (int i = 0; i < LPR; ++i) a[i] = dot_chunk<KB>(qh, w[u][i]);
-      const float s = transpose_reduce<LPR>(a, p);
-      const int row = g0 + u * GROUP_ROWS + p * RPL + rs;
-      const bool valid = row < n;
-      if (WRITE_DENSE && valid) srow[row] = s;
-      const uint32_t key = score_key(s);
-      const bool c = valid && !take_all && key >= tkey;
-      const uint64_t m = __ballot(c);
-      if (c) {
-        const uint32_t at = wcount + count + (uint32_t)__popcll(m & earlier);
-        if (at < (uint32_t)CAND_STAGE) stage[wave][at] = cand_entry(key, row);
-        kmax = max(kmax, key);
-      }
-      count += (uint32_t)__popcll(m);
-    }
-    if (lane == 0) segcnt[j] = count;
-    wcount += count;
   }
   kmax = wave_max_u32(kmax);
   if (lane == 0) {
-    for (; j < SEGS_PER_TILE; j += SCORE_WAVES) segcnt[j] = 0u;    // segments past the end
-    overflow[wave] = wcount > (uint32_t)CAND_STAGE ? 1u : 0u;
-    wmax[wave] = kmax;
+    for (int j = wave + filtered * SCORE_WAVES; j < SEGS_PER_TILE; j += SCORE_WAVES) sh.segcnt[j] = 0u;
+    sh.overflow[wave] = ok ? 0u : 1u;
+    sh.wmax[wave] = kmax;
   }
   __syncthreads();
   // the tile's candidates in position order: segment jj's entries start at
   // segoff[jj] (the counts of segments 0 .. jj-1) in the output and at sstart[jj]
-  // (the counts of the same wave's earlier segments) in its wave's stage
+  // (the counts of the same wave's earlier segments) in its wave's stash
   if (wave == 0) {
-    const uint32_t c = lane < SEGS_PER_TILE ? segcnt[lane] : 0u;
+    const uint32_t c = lane < SEGS_PER_TILE ? sh.segcnt[lane] : 0u;
     const uint32_t inc = wave_incl_scan(c);
     if (lane < SEGS_PER_TILE) {
-      segoff[lane + 1] = inc;
+      sh.segoff[lane + 1] = inc;
       uint32_t st = 0;
-      for (int q = lane % SCORE_WAVES; q < lane; q += SCORE_WAVES) st += segcnt[q];
-      sstart[lane] = st;
+      for (int q = lane % SCORE_WAVES; q < lane; q += SCORE_WAVES) st += sh.segcnt[q];
+      sh.sstart[lane] = st;
     }
-    if (lane == 0) segoff[0] = 0u;
+    if (lane == 0) sh.segoff[0] = 0u;
   }
   __syncthreads();
   bool ovf = false;
 #pragma unroll
-  for (int v = 0; v < SCORE_WAVES; ++v) ovf = ovf || overflow[v] != 0u;
-  const uint32_t tot = segoff[SEGS_PER_TILE];
+  for (int v = 0; v < SCORE_WAVES; ++v) ovf = ovf || sh.overflow[v] != 0u;
+  const uint32_t tot = sh.segoff[SEGS_PER_TILE];
   if (!ovf) {
     // every thread writes entries e, e + 256, ...: coalesced, streamed past the caches
-    uint32_t* wtile = cand + (size_t)unit * cand_stride + (size_t)blockIdx.x * TILE_ROWS;
+    uint32_t* wtile = a.cand + (size_t)unit * a.cand_stride + (size_t)tile * TILE_ROWS;
     for (uint32_t e = threadIdx.x; e < tot; e += SCORE_THREADS) {
       int lo = 0, hi = SEGS_PER_TILE;            // the segment holding entry e
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (segoff[mid] <= e) lo = mid; else hi = mid;
+        if (sh.segoff[mid] <= e) lo = mid; else hi = mid;
       }
-      __builtin_nontemporal_store(stage[lo % SCORE_WAVES][sstart[lo] + (e - segoff[lo])], wtile + e);
+      __builtin_nontemporal_store(sh.stash[lo % SCORE_WAVES][sh.sstart[lo] + (e - sh.segoff[lo])], wtile + e);
     }
   }
   if (threadIdx.x == 0) {
     uint32_t tmax = 0;
 #pragma unroll
-    for (int v = 0; v < SCORE_WAVES; ++v) tmax = max(tmax, wmax[v]);
-    counts[(size_t)unit * ntile_cap + blockIdx.x] = ((uint64_t)tmax << 32) | (ovf ? TILE_OVERFLOW : tot);
+    for (int v = 0; v < SCORE_WAVES; ++v) tmax = max(tmax, sh.wmax[v]);
+    a.counts[(size_t)unit * a.ntile_cap + tile] = ((uint64_t)tmax << 32) | (ovf ? TILE_OVERFLOW : tot);
   }
 }
 
-constexpr int SCORE_UNROLL = 2;
+// grid = B * H_kv
+template <int R, int KB, bool APPEND>
+__global__ __launch_bounds__(SCORE_THREADS) void prep_kernel(PrepArgs a, PrepAppend ap) {
+  __shared__ PrepShared sh;
+  prep_body<R, KB, APPEND, false>(sh, blockIdx.x, a, ap, nullptr, 0u);
+}
+
+// grid = (ceil(cap / TILE_ROWS), B * H_kv)
+template <int R, int KB, bool WRITE_DENSE>
+__global__ __launch_bounds__(SCORE_THREADS) void score_kernel(ScanArgs a) {
+  __shared__ ScanShared sh;
+  scan_body<R, KB, WRITE_DENSE, false>(sh, blockIdx.y, blockIdx.x, a, nullptr, 0u, nullptr, 0u);
+}
+
+// Waves per SIMD the fused kernel is compiled for: the most at which both roles fit
+// their registers without spilling (8, as the scan alone runs, for bf16 rows with
+// r <= 32); left to the compiler, the prep role's registers would set a lower one.
+template <int R, int KB>
+constexpr int fused_waves() { return R <= 32 ? (KB == 2 ? 8 : 7) : (KB == 2 ? 5 : 6); }
+
+// grid = B*H_kv + B*H_kv * ntile_cap, one-dimensional: workgroups [0, units) are the
+// preps (dispatched first), then the scan tiles unit by unit.
+template <int R, int KB, bool APPEND>
+__global__ __launch_bounds__(SCORE_THREADS) __attribute__((amdgpu_waves_per_eu(fused_waves<R, KB>()))) void prep_scan_kernel(PrepArgs pa, PrepAppend ap, ScanArgs sa,
+                                                                  uint64_t* sync, const uint32_t* epoch,
+                                                                  int units, uint32_t nonce, uint64_t wait_ticks) {
+  __shared__ ScoreShared sh;
+  const int64_t bid = blockIdx.x;
+  if (bid < units) {
+    const int unit = (int)bid;
+    prep_body<R, KB, APPEND, true>(sh.p, unit, pa, ap, sync, launch_tag(epoch, unit, nonce));
+  } else {
+    const int64_t id = bid - units;
+    const int unit = (int)(id / sa.ntile_cap);
+    const int tile = (int)(id - (int64_t)unit * sa.ntile_cap);
+    scan_body<R, KB, false, true>(sh.s, unit, tile, sa, sync, launch_tag(epoch, unit, nonce),
+                                  APPEND ? ap.pos : nullptr, wait_ticks);
+  }
+}
+
+PrepArgs prep_args(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
+                   const unsigned char* kproj, const int32_t* seq_len, int k, unsigned char* ws) {
+  PrepArgs a;
+  a.q = q;
+  a.M = M;
+  a.kproj = kproj;
+  a.seq_len = seq_len;
+  a.k = k;
+  a.qhat = reinterpret_cast<float*>(ws + L.off_qhat);
+  a.tlow = reinterpret_cast<uint32_t*>(ws + L.off_tlow);
+  a.n_kv_heads = s.n_kv_heads;
+  a.group = s.group;
+  a.cap = s.capacity;
+  return a;
+}
+
+ScanArgs scan_args(const sjsa_shape& s, const Layout& L, const unsigned char* kproj, const int32_t* seq_len,
+                   int k, unsigned char* ws) {
+  ScanArgs a;
+  a.kproj = kproj;
+  a.qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
+  a.tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
+  a.seq_len = seq_len;
+  a.k = k;
+  a.scores = reinterpret_cast<float*>(ws + L.off_scores);
+  a.cand = reinterpret_cast<uint32_t*>(ws + L.off_cand);
+  a.counts = reinterpret_cast<uint64_t*>(ws + L.off_counts);
+  a.n_kv_heads = s.n_kv_heads;
+  a.cap = s.capacity;
+  a.stride = L.score_stride;
+  a.ntile_cap = L.ntile_cap;
+  a.cand_stride = L.cand_stride;
+  return a;
+}
 
 }  // namespace
 
 hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
                        const void* kproj_v, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
                        const PrepAppend* ap) {
-  const unsigned char* kproj = static_cast<const unsigned char*>(kproj_v);
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
-  float* qhat = reinterpret_cast<float*>(ws + L.off_qhat);
-  uint32_t* tlow = reinterpret_cast<uint32_t*>(ws + L.off_tlow);
-  const dim3 grid((unsigned)L.units), block(PREP_THREADS);
+  const PrepArgs a = prep_args(s, L, q, M, static_cast<const unsigned char*>(kproj_v), seq_len, k, ws);
+  const dim3 grid((unsigned)L.units), block(SCORE_THREADS);
   const PrepAppend none{};
-#define SJSA_PREP2(RR, KB)                                                                              \
-  if (ap) prep_kernel<RR, KB, true><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads, \
-                                                              s.group, s.capacity, *ap);                   \
-  else prep_kernel<RR, KB, false><<<grid, block, 0, st>>>(q, M, kproj, seq_len, k, qhat, tlow, s.n_kv_heads,  \
-                                                            s.group, s.capacity, none)
+#define SJSA_PREP2(RR, KB)                                                             \
+  if (ap) prep_kernel<RR, KB, true><<<grid, block, 0, st>>>(a, *ap);                   \
+  else prep_kernel<RR, KB, false><<<grid, block, 0, st>>>(a, none)
 #define SJSA_PREP(RR) if (fp8) { SJSA_PREP2(RR, 1); } else { SJSA_PREP2(RR, 2); }
   switch (s.rank) {
     case 16: SJSA_PREP(16); break;
@@ -462,19 +746,11 @@ hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, 
 
 hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj_v, const int32_t* seq_len,
                         unsigned char* ws, hipStream_t st) {
-  const unsigned char* kproj = static_cast<const unsigned char*>(kproj_v);
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
-  const float* qhat = reinterpret_cast<const float*>(ws + L.off_qhat);
-  const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
-  float* scores = reinterpret_cast<float*>(ws + L.off_scores);
-  uint32_t* cand = reinterpret_cast<uint32_t*>(ws + L.off_cand);
-  uint64_t* counts = reinterpret_cast<uint64_t*>(ws + L.off_counts);
-  const dim3 grid((unsigned)((s.capacity + TILE_ROWS - 1) / TILE_ROWS), (unsigned)L.units), block(SCORE_THREADS);
+  const ScanArgs a = scan_args(s, L, static_cast<const unsigned char*>(kproj_v), seq_len, 0, ws);
+  const dim3 grid((unsigned)L.ntile_cap, (unsigned)L.units), block(SCORE_THREADS);
   const bool dense = (s.flags & SJSA_FLAG_WRITE_SCORES) != 0;
-#define SJSA_SCAN2(RR, KB, DD)                                                                     \
-  score_kernel<RR, KB, SCORE_UNROLL, DD><<<grid, block, 0, st>>>(kproj, qhat, tlow, seq_len, scores, cand, \
-                                                             counts, s.n_kv_heads, s.capacity,       \
-                                                             L.score_stride, L.ntile_cap, L.cand_stride)
+#define SJSA_SCAN2(RR, KB, DD) score_kernel<RR, KB, DD><<<grid, block, 0, st>>>(a)
 #define SJSA_SCAN(RR)                                              \
   if (fp8) {                                                       \
     if (dense) SJSA_SCAN2(RR, 1, true); else SJSA_SCAN2(RR, 1, false); \
@@ -491,5 +767,42 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj_
 #undef SJSA_SCAN2
   return hipGetLastError();
 }
+
+hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
+                            const void* kproj_v, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
+                            const PrepAppend* ap) {
+  const int64_t blocks = L.units * (L.ntile_cap + 1);
+  if ((s.flags & SJSA_FLAG_WRITE_SCORES) != 0 || blocks > 0x7fffffff) {
+    hipError_t e = launch_prep(s, L, q, M, kproj_v, seq_len, k, ws, st, ap);
+    return e == hipSuccess ? launch_score(s, L, kproj_v, seq_len, ws, st) : e;
+  }
+  static std::atomic<uint32_t> launches{1u};
+  const uint32_t nonce = launches.fetch_add(1u, std::memory_order_relaxed);
+  const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
+  const unsigned char* kproj = static_cast<const unsigned char*>(kproj_v);
+  const PrepArgs pa = prep_args(s, L, q, M, kproj, seq_len, k, ws);
+  const ScanArgs sa = scan_args(s, L, kproj, seq_len, k, ws);
+  uint64_t* sync = reinterpret_cast<uint64_t*>(ws + L.off_sync);
+  const uint32_t* epoch = reinterpret_cast<const uint32_t*>(ws + L.off_epoch);
+  const dim3 grid((unsigned)blocks), block(SCORE_THREADS);
+  const PrepAppend none{};
+  const int units = (int)L.units;
+  const uint64_t wait = (uint64_t)g_wait_us.load(std::memory_order_relaxed) * TICKS_PER_US;
+#define SJSA_PS2(RR, KB)                                                                                     \
+  if (ap) prep_scan_kernel<RR, KB, true><<<grid, block, 0, st>>>(pa, *ap, sa, sync, epoch, units, nonce, wait); \
+  else prep_scan_kernel<RR, KB, false><<<grid, block, 0, st>>>(pa, none, sa, sync, epoch, units, nonce, wait)
+#define SJSA_PS(RR) if (fp8) { SJSA_PS2(RR, 1); } else { SJSA_PS2(RR, 2); }
+  switch (s.rank) {
+    case 16: SJSA_PS(16); break;
+    case 32: SJSA_PS(32); break;
+    case 64: SJSA_PS(64); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SJSA_PS
+#undef SJSA_PS2
+  return hipGetLastError();
+}
+
+int32_t set_fused_wait_us(int32_t us) { return g_wait_us.exchange(us < 0 ? 0 : us); }
 
 }  // namespace sjsa

@@ -585,7 +585,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const unsigned char* __restrict__ kproj,
     const float* __restrict__ qhat, const uint32_t* __restrict__ tlow, const uint32_t* __restrict__ cand,
     const uint64_t* __restrict__ counts, float* __restrict__ dense, int64_t dense_stride, int64_t ntile_cap,
-    int64_t cand_stride) {
+    int64_t cand_stride, uint32_t* __restrict__ epoch) {
   __shared__ SelShared sh;
   const int unit = blockIdx.x;
   const int b = unit / n_kv_heads;
@@ -622,6 +622,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const bool cand_path = scores == nullptr;
   uint32_t tkey = 0;
   if (cand_path) {
+    // one more step of this unit done on this workspace: the next prep publishes
+    // under a new tag
+    if (tid == 0) epoch[unit] += 1u;
     tkey = tlow[unit * 2];
     load_chunk(0, ntile_cap);
     if (tid < R) sh.qh[tid] = qhat[(size_t)unit * QHAT_STRIDE + tid];
@@ -775,13 +778,14 @@ hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scor
   const uint64_t* counts = reinterpret_cast<const uint64_t*>(ws + L.off_counts);
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* dense = reinterpret_cast<float*>(ws + L.off_scores);
+  uint32_t* epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
   const dim3 grid((unsigned)L.units), block(SEL_THREADS);
   const unsigned char* kp = static_cast<const unsigned char*>(kproj);
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
 #define SJSA_SEL(RR, KB)                                                                                \
   select_kernel<RR, KB><<<grid, block, 0, st>>>(scores, stride, seq_len, s.n_kv_heads, s.capacity, k, idx, \
                                                 kp, qhat, tlow, cand, counts, dense, L.score_stride,      \
-                                                L.ntile_cap, L.cand_stride)
+                                                L.ntile_cap, L.cand_stride, epoch)
   switch (s.rank) {
     case 16: if (fp8) SJSA_SEL(16, 1); else SJSA_SEL(16, 2); break;
     case 32: if (fp8) SJSA_SEL(32, 1); else SJSA_SEL(32, 2); break;

@@ -15,8 +15,12 @@ constexpr int HIST_SHIFT = 20;
 constexpr int QHAT_STRIDE = 64;      // floats reserved per unit for q_hat (r <= 64)
 constexpr int SEG_ROWS = 128;        // rows per scan segment (one wave iteration)
 constexpr int TILE_ROWS = 4096;      // rows per scan workgroup; one candidate region
-constexpr int CAND_STAGE = 512;      // candidates a scan wave can stage in LDS
-constexpr uint32_t TILE_OVERFLOW = 0xffffffffu;   // tile count: a wave's stage overflowed
+constexpr uint32_t TILE_OVERFLOW = 0xffffffffu;   // tile count: the tile's candidates are not usable
+// Words a unit's prep hands to the scan workgroups of the same launch when the two
+// run as one kernel: 64-bit words (tag << 32 | value), the tag naming the launch.
+constexpr int SYNC_WORDS = 128;      // per unit
+constexpr int SYNC_THR = 64;         // word: threshold key ([0, r) hold q_hat)
+constexpr int SYNC_ROW = 96;         // words: the appended token's projected row (r*KB/4 <= 32)
 // A candidate entry holds the top CAND_KEY_BITS bits of its score key and the row's
 // offset inside its scan tile (TILE_ROWS = 2^CAND_ROW_BITS rows): the selection
 // ranks by the truncated keys and recomputes the exact score only of the entries
@@ -38,6 +42,8 @@ struct Layout {
   int64_t ntile_cap = 0;      // scan tiles per unit (capacity / TILE_ROWS, rounded up)
   int64_t cand_stride = 0;    // 4-byte candidate entries per unit (capacity rounded up to TILE_ROWS)
   size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
+  size_t off_sync = 0;        // SYNC_WORDS 64-bit words per unit
+  size_t off_epoch = 0;       // one u32 per unit: steps completed on this workspace
   size_t off_bias = 0;        // gated step: per-position logit terms
   size_t scores_end = 0, total = 0;
 };
@@ -65,6 +71,14 @@ hipError_t launch_prep(const sjsa_shape& s, const Layout& L, const uint16_t* q, 
                        const PrepAppend* ap = nullptr);
 hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj, const int32_t* seq_len,
                         unsigned char* ws, hipStream_t st);
+// prep and scan as one launch (the scan workgroups take q_hat and the threshold from
+// the prep workgroups as they are published); falls back to the two launches when the
+// one-dimensional grid would not fit or dense scores are requested.
+hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
+                            const void* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
+                            const PrepAppend* ap = nullptr);
+// Wait limit of the fused launch's scan workgroups (microseconds); returns the old one.
+int32_t set_fused_wait_us(int32_t us);
 // scores == nullptr: select from the scan's candidates in the workspace (recomputing a
 // unit's scores from kproj/qhat when needed); else exact top-k of the given dense scores.
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,

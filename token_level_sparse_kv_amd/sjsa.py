@@ -58,6 +58,9 @@ _SIGS = {
                                   _P]),
     "sjsa_prep": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
     "sjsa_scan": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_prep_scan": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "sjsa_set_fused_wait_us": (ctypes.c_int32, [ctypes.c_int32]),
     "sjsa_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
     "sjsa_attend": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_float,
                                    _P, _P, ctypes.c_size_t, _P]),
@@ -309,6 +312,29 @@ def scan(shape: Shape, Kproj, seq_len, workspace, stream=None):
     _need(seq_len, "seq_len", torch.int32, (shape.batch,))
     _check(lib().sjsa_scan(ctypes.byref(shape), _ptr(Kproj), _ptr(seq_len), _ptr(workspace), workspace.numel(),
                            _stream(stream)))
+
+
+def prep_scan(shape: Shape, q, M, Kproj, seq_len, k, workspace, k_new=None, v_new=None, pos=None, K=None, V=None,
+              stream=None):
+    """Prep and scan in one launch, as the decode steps run them; with k_new (and
+    v_new, pos, K, V) the step's new token is appended first, as prep_append does.
+    select() must follow on the same workspace before the next prep_scan()."""
+    _need(q, "q", torch.bfloat16, (shape.batch, shape.n_kv_heads * shape.group, shape.head_dim))
+    _need(M, "M", torch.float32, (shape.n_kv_heads, shape.rank, shape.head_dim))
+    _need_kproj(Kproj, (shape.batch, shape.n_kv_heads, shape.capacity, shape.rank), bool(shape.flags & SJSA_FLAG_KPROJ_FP8))
+    _need(seq_len, "seq_len", torch.int32, (shape.batch,))
+    if k_new is not None:
+        _need(K, "K", torch.bfloat16, (shape.batch, shape.n_kv_heads, shape.capacity, shape.head_dim))
+        _need(V, "V", torch.bfloat16, K.shape)
+        _append_one_checks(k_new, v_new, pos, K, M)
+    _check(lib().sjsa_prep_scan(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(Kproj), _ptr(seq_len), int(k),
+                                _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(K), _ptr(V), _ptr(workspace),
+                                workspace.numel(), _stream(stream)))
+
+
+def set_fused_wait_us(microseconds: int) -> int:
+    """Wait limit of the fused prep + scan launch's scan workgroups; returns the old one."""
+    return int(lib().sjsa_set_fused_wait_us(int(microseconds)))
 
 
 def select(shape: Shape, Kproj, seq_len, k, workspace, idx=None, stream=None):
