@@ -60,7 +60,10 @@ def traffic_from_profile(scan_bytes_per_launch):
             p = json.load(f)
     except (OSError, ValueError):
         return None
-    if p.get("source_sha256") != source_hash(SCAN_SOURCES):
+    try:
+        if p.get("source_sha256") != source_hash(SCAN_SOURCES):
+            return None
+    except OSError:
         return None
     fetch = p["fetch_kib_per_launch"] * 1024.0 / p["copy_fetch_factor"]
     write = p["write_kib_per_launch"] * 1024.0 / p["copy_write_factor"]
