@@ -206,3 +206,27 @@ def test_zero_wait_limit_falls_back_exactly():
     assert old == 200
     _same(ref, got, "zero wait")
     _oracle(wl, got, wl.q, seq, 700, False, "zero wait", [(0, 0), (2, 1), (3, 0)])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_fused_edge_lengths(fp8):
+    # capacity not a multiple of the 4096-row tile, an empty sequence, a sequence no
+    # longer than the budget (every position taken), one exactly a tile long, one whose
+    # appended slot lies past its length; fused step against the separate launches
+    seq = [0, 300, 4096, 10001, 7000]
+    pos = [5, 299, 4095, 10000, 9000]          # the last: a slot past the sequence's length
+    k = 300
+    tag = f"prep_scan edge lengths fp8={fp8}"
+    say(tag)
+    wl = workloads.gaussian(5, 2, 4, 128, 32, max(seq), k, seed=90, capacity=10001, device="cuda", seq_len=seq)
+    Kp = _cache(wl, fp8)
+    seq_len = torch.tensor(seq, dtype=torch.int32, device="cuda")
+    k_new, v_new = workloads.new_token(wl, seed=91, T=1)
+    new = (k_new, v_new, torch.tensor(pos, dtype=torch.int32, device="cuda"))
+    ref = _step(wl, Kp, wl.q, seq_len, k, "separate", new)
+    got = _step(wl, Kp, wl.q, seq_len, k, "fused", new)
+    _same(ref, got, tag)
+    ix = got[3].cpu().numpy()
+    assert np.all(ix[0] == -1)                                   # empty sequence: nothing selected
+    assert np.array_equal(ix[1, 0, :300], np.arange(300))        # n <= k: every position
+    _oracle(wl, got, wl.q, seq, k, fp8, tag, [(1, 0), (2, 1), (3, 0), (4, 1)])
