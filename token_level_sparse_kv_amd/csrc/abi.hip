@@ -416,6 +416,18 @@ int sjsa_gated_decode_step(const sjsa_shape* shape, const void* q, const void* K
   if (workspace_bytes < L.total) return SJSA_ERR_WORKSPACE;
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t s = (hipStream_t)stream;
+  if ((shape->capacity + unit_size - 1) / unit_size <= GATE_FUSED_UNITS_MAX && k_units <= GATE_FUSED_KEPT_MAX) {
+    // every attention workgroup makes its unit's selection itself: no selection launch
+    GatedSelect g;
+    g.gate_scores = gate_scores;
+    g.gate_stride = gate_stride;
+    g.unit_size = unit_size;
+    g.k_units = k_units;
+    g.lambda = lambda;
+    g.idx = idx;
+    return status_of(launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, ktok,
+                                   seq_len, resolve_scale(sm_scale), out, ws, s, nullptr, &g));
+  }
   float* bias = reinterpret_cast<float*>(ws + L.off_bias);
   hipError_t e = launch_gate_select(*shape, gate_scores, gate_stride, seq_len, unit_size, k_units, lambda, idx,
                                     bias, s);

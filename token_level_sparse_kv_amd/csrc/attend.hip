@@ -23,6 +23,7 @@
 // log-sum-exp merge.
 #include "sjsa_device.h"
 #include "sjsa_internal.h"
+#include "unit_select.h"
 
 namespace sjsa {
 namespace {
@@ -33,20 +34,50 @@ constexpr int ATT_U = 4;             // rows in flight per slot
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.f;  // log2 units a logit may exceed the softmax reference by
 
+// Gated-logit selection run by every attention workgroup of a unit (GATE form):
+// the unit scores u, the unit size, the budget in units, lambda, and where the
+// index list goes.
+struct GateArgs {
+  const float* u = nullptr;
+  int64_t ustride = 0;
+  int unit_size = 1;
+  int k_units = 1;
+  float lam = 0.f;
+  int32_t* idx_out = nullptr;
+};
+constexpr int GATE_FUSED_MAX_UNITS = GATE_FUSED_UNITS_MAX;   // unit scores staged in LDS by the GATE form
+constexpr int GATE_FUSED_MAX_KEPT = GATE_FUSED_KEPT_MAX;     // kept units the GATE form can list
+constexpr float GATE_LOG2E = 1.4426950408889634f;
+
+struct GateShared {
+  UnitSelectSharedT<ATT_THREADS, GATE_FUSED_MAX_KEPT> sel;
+  float su[GATE_FUSED_MAX_UNITS];
+  float red[2][ATT_THREADS / 64];
+};
+
 // BIAS: every index entry carries an additive exp2-domain logit term (bias, laid out
 // like idx), as the gated-logit variant needs.
-template <int G, int U, bool BIAS>
+// GATE (with BIAS): the workgroup first makes its unit's gated selection itself (the
+// same gates, selection and logit terms as gate_select_kernel, here with 256
+// threads; every split of the unit repeats it, which costs less than a launch and a
+// round trip of the index list), keeps its own chunk of the positions and their
+// terms in LDS and writes that chunk of the index list.
+template <int G, int U, bool BIAS, bool GATE = false>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ bias, const int32_t* __restrict__ seq_len,
     int n_kv_heads, int64_t cap, int k, int chunk, int nsplit, float qscale, float* __restrict__ partials,
-    void* __restrict__ out, int out_f32) {
+    void* __restrict__ out, int out_f32, GateArgs ga) {
+  static_assert(!GATE || BIAS, "the gated selection gives every entry a logit term");
+  constexpr int ACC_BYTES = SLOTS * G * HEAD_DIM * 4;
+  constexpr int RAW_BYTES = GATE && sizeof(GateShared) > ACC_BYTES ? sizeof(GateShared) : ACC_BYTES;
   __shared__ int32_t sidx[1024];
   __shared__ float sbias[BIAS ? 1024 : 1];
   __shared__ uint32_t sq2[G][HEAD_DIM / 2];     // query heads as packed bf16 pairs
   __shared__ float sm_m[SLOTS][G];
   __shared__ float sm_l[SLOTS][G];
-  __shared__ float sm_acc[SLOTS][G][HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) unsigned char sraw[RAW_BYTES];   // slot combine (GATE: selection first)
+  auto sm_acc = reinterpret_cast<float (*)[G][HEAD_DIM]>(sraw);
 
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
@@ -59,7 +90,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   const int first = split * chunk;
   const int cnt = max(0, min(chunk, k - first));
   const int32_t* ids = idx + (size_t)unit * k + first;
-  const float* bss = BIAS ? bias + (size_t)unit * k + first : nullptr;
+  const float* bss = (BIAS && !GATE) ? bias + (size_t)unit * k + first : nullptr;
   const uint16_t* Kb = K + (size_t)unit * cap * HEAD_DIM + t * 8;
   const uint16_t* Vb = V + (size_t)unit * cap * HEAD_DIM + t * 8;
 
@@ -74,21 +105,82 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       vw[u] = ld16_stream(Vb + (size_t)row * HEAD_DIM);
     }
   };
-  // the slot's first batch of rows is requested straight from the index list, before
-  // the workgroup stages the list and the queries in LDS
   int32_t j0[U];
   float b0[U];
   u32x4 kw0[U], vw0[U];
+  if constexpr (GATE) {
+    // ---- the unit's gated selection (as gate_select_kernel): normalized softmax
+    // gates from a running (max, sum of 2^((u - max) log2 e)) per thread; the current
+    // unit (the last) forced and the k_units - 1 largest other scores taken; this
+    // workgroup's chunk of the kept positions and their logit terms into LDS
+    GateShared& gs = *reinterpret_cast<GateShared*>(sraw);
+    const int nu = (int)((n + ga.unit_size - 1) / ga.unit_size);
+    const float* ug = ga.u + (size_t)unit * ga.ustride;
+    float tm = -INFINITY, ts = 0.f;
+    for (int i = tid; i < nu; i += ATT_THREADS) {
+      const float x = ug[i];
+      gs.su[i] = x;
+      const float nm = fmaxf(tm, x);
+      ts = ts * exp2f((tm - nm) * GATE_LOG2E) + exp2f((x - nm) * GATE_LOG2E);   // tm = -inf: ts = 0
+      tm = nm;
+    }
+    const float wm = wave_max_f32(tm);
+    float ws = wm == -INFINITY ? 0.f : ts * exp2f((tm - wm) * GATE_LOG2E);
+    ws = row16_sum(ws);
+    ws = readlane_f32(ws, 0) + readlane_f32(ws, 16) + readlane_f32(ws, 32) + readlane_f32(ws, 48);
+    if ((tid & 63) == 0) { gs.red[0][tid >> 6] = wm; gs.red[1][tid >> 6] = ws; }
+    __syncthreads();                            // also publishes the staged scores
+    float mx = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    j0[u] = slot * U + u < cnt ? ids[slot * U + u] : -1;
-    b0[u] = (BIAS && slot * U + u < cnt) ? bss[slot * U + u] : 0.f;
-  }
-  load_rows(j0, kw0, vw0);
+    for (int w = 0; w < ATT_THREADS / 64; ++w) mx = fmaxf(mx, gs.red[0][w]);
+    float sm = 0.f;
+#pragma unroll
+    for (int w = 0; w < ATT_THREADS / 64; ++w)
+      sm += gs.red[0][w] == -INFINITY ? 0.f : gs.red[1][w] * exp2f((gs.red[0][w] - mx) * GATE_LOG2E);
+    const float lse2 = log2f(sm);
+    const int cur = nu - 1;
+    const uint32_t nsel = select_kept_units(
+        nu, nu <= ga.k_units, ga.k_units - 1, [&](int i) { return gs.su[i]; }, [&](int i) { return i == cur; },
+        [&](int i) { return i < cur; }, gs.sel);
+    int32_t* iout = ga.idx_out + (size_t)unit * k + first;
+    for (int i = tid; i < cnt; i += ATT_THREADS) {
+      const int e = first + i;
+      const int sl = e / ga.unit_size;
+      int32_t p = -1;
+      float bt = 0.f;
+      if (sl < (int)nsel) {
+        const int ku = gs.sel.kept[sl];
+        const int64_t pos = (int64_t)ku * ga.unit_size + (e - sl * ga.unit_size);
+        if (pos < n) {
+          p = (int32_t)pos;
+          bt = ga.lam * ((gs.su[ku] - mx) * GATE_LOG2E - lse2);
+        }
+      }
+      sidx[i] = p;
+      sbias[i] = bt;
+      iout[i] = p;
+    }
+    __syncthreads();                            // the chunk is staged; sraw is free again
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      j0[u] = slot * U + u < cnt ? sidx[slot * U + u] : -1;
+      b0[u] = slot * U + u < cnt ? sbias[slot * U + u] : 0.f;
+    }
+    load_rows(j0, kw0, vw0);
+  } else {
+    // the slot's first batch of rows is requested straight from the index list, before
+    // the workgroup stages the list and the queries in LDS
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      j0[u] = slot * U + u < cnt ? ids[slot * U + u] : -1;
+      b0[u] = (BIAS && slot * U + u < cnt) ? bss[slot * U + u] : 0.f;
+    }
+    load_rows(j0, kw0, vw0);
 
-  for (int i = tid; i < cnt; i += ATT_THREADS) {
-    sidx[i] = ids[i];
-    if constexpr (BIAS) sbias[i] = bss[i];
+    for (int i = tid; i < cnt; i += ATT_THREADS) {
+      sidx[i] = ids[i];
+      if constexpr (BIAS) sbias[i] = bss[i];
+    }
   }
   // query heads kept in LDS as bf16 pairs (read per use: fewer registers, more
   // waves in flight); the exp2-domain scale is applied to each finished dot
@@ -469,17 +561,22 @@ namespace {
 template <int G>
 void launch_attend_g(const Layout& L, const uint16_t* q, const uint16_t* K, const uint16_t* V, const int32_t* idx,
                      const float* bias, int k, const int32_t* seq_len, int n_kv_heads, int64_t cap, float qscale,
-                     float* partials, void* out, int out_f32, hipStream_t st) {
+                     float* partials, void* out, int out_f32, hipStream_t st, const GateArgs* gate) {
   const dim3 grid((unsigned)L.nsplit, (unsigned)L.units), block(ATT_THREADS);
-  if (bias) {
+  if (gate) {
+    attend_kernel<G, ATT_U, true, true><<<grid, block, 0, st>>>(q, K, V, gate->idx_out, nullptr, seq_len, n_kv_heads,
+                                                                cap, k, L.chunk, L.nsplit, qscale, partials, out,
+                                                                out_f32, *gate);
+  } else if (bias) {
     attend_kernel<G, ATT_U, true><<<grid, block, 0, st>>>(q, K, V, idx, bias, seq_len, n_kv_heads, cap, k, L.chunk,
-                                                          L.nsplit, qscale, partials, out, out_f32);
+                                                          L.nsplit, qscale, partials, out, out_f32, GateArgs{});
   } else if constexpr (G == 8) {
     attend_mfma_kernel<G><<<grid, block, 0, st>>>(q, K, V, idx, seq_len, n_kv_heads, cap, k, L.chunk, L.nsplit,
                                                   qscale, partials, out, out_f32);
   } else {
     attend_kernel<G, ATT_U, false><<<grid, block, 0, st>>>(q, K, V, idx, nullptr, seq_len, n_kv_heads, cap, k,
-                                                           L.chunk, L.nsplit, qscale, partials, out, out_f32);
+                                                           L.chunk, L.nsplit, qscale, partials, out, out_f32,
+                                                           GateArgs{});
   }
   const dim3 mgrid((unsigned)(L.units * G));
   if (L.nsplit > 8) merge_kernel<G, 32><<<mgrid, dim3(HEAD_DIM), 0, st>>>(partials, L.nsplit, out, out_f32);
@@ -490,19 +587,30 @@ void launch_attend_g(const Layout& L, const uint16_t* q, const uint16_t* K, cons
 
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
-                         float sm_scale, void* out, unsigned char* ws, hipStream_t st, const float* bias) {
+                         float sm_scale, void* out, unsigned char* ws, hipStream_t st, const float* bias,
+                         const GatedSelect* gsel) {
+  GateArgs ga;
+  if (gsel) {
+    ga.u = gsel->gate_scores;
+    ga.ustride = gsel->gate_stride;
+    ga.unit_size = gsel->unit_size;
+    ga.k_units = gsel->k_units;
+    ga.lam = gsel->lambda;
+    ga.idx_out = gsel->idx;
+  }
+  const GateArgs* gate = gsel ? &ga : nullptr;
   float* partials = reinterpret_cast<float*>(ws + L.off_partials);
   const float qscale = sm_scale * LOG2E;
   const int out_f32 = (s.flags & SJSA_FLAG_OUT_F32) ? 1 : 0;
   switch (s.group) {
     case 1: launch_attend_g<1>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
-                               out_f32, st); break;
+                               out_f32, st, gate); break;
     case 2: launch_attend_g<2>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
-                               out_f32, st); break;
+                               out_f32, st, gate); break;
     case 4: launch_attend_g<4>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
-                               out_f32, st); break;
+                               out_f32, st, gate); break;
     case 8: launch_attend_g<8>(L, q, K, V, idx, bias, k, seq_len, s.n_kv_heads, s.capacity, qscale, partials, out,
-                               out_f32, st); break;
+                               out_f32, st, gate); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -84,11 +84,25 @@ int32_t set_fused_wait_us(int32_t us);
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
                          const void* kproj, const int32_t* seq_len, int k, int32_t* idx, unsigned char* ws,
                          hipStream_t st);
+// The gated-logit selection, when the attention launch makes it itself (gsel below).
+struct GatedSelect {
+  const float* gate_scores = nullptr;   // [B * H_kv, gate_stride] unit scores
+  int64_t gate_stride = 0;
+  int unit_size = 1;
+  int k_units = 1;
+  float lambda = 0.f;
+  int32_t* idx = nullptr;               // [B * H_kv, k_units * unit_size] output
+};
+// Largest unit count and budget the attention launch selects for itself.
+constexpr int GATE_FUSED_UNITS_MAX = 2048;
+constexpr int GATE_FUSED_KEPT_MAX = 512;
 // bias != nullptr: one exp2-domain logit term per index entry, laid out like idx.
+// gsel != nullptr: every attention workgroup makes its unit's gated selection first
+// (k = k_units * unit_size; idx and bias are not read, the index list is written).
 hipError_t launch_attend(const sjsa_shape& s, const Layout& L, const uint16_t* q, const uint16_t* K,
                          const uint16_t* V, const int32_t* idx, int k, const int32_t* seq_len,
                          float sm_scale, void* out, unsigned char* ws, hipStream_t st,
-                         const float* bias = nullptr);
+                         const float* bias = nullptr, const GatedSelect* gsel = nullptr);
 // Block-sparse step: workspace of the block logits and the tiles' softmax partials,
 // then the attention partials (att).
 struct BlockLayout {

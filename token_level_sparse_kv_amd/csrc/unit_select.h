@@ -1,7 +1,8 @@
 // Exact selection of whole units (runs of consecutive positions) by a per-unit
 // score, shared by the gated-logit step (units = gated context units) and the
-// block-sparse step (units = key blocks). One 1024-thread workgroup per (sequence,
-// KV head):
+// block-sparse step (units = key blocks). One workgroup of NT threads (1024 for the
+// selection kernels, 256 where the selection is fused into the attention) per
+// (sequence, KV head):
 //   * forced units are always kept; when the sequence has at most `budget` units,
 //     every unit is kept;
 //   * otherwise `need` more units are taken among the eligible ones, largest score
@@ -23,15 +24,21 @@ namespace sjsa {
 constexpr int SEL_UNIT_THREADS = 1024;
 constexpr int SEL_UNIT_WAVES = SEL_UNIT_THREADS / 64;
 
-struct UnitSelectShared {
+// LDS of the selector: NT threads, room for KC kept units.
+template <int NT = SEL_UNIT_THREADS, int KC = SJSA_MAX_SELECT_UNITS>
+struct UnitSelectSharedT {
+  static constexpr int THREADS = NT;
+  static constexpr int KEPT_CAP = KC;
   uint32_t hist[256];
-  uint32_t wsum[SEL_UNIT_WAVES];
+  uint32_t wsum[NT / 64];
   uint32_t misc[4];
-  int32_t kept[SJSA_MAX_SELECT_UNITS];
+  int32_t kept[KC];
 };
+using UnitSelectShared = UnitSelectSharedT<>;
 
-// Block-wide exclusive prefix sum of one value per thread; total gets the sum.
-// Every thread of the workgroup must call it.
+// Block-wide exclusive prefix sum of one value per thread (NT threads); total gets
+// the sum. Every thread of the workgroup must call it.
+template <int NT>
 __device__ __forceinline__ uint32_t unit_block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
@@ -39,7 +46,7 @@ __device__ __forceinline__ uint32_t unit_block_excl_scan(uint32_t v, uint32_t* w
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < SEL_UNIT_WAVES; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const uint32_t t = wsum[w];
     before += w < wave ? t : 0u;
     tot += t;
@@ -53,10 +60,12 @@ __device__ __forceinline__ uint32_t unit_block_excl_scan(uint32_t v, uint32_t* w
 // U: units of the sequence; all: keep every unit; need: eligible units to take
 // (need <= the eligible units when !all); score(i): the unit's score (called for
 // eligible units only); forced(i), eligible(i): predicates for i < U (disjoint).
-// Every thread of the 1024-thread workgroup must call it.
-template <class ScoreF, class ForcedF, class EligF>
+// Every thread of the workgroup must call it. At most KEPT_CAP units are listed.
+template <class SH, class ScoreF, class ForcedF, class EligF>
 __device__ uint32_t select_kept_units(int U, bool all, int need, ScoreF score, ForcedF forced, EligF eligible,
-                                      UnitSelectShared& sh) {
+                                      SH& sh) {
+  constexpr int NT = SH::THREADS;
+  constexpr uint32_t KC = (uint32_t)SH::KEPT_CAP;
   const int tid = threadIdx.x;
   // keep eligible unit i iff (key & mask) > prefix, or (key & mask) == prefix and
   // either the whole boundary digit is taken or it is among the first take_eq
@@ -68,9 +77,9 @@ __device__ uint32_t select_kept_units(int U, bool all, int need, ScoreF score, F
     uint32_t remaining = (uint32_t)need;
     if (tid == 0) { sh.misc[0] = 0u; sh.misc[1] = 0u; sh.misc[2] = 0u; }
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += SEL_UNIT_THREADS) sh.hist[i] = 0u;
+      for (int i = tid; i < 256; i += NT) sh.hist[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < U; i += SEL_UNIT_THREADS) {
+      for (int i = tid; i < U; i += NT) {
         if (!eligible(i)) continue;
         const uint32_t key = score_key(score(i));
         if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
@@ -107,7 +116,7 @@ __device__ uint32_t select_kept_units(int U, bool all, int need, ScoreF score, F
 
   // ordered compaction: one scan of (boundary-equal << 16 | kept for sure)
   uint32_t ndef = 0, neq = 0;
-  for (int base = 0; base < U; base += SEL_UNIT_THREADS) {
+  for (int base = 0; base < U; base += NT) {
     const int i = base + tid;
     bool def = false, eq = false;
     if (i < U) {
@@ -120,25 +129,25 @@ __device__ uint32_t select_kept_units(int U, bool all, int need, ScoreF score, F
       }
     }
     uint32_t tot;
-    const uint32_t ex = unit_block_excl_scan((eq ? 0x10000u : 0u) | (def ? 1u : 0u), sh.wsum, tot);
+    const uint32_t ex = unit_block_excl_scan<NT>((eq ? 0x10000u : 0u) | (def ? 1u : 0u), sh.wsum, tot);
     const uint32_t eq_before = neq + (ex >> 16);
     const bool keep = def || (eq && eq_before < take_eq);
     const uint32_t slot = ndef + (ex & 0xffffu) + min(eq_before, take_eq);
-    if (keep && slot < (uint32_t)SJSA_MAX_SELECT_UNITS) sh.kept[slot] = i;
+    if (keep && slot < KC) sh.kept[slot] = i;
     ndef += tot & 0xffffu;
     neq += tot >> 16;
   }
   __syncthreads();
-  return min(ndef + min(neq, take_eq), (uint32_t)SJSA_MAX_SELECT_UNITS);
+  return min(ndef + min(neq, take_eq), KC);
 }
 
 // Positions of the kept units, ascending: entry e of the list belongs to kept unit
 // e / unit_size; positions >= n and entries past the kept units are -1. extra(e, s,
 // valid) is called for every entry (s = kept slot) to write per-entry side data.
-template <class ExtraF>
-__device__ void write_kept_positions(const UnitSelectShared& sh, uint32_t nsel, int unit_size, float inv_unit,
+template <class SH, class ExtraF>
+__device__ void write_kept_positions(const SH& sh, uint32_t nsel, int unit_size, float inv_unit,
                                      int64_t n, int ktok, int32_t* __restrict__ out, ExtraF extra) {
-  for (int e = threadIdx.x; e < ktok; e += SEL_UNIT_THREADS) {
+  for (int e = threadIdx.x; e < ktok; e += SH::THREADS) {
     int s = (int)((float)e * inv_unit);          // e < 2^24: off by at most one, fixed below
     s -= s * unit_size > e ? 1 : 0;
     s += (s + 1) * unit_size <= e ? 1 : 0;
