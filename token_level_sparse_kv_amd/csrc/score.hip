@@ -159,7 +159,9 @@ struct PrepArgs {
 //    exact top k is among the rows that reach it unless the sample misjudges the
 //    distribution, a case the select stage detects and handles exactly: the
 //    threshold only decides how much work the select stage does, never its result.
-//  * tlow[2u + 1] = 1 when k >= n (every position is selected; the scan has no work).
+//  * tlow[2u + 1]: bit 0 set when k >= n (every position is selected; the scan has no
+//    work); bits TLOW_SHIFT_POS.. the shift of the candidates' relative keys (see
+//    cand_rel), set so that the sampled keys' range above the threshold fills them.
 // With APPEND the unit's new token (decode: one token per sequence at slot pos[b]) is
 // appended first: threads 0..31 copy its K and V rows and all threads compute its
 // projected row with the KeyProj layout (bit-identical to the append kernel). A sample
@@ -242,7 +244,7 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
     sh.qraw[tid >> 4][part * 4 + 3] = qw.w;
   }
   for (int i = tid; i < PREP_BINS; i += SCORE_THREADS) sh.hist[i] = 0u;
-  if (tid == 0) sh.misc[0] = 0xffffffffu;
+  if (tid == 0) { sh.misc[0] = 0xffffffffu; sh.misc[2] = 0u; }
   __syncthreads();
   if constexpr (APPEND && PUBLISH) {
     if (tid < RW) publish(sw + SYNC_ROW + tid, tag, sh.row[tid]);
@@ -289,7 +291,10 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
     if (tid == 0) {
       a.tlow[unit * 2] = 0u;
       a.tlow[unit * 2 + 1] = 1u;
-      if constexpr (PUBLISH) publish(sw + SYNC_THR, tag, 0u);
+      if constexpr (PUBLISH) {
+        publish(sw + SYNC_THR, tag, 0u);
+        publish(sw + SYNC_THR + 1, tag, 0u);
+      }
     }
     return;
   }
@@ -334,9 +339,15 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
     }
     __builtin_amdgcn_sched_barrier(0);                // one pass of loads in flight at a time
   }
+  // the greatest sampled key (NaN, +-inf included) sets the unit's candidate key shift
+  uint32_t kmx = 0u;
+#pragma unroll
+  for (int t = 0; t < BATCHES; ++t)
+    if (64 * (wave + t * SCORE_WAVES) + p * RPL + rs < S) kmx = max(kmx, score_key(sc[t]));
+  kmx = wave_max_u32(kmx);
   lo = wave_min_f32(lo);
   hi = wave_max_f32(hi);
-  if (lane == 0) { sh.red[wave] = lo; sh.red[SCORE_WAVES + wave] = hi; }
+  if (lane == 0) { sh.red[wave] = lo; sh.red[SCORE_WAVES + wave] = hi; atomicMax(&sh.misc[2], kmx); }
   __syncthreads();
 #pragma unroll
   for (int v = 0; v < SCORE_WAVES; ++v) {
@@ -392,9 +403,20 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
   // fewer than m binned samples (most scores NaN or -inf): every row is a candidate
   if (tid == 0) {
     const uint32_t thr = total >= mm ? sh.misc[0] : 0u;
+    // candidate keys are stored as (key - thr) >> shift in CAND_KEY_BITS bits: the
+    // shift that fits four times the sampled range above the threshold (keys of rows
+    // beyond that saturate); at most CAND_ROW_BITS, where no key saturates, which is
+    // also the shift when the threshold is 0
+    const uint32_t range = sh.misc[2] > thr ? sh.misc[2] - thr : 0u;
+    const int bits = range ? 32 - __clz(range) : 0;
+    const uint32_t shift =
+        total >= mm ? (uint32_t)min(CAND_ROW_BITS, max(0, bits + CAND_HEADROOM - CAND_KEY_BITS)) : (uint32_t)CAND_ROW_BITS;
     a.tlow[unit * 2] = thr;
-    a.tlow[unit * 2 + 1] = 0u;
-    if constexpr (PUBLISH) publish(sw + SYNC_THR, tag, thr);
+    a.tlow[unit * 2 + 1] = shift << TLOW_SHIFT_POS;
+    if constexpr (PUBLISH) {
+      publish(sw + SYNC_THR, tag, thr);
+      publish(sw + SYNC_THR + 1, tag, shift);
+    }
   }
 }
 
@@ -423,9 +445,9 @@ struct ScanArgs {
 // after which lane (rs, p) owns the score of group row p*RPL + rs.
 //
 // Each wave first scores all its rows into a private LDS stash (one key per row);
-// then it takes the threshold and keeps the rows whose key reaches it as candidates,
-// 32-bit entries (the key's top 20 bits, the row's offset in its tile; see
-// cand_entry) in position order: with a ballot of the flags in lane order, the number
+// then it takes the threshold (and the unit's key shift) and keeps the rows whose key
+// reaches it as candidates, 32-bit entries (the key relative to the threshold in 20
+// bits, the row's offset in its tile; see cand_entry) in position order: with a ballot of the flags in lane order, the number
 // of flagged rows before a row is the popcount of the ballot under a per-lane mask of
 // the lanes that hold earlier rows (earlier lane columns, and this column above this
 // lane). The candidates are compacted in place over the stash (a segment's entries
@@ -454,7 +476,7 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
   const int wave = threadIdx.x >> 6;
   const int seg0 = tile * SEGS_PER_TILE;
   if (seg0 * SEG_ROWS >= n) return;            // the whole tile lies past the end
-  const bool take_all = POLL ? a.k >= n : a.tlow[unit * 2 + 1] != 0u;
+  const bool take_all = POLL ? a.k >= n : (a.tlow[unit * 2 + 1] & 1u) != 0u;
   if (take_all && !WRITE_DENSE) return;
   const int p = lane % LPR;
   const int rs = lane / LPR;
@@ -564,13 +586,16 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
       }
     }
   }
-  uint32_t tkey = 0;
+  uint32_t tkey = 0, tshift = 0;           // the threshold key and the candidate key shift
   if (ok && !take_all && nseg > 0) {
     if constexpr (POLL) {
-      ok = poll_words(sw + SYNC_THR, 1, tag, deadline, tkey);
-      tkey = readlane_u32(tkey, 0);
+      uint32_t v;
+      ok = poll_words(sw + SYNC_THR, 2, tag, deadline, v);
+      tkey = readlane_u32(v, 0);
+      tshift = readlane_u32(v, 1);
     } else {
       tkey = a.tlow[unit * 2];
+      tshift = a.tlow[unit * 2 + 1] >> TLOW_SHIFT_POS;
     }
   }
   uint32_t wcount = 0;                     // candidates of this wave so far
@@ -590,7 +615,7 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
         const bool c = row < n && key[u] >= tkey;
         const uint64_t m = __ballot(c);
         if (c) {
-          stash[wcount + count + (uint32_t)__popcll(m & earlier)] = cand_entry(key[u], row);
+          stash[wcount + count + (uint32_t)__popcll(m & earlier)] = cand_entry(cand_rel(key[u], tkey, tshift), row);
           kmax = max(kmax, key[u]);
         }
         count += (uint32_t)__popcll(m);

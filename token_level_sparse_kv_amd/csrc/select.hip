@@ -593,8 +593,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const int lane = tid & 63, wave = tid >> 6;
 
   // Candidates. Scan tile x (rows [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in
-  // position order, at entries [x*TILE_ROWS, ...) as (top CAND_KEY_BITS key bits,
-  // row offset in the tile); counts[x] holds their number (TILE_OVERFLOW when it
+  // position order, at entries [x*TILE_ROWS, ...) as (the key relative to the
+  // threshold, cand_rel, in CAND_KEY_BITS bits; the row offset in the tile); counts[x] holds their number (TILE_OVERFLOW when it
   // could not keep them all) and their greatest key. Every candidate key is at least
   // the scan's threshold key, so [threshold, greatest key] bounds the keys. Tiles are
   // gathered in chunks of CHUNK_T; wave w owns TPW consecutive tiles of a chunk and
@@ -620,12 +620,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     }
   };
   const bool cand_path = scores == nullptr;
-  uint32_t tkey = 0;
+  uint32_t tkey = 0, tshift = 0;
   if (cand_path) {
     // one more step of this unit done on this workspace: the next prep publishes
     // under a new tag
     if (tid == 0) epoch[unit] += 1u;
     tkey = tlow[unit * 2];
+    tshift = tlow[unit * 2 + 1] >> TLOW_SHIFT_POS;
     load_chunk(0, ntile_cap);
     if (tid < R) sh.qh[tid] = qhat[(size_t)unit * QHAT_STRIDE + tid];
     if (tid == 0) sh.misc[6] = 0;                 // boundary entry counter (read after many barriers)
@@ -700,12 +701,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
   const bool overflowed = __syncthreads_or(ovf) != 0;
   if (!overflowed && total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
-    // threshold on the truncated keys (range [threshold, greatest key] >> CAND_ROW_BITS)
+    // threshold on the relative keys (range [0, relative greatest key])
     kmax = (uint32_t)sh.misc[5];
     uint32_t needT;
     bool all_eq;
-    uint32_t T = lds_threshold_range(ckey, (int)total, tkey >> CAND_ROW_BITS, kmax >> CAND_ROW_BITS,
-                                     (uint32_t)kk, sh, &needT, &all_eq);
+    uint32_t T = lds_threshold_range(ckey, (int)total, 0u, cand_rel(kmax, tkey, tshift), (uint32_t)kk, sh, &needT,
+                                     &all_eq);
     if (needT == 0xffffffffu) all_eq = true;
     const unsigned char* kp_unit = kproj + (size_t)unit * cap * R * KB;
     int nb = 0;                                   // entries on the boundary truncated key T
@@ -742,13 +743,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       }
       __syncthreads();
       needT = 0;                                  // keep the keys above T
-    } else if (!all_eq && needT > 0) {
+    } else if (!all_eq && needT > 0 && T < CAND_REL_MAX) {
       // many boundary entries: recompute their exact keys and rank on full keys, each
-      // entry's key becoming (truncated key, low key bits or 0 off the boundary)
+      // entry's key becoming (relative key, the exact key's offset inside the boundary's
+      // 2^shift-key range scaled to CAND_ROW_BITS bits, or 0 off the boundary)
       for (int i = tid; i < (int)total; i += SEL_THREADS) {
         const uint32_t kt = ckey[i];
         uint32_t low = 0;
-        if (kt == T) low = score_key(row_score<R, KB>(sh.qh, kp_unit + (size_t)cpos[i] * R * KB)) & CAND_ROW_MASK;
+        if (kt == T) {
+          const uint32_t ex = score_key(row_score<R, KB>(sh.qh, kp_unit + (size_t)cpos[i] * R * KB));
+          low = ((ex - tkey - (T << tshift)) & ((1u << tshift) - 1u)) << (CAND_ROW_BITS - tshift);
+        }
         ckey[i] = (kt << CAND_ROW_BITS) | low;
       }
       for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
@@ -757,10 +762,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       const uint32_t lo = T << CAND_ROW_BITS;
       T = lds_threshold_range(ckey, (int)total, lo, lo | CAND_ROW_MASK, needT, sh, &needT, &all_eq);
     }
-    // compact in place in LDS, then write the result with coalesced stores
-    compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, sh);
-    for (int i = tid; i < kk; i += SEL_THREADS) out[i] = cpos[i];
-    return;
+    if (!(!all_eq && needT > 0 && nb > 64 && T >= CAND_REL_MAX)) {
+      // compact in place in LDS, then write the result with coalesced stores
+      compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, sh);
+      for (int i = tid; i < kk; i += SEL_THREADS) out[i] = cpos[i];
+      return;
+    }
+    // (many entries on a saturated relative key: their exact order does not fit the
+    // packed keys; the exact selection below handles the unit)
+    __syncthreads();
   }
   // the sampled threshold misjudged this unit: exact selection over recomputed scores
   float* row = dense + (size_t)unit * dense_stride;

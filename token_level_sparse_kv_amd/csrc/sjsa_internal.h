@@ -21,17 +21,27 @@ constexpr uint32_t TILE_OVERFLOW = 0xffffffffu;   // tile count: the tile's cand
 constexpr int SYNC_WORDS = 128;      // per unit
 constexpr int SYNC_THR = 64;         // word: threshold key ([0, r) hold q_hat)
 constexpr int SYNC_ROW = 96;         // words: the appended token's projected row (r*KB/4 <= 32)
-// A candidate entry holds the top CAND_KEY_BITS bits of its score key and the row's
-// offset inside its scan tile (TILE_ROWS = 2^CAND_ROW_BITS rows): the selection
-// ranks by the truncated keys and recomputes the exact score only of the entries
-// that share the boundary's truncated key.
+// A candidate entry holds its key relative to the unit's threshold key,
+// rel = (key - threshold) >> shift clamped to CAND_KEY_BITS bits, above the row's
+// offset inside its scan tile (TILE_ROWS = 2^CAND_ROW_BITS rows). The prep picks the
+// unit's shift so that four times the sampled keys' range above the threshold fits
+// the CAND_KEY_BITS bits (shift <= CAND_ROW_BITS, since keys have 32 bits): the
+// selection ranks by rel and recomputes the exact score only of the entries that
+// share the boundary's rel, which at this resolution is rarely more than one.
 constexpr int CAND_ROW_BITS = 12;
 constexpr int CAND_KEY_BITS = 32 - CAND_ROW_BITS;
 constexpr uint32_t CAND_ROW_MASK = (1u << CAND_ROW_BITS) - 1u;
+constexpr uint32_t CAND_REL_MAX = (1u << CAND_KEY_BITS) - 1u;
 static_assert(TILE_ROWS == 1 << CAND_ROW_BITS, "a tile offset fills the entry's low bits");
-__host__ __device__ constexpr uint32_t cand_entry(uint32_t key, int row) {
-  return (key & ~CAND_ROW_MASK) | ((uint32_t)row & CAND_ROW_MASK);
+__host__ __device__ constexpr uint32_t cand_rel(uint32_t key, uint32_t tkey, uint32_t shift) {
+  return key <= tkey ? 0u : ((key - tkey) >> shift < CAND_REL_MAX ? (key - tkey) >> shift : CAND_REL_MAX);
 }
+__host__ __device__ constexpr uint32_t cand_entry(uint32_t rel, int row) {
+  return (rel << CAND_ROW_BITS) | ((uint32_t)row & CAND_ROW_MASK);
+}
+// tlow[2u + 1]: bit 0 = every position is taken (k >= n); bits 8.. = the unit's shift
+constexpr int TLOW_SHIFT_POS = 8;
+constexpr int CAND_HEADROOM = 2;      // log2 of the relative keys' span over the sampled range
 constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
 
 struct Layout {
