@@ -46,6 +46,8 @@ constexpr int CAND_CAP = LDS_WORDS / 2;         // candidate path: ckey | cpos
 static_assert(A_CAP + 2 * C_CAP == LDS_WORDS, "dense lists fill the list storage");
 
 constexpr int HIST2_BINS = 2048;                // second histogram (candidate path, round 1)
+constexpr int HIST1_BITS = 12;                  // candidate path: first digit of the relative keys
+static_assert(1 << HIST1_BITS <= HIST_BINS && HIST1_BITS < CAND_KEY_BITS, "first digit fits sh.hist");
 
 struct SelShared {
   uint32_t hist[HIST_BINS];
@@ -207,12 +209,15 @@ __device__ void find_bucket_fast(const uint32_t* hist, int nbins, uint32_t need,
 // the top, 12 at a time in sh.hist and 11 in sh.hist2 for the second round (both
 // must be zero on entry, so that the first two rounds need no clearing pass), so
 // the first histogram spreads the keys over up to 4096 bins whatever part of the
-// key range they occupy. When the bin holding rank `need` is taken whole, the
+// key range they occupy. With `prebuilt` the caller has already counted the keys
+// into sh.hist by their top 12 bits of [kmin, kmax] (the first round's digit). When
+// the bin holding rank `need` is taken whole, the
 // threshold stops there. Returns T and *needT such that the selection is: keys
 // above T, plus the first needT keys equal to T; *all_eq is set when that takes
 // every key equal to T.
 __device__ uint32_t lds_threshold_range(const uint32_t* keys, int cnt, uint32_t kmin, uint32_t kmax,
-                                        uint32_t need, SelShared& sh, uint32_t* needT, bool* all_eq) {
+                                        uint32_t need, SelShared& sh, uint32_t* needT, bool* all_eq,
+                                        bool prebuilt = false) {
   *all_eq = false;
   const int tid = threadIdx.x;
   int hi = 32 - __clz(kmax - kmin);           // significant bits of the offsets
@@ -227,18 +232,20 @@ __device__ uint32_t lds_threshold_range(const uint32_t* keys, int cnt, uint32_t 
       __syncthreads();
     }
     const uint64_t want = (uint64_t)prefix >> hi;
-    // KU keys per thread per batch: all their LDS reads are issued before any atomic
-    constexpr int KU = 8;
-    for (int i0 = tid; i0 < cnt; i0 += KU * SEL_THREADS) {
-      uint32_t off[KU];
+    if (!(prebuilt && round == 0)) {
+      // KU keys per thread per batch: all their LDS reads are issued before any atomic
+      constexpr int KU = 8;
+      for (int i0 = tid; i0 < cnt; i0 += KU * SEL_THREADS) {
+        uint32_t off[KU];
 #pragma unroll
-      for (int u = 0; u < KU; ++u) off[u] = keys[min(i0 + u * SEL_THREADS, cnt - 1)] - kmin;
+        for (int u = 0; u < KU; ++u) off[u] = keys[min(i0 + u * SEL_THREADS, cnt - 1)] - kmin;
 #pragma unroll
-      for (int u = 0; u < KU; ++u)
-        if (i0 + u * SEL_THREADS < cnt && ((uint64_t)off[u] >> hi) == want)
-          atomicAdd(&hist[(off[u] >> shift) & (uint32_t)(nb - 1)], 1u);
+        for (int u = 0; u < KU; ++u)
+          if (i0 + u * SEL_THREADS < cnt && ((uint64_t)off[u] >> hi) == want)
+            atomicAdd(&hist[(off[u] >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     find_bucket_fast(hist, nb, need, sh);
     const uint32_t bin = (uint32_t)sh.misc[0];
     const uint32_t above = (uint32_t)sh.misc[1];
@@ -342,11 +349,13 @@ __device__ __forceinline__ void strided_rank(const bool (&f)[NE], uint32_t (&ran
   *total = table[NE * SEL_WAVES];
 }
 
-// Ordered compaction of the candidate list in place: keep keys above T, and the
-// first needT keys equal to T (all of them when all_eq). pos_l[0 .. kept) receives
-// the kept positions in list order. Returns the kept count.
-__device__ uint32_t compact_candidates(const uint32_t* key_l, int32_t* pos_l, int cnt, uint32_t T,
-                                       uint32_t needT, bool all_eq, SelShared& sh) {
+// Ordered compaction of the candidate list: keep keys above T, and the first needT
+// keys equal to T (all of them when all_eq). out[0 .. kept) receives the kept
+// positions in list order (slots at or past `limit` are not written). Returns the
+// kept count.
+__device__ uint32_t compact_candidates(const uint32_t* key_l, const int32_t* pos_l, int cnt, uint32_t T,
+                                       uint32_t needT, bool all_eq, int32_t* out, uint32_t limit,
+                                       SelShared& sh) {
   const int tid = threadIdx.x;
   uint32_t* table = sh.hist;
   uint32_t* table2 = sh.hist + 256;
@@ -366,7 +375,7 @@ __device__ uint32_t compact_candidates(const uint32_t* key_l, int32_t* pos_l, in
     if (all_eq) {
 #pragma unroll
       for (int e = 0; e < CEPT; ++e) sel[e] = sel[e] || eq[e];
-    } else {
+    } else if (needT > 0) {
       uint32_t req[CEPT], totEq;
       strided_rank(eq, req, table2, &totEq);
 #pragma unroll
@@ -374,12 +383,12 @@ __device__ uint32_t compact_candidates(const uint32_t* key_l, int32_t* pos_l, in
       baseEq += totEq;
     }
     uint32_t rs[CEPT], totS;
-    strided_rank(sel, rs, table, &totS);    // its barriers also order every read above before the writes
+    strided_rank(sel, rs, table, &totS);
 #pragma unroll
     for (int e = 0; e < CEPT; ++e)
-      if (sel[e]) pos_l[baseS + rs[e]] = pos[e];
+      if (sel[e] && baseS + rs[e] < limit) out[baseS + rs[e]] = pos[e];
     baseS += totS;
-    __syncthreads();
+    // the next pass's strided_rank rewrites table only after its first barrier
   }
   return baseS;
 }
@@ -594,9 +603,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
   // Candidates. Scan tile x (rows [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in
   // position order, at entries [x*TILE_ROWS, ...) as (the key relative to the
-  // threshold, cand_rel, in CAND_KEY_BITS bits; the row offset in the tile); counts[x] holds their number (TILE_OVERFLOW when it
-  // could not keep them all) and their greatest key. Every candidate key is at least
-  // the scan's threshold key, so [threshold, greatest key] bounds the keys. Tiles are
+  // threshold, cand_rel, in CAND_KEY_BITS bits; the row offset in the tile); counts[x]
+  // holds their number (TILE_OVERFLOW when it could not keep them all) and their
+  // greatest key. Every candidate key is at least the scan's threshold key, so no
+  // relative key wraps. The gather counts the relative keys by their first digit as
+  // it places them. Tiles are
   // gathered in chunks of CHUNK_T; wave w owns TPW consecutive tiles of a chunk and
   // loads their first SPEC*64 entries unconditionally (entries past the count are
   // never used) together with the counts, so one memory round trip serves a chunk.
@@ -656,17 +667,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) sh.hist2[i] = 0u;
   const int64_t ntiles = (n + TILE_ROWS - 1) / TILE_ROWS;
   uint32_t total = 0;
-  uint32_t kmax = 0u;                             // wave 0: greatest candidate key so far
   bool ovf = false;
   for (int64_t t0 = 0; t0 < ntiles; t0 += CHUNK_T) {
     if (t0 > 0) load_chunk(t0, ntiles);
     const uint32_t c = (uint32_t)cw;
     const bool own = tid < CHUNK_T && t0 + tid < ntiles;
     ovf = ovf || (own && c == TILE_OVERFLOW);
-    if (wave == 0) {
-      kmax = max(kmax, wave_max_u32(own ? (uint32_t)(cw >> 32) : 0u));
-      if (lane == 0) sh.misc[5] = (int32_t)kmax;     // read after the loop's last barrier
-    }
     uint32_t chunk_total;
     const uint32_t incl = block_incl_scan(own && c != TILE_OVERFLOW ? c : 0u, sh.scan, &chunk_total);
     if (tid < CHUNK_T) toff[tid + 1] = incl;
@@ -684,6 +690,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         if (j < ct && dst < (uint32_t)CAND_CAP) {
           ckey[dst] = v[i][e] >> CAND_ROW_BITS;
           cpos[dst] = (int32_t)((t0 + tl) * TILE_ROWS + (v[i][e] & CAND_ROW_MASK));
+          atomicAdd(&sh.hist[v[i][e] >> (32 - HIST1_BITS)], 1u);
         }
       }
       for (uint32_t j = SPEC * 64 + lane; j < ct; j += 64) {     // tiles with many candidates
@@ -692,6 +699,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
           const uint32_t x = __builtin_nontemporal_load(cand_u + (t0 + tl) * TILE_ROWS + j);
           ckey[dst] = x >> CAND_ROW_BITS;
           cpos[dst] = (int32_t)((t0 + tl) * TILE_ROWS + (x & CAND_ROW_MASK));
+          atomicAdd(&sh.hist[x >> (32 - HIST1_BITS)], 1u);
         }
       }
     }
@@ -701,12 +709,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
   const bool overflowed = __syncthreads_or(ovf) != 0;
   if (!overflowed && total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
-    // threshold on the relative keys (range [0, relative greatest key])
-    kmax = (uint32_t)sh.misc[5];
+    // threshold on the relative keys over their whole range [0, CAND_REL_MAX]: the
+    // gather has counted them by their top HIST1_BITS bits already
     uint32_t needT;
     bool all_eq;
-    uint32_t T = lds_threshold_range(ckey, (int)total, 0u, cand_rel(kmax, tkey, tshift), (uint32_t)kk, sh, &needT,
-                                     &all_eq);
+    uint32_t T = lds_threshold_range(ckey, (int)total, 0u, CAND_REL_MAX, (uint32_t)kk, sh, &needT, &all_eq, true);
     if (needT == 0xffffffffu) all_eq = true;
     const unsigned char* kp_unit = kproj + (size_t)unit * cap * R * KB;
     int nb = 0;                                   // entries on the boundary truncated key T
@@ -764,8 +771,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     }
     if (!(!all_eq && needT > 0 && nb > 64 && T >= CAND_REL_MAX)) {
       // compact in place in LDS, then write the result with coalesced stores
-      compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, sh);
-      for (int i = tid; i < kk; i += SEL_THREADS) out[i] = cpos[i];
+      compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, out, (uint32_t)kk, sh);
       return;
     }
     // (many entries on a saturated relative key: their exact order does not fit the
