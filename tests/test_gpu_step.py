@@ -203,3 +203,32 @@ def test_scan_stage_overflow_falls_back_exactly():
     kp = np.tile(low, (1, 1, n, 1)).astype(np.uint16)
     kp[0, 0, :4096] = high
     _ties_check(wl, kp, k, "stage overflow")
+
+
+@pytest.mark.parametrize("k", [100, 400])
+def test_outliers_between_sampled_rows(k):
+    # 300 rows score far above every other row and sit between the sampled pairs
+    # (rows 2*floor(i*n/2048) and the one after), so the sampled threshold and key
+    # range know nothing of them: their candidate keys saturate. With k = 100 the
+    # boundary lies among the outliers, with k = 400 every outlier is taken whole.
+    say(f"step unsampled outliers k={k}")
+    n = 40000
+    wl = workloads.gaussian(1, 2, 4, 128, 16, n, k, seed=28, device="cuda")
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    kp = kproj_oracle(bits(wl.K), M)
+    from oracle.numerics import round_to_bf16
+    starts = 2 * ((np.arange(1024, dtype=np.int64) * n) // 2048)
+    rows = (starts + 10)[::3][:300]
+    assert not np.isin(rows, np.concatenate([starts, starts + 1])).any()
+    rng = np.random.default_rng(29)
+    for h in range(2):
+        qhat = jssa.project_query(jssa.mean_query(q[0, 4 * h:4 * h + 4]), M[h]).astype(np.float64)
+        mag = rng.uniform(64.0, 128.0, size=(300, 1))
+        kp[0, h, rows] = round_to_bf16(np.sign(qhat)[None, :] * mag)
+    o, ix, _ = _run_and_check(wl, kp, k, tag=f"outliers k{k}")
+    for h in range(2):
+        if k == 400:
+            assert np.isin(rows, ix[0, h]).all()
+        else:
+            assert np.isin(ix[0, h], rows).all()
