@@ -34,6 +34,10 @@ constexpr int ATT_U = 4;             // rows in flight per slot
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.f;  // log2 units a logit may exceed the softmax reference by
 
+// Softmax weight 2^x for x <= RESCALE_SLACK: the hardware exp2 alone (results below
+// 2^-126 come out as 0, which changes no sum of weights that holds one weight >= 1).
+__device__ __forceinline__ float weight_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Gated-logit selection run by every attention workgroup of a unit (GATE form):
 // the unit scores u, the unit size, the budget in units, lambda, and where the
 // index list goes.
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       const float ref = m[g] == -INFINITY ? 0.f : m[g];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        p[u][g] = exp2f(z[u][g] - ref);
+        p[u][g] = weight_exp2(z[u][g] - ref);
         l[g] += p[u][g];
       }
     }
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float pv = exp2f(z[v] - ref);
+      const float pv = weight_exp2(z[v] - ref);
       lsum += pv;
       ph[v] = f32_to_bf16_rne(pv);
       pl[v] = f32_to_bf16_rne(pv - __uint_as_float(ph[v] << 16));
