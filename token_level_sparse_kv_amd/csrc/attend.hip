@@ -21,6 +21,8 @@
 // (m, l, acc) partial and merge_kernel (one workgroup per (unit, query head),
 // launched next on the same stream) combines the partials in split order with a
 // log-sum-exp merge.
+#include <utility>
+
 #include "sjsa_device.h"
 #include "sjsa_internal.h"
 #include "unit_select.h"
@@ -37,6 +39,36 @@ constexpr float RESCALE_SLACK = 8.f;  // log2 units a logit may exceed the softm
 // Softmax weight 2^x for x <= RESCALE_SLACK: the hardware exp2 alone (results below
 // 2^-126 come out as 0, which changes no sum of weights that holds one weight >= 1).
 __device__ __forceinline__ float weight_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;   // lane t of a row reads lane t ^ 7
+// Lane i of each DPP row, broadcast to the whole row (row_newbcast:i).
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(I >= 0 && I < 16, "a row has 16 lanes");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + I, 0xF, 0xF, true));
+}
+// out[i] = lane i's v, for lanes 0 .. sizeof...(I) - 1 of the row.
+template <int... I>
+__device__ __forceinline__ void row_bcast_all(float v, float* out, std::integer_sequence<int, I...>) {
+  ((out[I] = row_bcast<I>(v)), ...);
+}
+
+// Transposed sum over the 16 lanes of a DPP row: v[i] is lane t's share of value i;
+// lane t gets the full sum of value t. Four exchange rounds with partners t ^ 8,
+// t ^ 7, t ^ 2 and t ^ 1; in each a lane keeps the half of its values whose index
+// bit (3, 2, 1, 0 in turn) equals its own lane bit and adds the partner's share of
+// that half (15 additions instead of the 64 of four full row sums).
+__device__ __forceinline__ float row16_transpose_sum(const float (&v)[16], int t) {
+  float b[8], c[4], d[2];
+  const bool h3 = (t & 8) != 0, h2 = (t & 4) != 0, h1 = (t & 2) != 0, h0 = (t & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = (h3 ? v[i + 8] : v[i]) + dpp<DPP_ROW_ROR8>(h3 ? v[i] : v[i + 8]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = (h2 ? b[i + 4] : b[i]) + dpp<DPP_ROW_HALF_MIRROR>(h2 ? b[i] : b[i + 4]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) d[i] = (h1 ? c[i + 2] : c[i]) + dpp<DPP_QUAD_XOR2>(h1 ? c[i] : c[i + 2]);
+  return (h0 ? d[1] : d[0]) + dpp<DPP_QUAD_XOR1>(h0 ? d[0] : d[1]);
+}
 
 // Gated-logit selection run by every attention workgroup of a unit (GATE form):
 // the unit scores u, the unit size, the budget in units, lambda, and where the
@@ -260,7 +292,78 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     }
   };
 
-  if (slot * U < cnt) consume(j0, b0, kw0, vw0);
+  // G * U = 16: lane t of a slot owns the logit of row t / G and query head t % G. Its
+  // dot partials are summed with the transposed row reduction, the softmax
+  // bookkeeping runs once per logit (the head's reference is kept by each of its
+  // lanes, the running sum as per-lane shares), and each weight is broadcast from
+  // its lane for the V accumulation.
+  constexpr bool TR = G * U == 16;
+  const int tu = t / G, tg = t % G;
+  float m_t = -INFINITY, l_t = 0.f;
+  auto consume_tr = [&](int base, const int32_t (&j)[U], const u32x4 (&kw)[U], const u32x4 (&vw)[U]) {
+    float a[16];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(&sq2[g][t * 4]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x = dot2_bf16(qv.x, kw[u].x, 0.f);
+        x = dot2_bf16(qv.y, kw[u].y, x);
+        x = dot2_bf16(qv.z, kw[u].z, x);
+        a[(u * G + g) & 15] = dot2_bf16(qv.w, kw[u].w, x);
+      }
+    }
+    const float dot = row16_transpose_sum(a, t);
+    // which rows of the batch are valid, as a bit mask (an index into a register
+    // array would go through scratch memory); the lane's term comes from LDS
+    uint32_t okm = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) okm |= (j[u] >= 0 && (int64_t)j[u] < n) ? 1u << u : 0u;
+    const bool ok = ((okm >> tu) & 1u) != 0u;
+    float z;
+    if constexpr (BIAS) z = ok ? fmaf(dot, qscale, sbias[base + tu]) : -INFINITY;
+    else z = ok ? dot * qscale : -INFINITY;
+    // the head's greatest logit of the batch: lanes t, t-4, t-8, t-12 (mod 16) hold
+    // its U logits
+    float mx = fmaxf(z, dpp<DPP_ROW_ROR4>(z));
+    mx = fmaxf(mx, dpp<DPP_ROW_ROR8>(mx));
+    const bool raise = mx > m_t + RESCALE_SLACK;
+    if (__ballot(raise) != 0) {
+      const float sc = raise ? weight_exp2(m_t - mx) : 1.f;
+      l_t *= sc;
+      m_t = raise ? mx : m_t;
+      float scg[G];                             // head g's factor, from lane g
+      row_bcast_all(sc, scg, std::make_integer_sequence<int, (G < 16 ? G : 16)>{});
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= scg[g];
+      }
+    }
+    const float ref = m_t == -INFINITY ? 0.f : m_t;
+    const float pt = weight_exp2(z - ref);
+    l_t += pt;
+    float p[16];                                // the batch's weights, from their lanes
+    row_bcast_all(pt, p, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      vf[0] = bf_lo(vw[u].x); vf[1] = bf_hi(vw[u].x); vf[2] = bf_lo(vw[u].y); vf[3] = bf_hi(vw[u].y);
+      vf[4] = bf_lo(vw[u].z); vf[5] = bf_hi(vw[u].z); vf[6] = bf_lo(vw[u].w); vf[7] = bf_hi(vw[u].w);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[(u * G + g) & 15], vf[e], acc[g][e]);
+      }
+    }
+  };
+  auto step = [&](int base, const int32_t (&j)[U], const float (&bj)[U], const u32x4 (&kw)[U],
+                  const u32x4 (&vw)[U]) {
+    if constexpr (TR) consume_tr(base, j, kw, vw);
+    else consume(j, bj, kw, vw);
+  };
+
+  if (slot * U < cnt) step(slot * U, j0, b0, kw0, vw0);
   for (int base = slot * U + SLOTS * U; base < cnt; base += SLOTS * U) {
     int32_t j[U];
     float bj[U];
@@ -271,13 +374,20 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       bj[u] = (BIAS && base + u < cnt) ? sbias[base + u] : 0.f;
     }
     load_rows(j, kw, vw);
-    consume(j, bj, kw, vw);
+    step(base, j, bj, kw, vw);
+  }
+  if constexpr (TR) {
+    // the head's running sum: its shares sit in lanes t, t-4, t-8, t-12 (mod 16);
+    // lane g (row 0 of the batch) then holds head g's reference and sum
+    float lt = l_t + dpp<DPP_ROW_ROR4>(l_t);
+    lt += dpp<DPP_ROW_ROR8>(lt);
+    if (t < G) { sm_m[slot][t] = m_t; sm_l[slot][t] = lt; }
   }
 
   // ---- combine the 16 slots of this workgroup
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if (t == 0) { sm_m[slot][g] = m[g]; sm_l[slot][g] = l[g]; }
+    if (!TR && t == 0) { sm_m[slot][g] = m[g]; sm_l[slot][g] = l[g]; }
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm_acc[slot][g][t * 8 + e] = acc[g][e];
   }
