@@ -133,10 +133,12 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   // loads are unconditional (an invalid entry reads row 0, which always exists, and
   // gets zero weight), so the compiler can keep every load of a batch in flight;
   // each selected row is read once, so the loads are nontemporal
+  const uint32_t cap_u = (uint32_t)min(cap, (int64_t)INT32_MAX);
+  const uint32_t n_u = (uint32_t)min(n, (int64_t)INT32_MAX);
   auto load_rows = [&](const int32_t (&j)[U], u32x4 (&kw)[U], u32x4 (&vw)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = (j[u] >= 0 && (int64_t)j[u] < cap) ? j[u] : 0;
+      const uint32_t row = (uint32_t)j[u] < cap_u ? (uint32_t)j[u] : 0u;
       kw[u] = ld16_stream(Kb + (size_t)row * HEAD_DIM);
       vw[u] = ld16_stream(Vb + (size_t)row * HEAD_DIM);
     }
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     // array would go through scratch memory); the lane's term comes from LDS
     uint32_t okm = 0u;
 #pragma unroll
-    for (int u = 0; u < U; ++u) okm |= (j[u] >= 0 && (int64_t)j[u] < n) ? 1u << u : 0u;
+    for (int u = 0; u < U; ++u) okm |= (uint32_t)j[u] < n_u ? 1u << u : 0u;
     const bool ok = ((okm >> tu) & 1u) != 0u;
     float z;
     if constexpr (BIAS) z = ok ? fmaf(dot, qscale, sbias[base + tu]) : -INFINITY;
