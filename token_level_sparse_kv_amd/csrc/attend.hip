@@ -52,19 +52,26 @@ template <int... I>
 __device__ __forceinline__ void row_bcast_all(float v, float* out, std::integer_sequence<int, I...>) {
   ((out[I] = row_bcast<I>(v)), ...);
 }
+// out[g] = lane 4g's v (the first lane of quad g), for g < sizeof...(I) <= 4.
+template <int... I>
+__device__ __forceinline__ void row_bcast_heads(float v, float* out, std::integer_sequence<int, I...>) {
+  ((out[I] = row_bcast<(4 * I) & 15>(v)), ...);
+}
 
-// Transposed sum over the 16 lanes of a DPP row: v[i] is lane t's share of value i;
-// lane t gets the full sum of value t. Four exchange rounds with partners t ^ 8,
-// t ^ 7, t ^ 2 and t ^ 1; in each a lane keeps the half of its values whose index
-// bit (3, 2, 1, 0 in turn) equals its own lane bit and adds the partner's share of
-// that half (15 additions instead of the 64 of four full row sums).
+// Transposed sum over the 16 lanes of a DPP row; lane t gets the full sum of value t.
+// Lane t keeps its share of value i ^ ((t >> 2) << 2) in slot i (its caller permutes
+// the upper two index bits by the lane's own), so the first two exchange rounds
+// (partners t ^ 8 and t ^ 7, which flip bit 3, resp. bit 2, of t >> 2) add the
+// partner's upper half of the slots to the lane's lower half without selects; the
+// last two (partners t ^ 2 and t ^ 1) keep the half whose index bit matches the
+// lane's. 15 additions instead of the 64 of sixteen full row sums.
 __device__ __forceinline__ float row16_transpose_sum(const float (&v)[16], int t) {
   float b[8], c[4], d[2];
-  const bool h3 = (t & 8) != 0, h2 = (t & 4) != 0, h1 = (t & 2) != 0, h0 = (t & 1) != 0;
+  const bool h1 = (t & 2) != 0, h0 = (t & 1) != 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) b[i] = (h3 ? v[i + 8] : v[i]) + dpp<DPP_ROW_ROR8>(h3 ? v[i] : v[i + 8]);
+  for (int i = 0; i < 8; ++i) b[i] = v[i] + dpp<DPP_ROW_ROR8>(v[i + 8]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = (h2 ? b[i + 4] : b[i]) + dpp<DPP_ROW_HALF_MIRROR>(h2 ? b[i] : b[i + 4]);
+  for (int i = 0; i < 4; ++i) c[i] = b[i] + dpp<DPP_ROW_HALF_MIRROR>(b[i + 4]);
 #pragma unroll
   for (int i = 0; i < 2; ++i) d[i] = (h1 ? c[i + 2] : c[i]) + dpp<DPP_QUAD_XOR2>(h1 ? c[i] : c[i + 2]);
   return (h0 ? d[1] : d[0]) + dpp<DPP_QUAD_XOR1>(h0 ? d[0] : d[1]);
@@ -294,25 +301,27 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     }
   };
 
-  // G * U = 16: lane t of a slot owns the logit of row t / G and query head t % G. Its
-  // dot partials are summed with the transposed row reduction, the softmax
-  // bookkeeping runs once per logit (the head's reference is kept by each of its
-  // lanes, the running sum as per-lane shares), and each weight is broadcast from
-  // its lane for the V accumulation.
+  // G * U = 16: lane t of a slot owns the logit of query head t / U and row t % U
+  // (value t = g * U + u). Its dot partials are summed with the transposed row
+  // reduction (slot i holds value i ^ ((t >> 2) << 2): head (i >> 2) ^ (t >> 2), row
+  // i & 3), the softmax bookkeeping runs once per logit (the head's reference is kept
+  // by each of its lanes, the running sum as per-lane shares), and each weight is
+  // broadcast from its lane for the V accumulation.
   constexpr bool TR = G * U == 16;
-  const int tu = t / G, tg = t % G;
+  static_assert(!TR || (G == 4 && U == 4), "the lane layout covers 4 heads of 4 rows");
+  const int tg = t / U, tu = t % U;
   float m_t = -INFINITY, l_t = 0.f;
   auto consume_tr = [&](int base, const int32_t (&j)[U], const u32x4 (&kw)[U], const u32x4 (&vw)[U]) {
     float a[16];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const u32x4 qv = *reinterpret_cast<const u32x4*>(&sq2[g][t * 4]);
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(&sq2[(g ^ tg) & (G - 1)][t * 4]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x = dot2_bf16(qv.x, kw[u].x, 0.f);
         x = dot2_bf16(qv.y, kw[u].y, x);
         x = dot2_bf16(qv.z, kw[u].z, x);
-        a[(u * G + g) & 15] = dot2_bf16(qv.w, kw[u].w, x);
+        a[(g * U + u) & 15] = dot2_bf16(qv.w, kw[u].w, x);
       }
     }
     const float dot = row16_transpose_sum(a, t);
@@ -325,17 +334,16 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     float z;
     if constexpr (BIAS) z = ok ? fmaf(dot, qscale, sbias[base + tu]) : -INFINITY;
     else z = ok ? dot * qscale : -INFINITY;
-    // the head's greatest logit of the batch: lanes t, t-4, t-8, t-12 (mod 16) hold
-    // its U logits
-    float mx = fmaxf(z, dpp<DPP_ROW_ROR4>(z));
-    mx = fmaxf(mx, dpp<DPP_ROW_ROR8>(mx));
+    // the head's greatest logit of the batch: its U logits fill a quad of lanes
+    float mx = fmaxf(z, dpp<DPP_QUAD_XOR1>(z));
+    mx = fmaxf(mx, dpp<DPP_QUAD_XOR2>(mx));
     const bool raise = mx > m_t + RESCALE_SLACK;
     if (__ballot(raise) != 0) {
       const float sc = raise ? weight_exp2(m_t - mx) : 1.f;
       l_t *= sc;
       m_t = raise ? mx : m_t;
-      float scg[G];                             // head g's factor, from lane g
-      row_bcast_all(sc, scg, std::make_integer_sequence<int, (G < 16 ? G : 16)>{});
+      float scg[G];                             // head g's factor, from lane g * U
+      row_bcast_heads(sc, scg, std::make_integer_sequence<int, (G < 16 ? G : 16)>{});
 #pragma unroll
       for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
       for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[(u * G + g) & 15], vf[e], acc[g][e]);
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[(g * U + u) & 15], vf[e], acc[g][e]);
       }
     }
   };
@@ -379,11 +387,11 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     step(base, j, bj, kw, vw);
   }
   if constexpr (TR) {
-    // the head's running sum: its shares sit in lanes t, t-4, t-8, t-12 (mod 16);
-    // lane g (row 0 of the batch) then holds head g's reference and sum
-    float lt = l_t + dpp<DPP_ROW_ROR4>(l_t);
-    lt += dpp<DPP_ROW_ROR8>(lt);
-    if (t < G) { sm_m[slot][t] = m_t; sm_l[slot][t] = lt; }
+    // the head's running sum: its shares fill a quad of lanes; lane g * U then
+    // writes head g's reference and sum
+    float lt = l_t + dpp<DPP_QUAD_XOR1>(l_t);
+    lt += dpp<DPP_QUAD_XOR2>(lt);
+    if (tu == 0) { sm_m[slot][tg] = m_t; sm_l[slot][tg] = lt; }
   }
 
   // ---- combine the 16 slots of this workgroup
