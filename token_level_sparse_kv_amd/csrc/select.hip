@@ -615,7 +615,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   // clamped to the capacity), so they overlap the kernel's first load; later chunks
   // clamp to the sequence.
   constexpr int TPW = 2;
-  constexpr int SPEC = 4;
+  constexpr int SPEC = 5;
   constexpr int CHUNK_T = SEL_WAVES * TPW;
   const uint64_t* cnt_u = counts + (size_t)unit * ntile_cap;
   const uint32_t* cand_u = cand + (size_t)unit * cand_stride;
