@@ -209,20 +209,30 @@ __global__ __launch_bounds__(SEL_UNIT_THREADS) void block_select_kernel(
   const int m = (int)(n / bs);                       // complete blocks (scored)
   const int nb = (int)((n + bs - 1) / bs);           // all blocks
   const int tid = threadIdx.x;
-  if (tid < G) {
-    // each head's softmax normaliser from the tiles' (max, sum) pairs, in tile order
+  const int lane = tid & 63, wave = tid >> 6;
+  static_assert(G <= SEL_UNIT_THREADS / 64, "one wave per query head");
+  if (wave < G) {
+    // head `wave`'s softmax normaliser from the tiles' (max, sum) pairs: lane l
+    // merges tiles l, l + 64, ... in order (all of a wave's loads in flight at
+    // once), then the wave combines its lanes (max, then sum rescaled to it)
     float M = -INFINITY, S = 0.f;
     const int tiles = (m + BLK_TILE - 1) / BLK_TILE;
-    for (int i = 0; i < tiles; ++i) {
-      const float* p = ms + (((size_t)unit * ntile + i) * G + tid) * 2;
+    for (int i = lane; i < tiles; i += 64) {
+      const float* p = ms + (((size_t)unit * ntile + i) * G + wave) * 2;
       const float tm = p[0], ts = p[1];
       if (tm == -INFINITY) continue;
       const float nm = fmaxf(M, tm);
       S = S * exp2f(M - nm) + ts * exp2f(tm - nm);
       M = nm;
     }
-    head_m[tid] = M;
-    head_s[tid] = S > 0.f ? 1.f / S : 0.f;
+    const float wm = wave_max_f32(M);
+    float ws = M == -INFINITY ? 0.f : S * exp2f(M - wm);
+    ws = row16_sum(ws);
+    ws = (readlane_f32(ws, 0) + readlane_f32(ws, 16)) + (readlane_f32(ws, 32) + readlane_f32(ws, 48));
+    if (lane == 0) {
+      head_m[wave] = wm;
+      head_s[wave] = ws > 0.f ? 1.f / ws : 0.f;
+    }
   }
   __syncthreads();
   const bool staged = m <= BLK_LDS_SCORES;
