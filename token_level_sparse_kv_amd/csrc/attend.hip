@@ -12,7 +12,8 @@
 // handles `chunk` consecutive entries of its unit's index list; each slot walks
 // its share of rows, U rows at a time (nontemporal loads: every row is read once),
 // computing the G logits per row (lane t holds head dims 8t..8t+7, dotted as bf16
-// pairs; a DPP row reduction finishes each dot), and keeps an online softmax
+// pairs; DPP row reductions finish the dots: at G = 4 one transposed reduction
+// leaves each lane one of the batch's 16 logits), and keeps an online softmax
 // (reference m, sum l, accumulator acc) per query head in the exp2 domain (logits
 // scaled by sm_scale*log2(e)); the reference is raised only when a logit exceeds it
 // by more than RESCALE_SLACK, so most iterations skip the rescale. Slots are
