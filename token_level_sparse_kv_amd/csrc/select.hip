@@ -716,9 +716,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     uint32_t T = lds_threshold_range(ckey, (int)total, 0u, CAND_REL_MAX, (uint32_t)kk, sh, &needT, &all_eq, true);
     if (needT == 0xffffffffu) all_eq = true;
     const unsigned char* kp_unit = kproj + (size_t)unit * cap * R * KB;
-    int nb = 0;                                   // entries on the boundary truncated key T
+    int nb = 0;                                   // entries on the boundary relative key T
     if (!all_eq && needT > 0) {
-      // only some entries of the boundary truncated key T are taken: list them
+      // only some entries of the boundary relative key T are taken: list them
       uint32_t* bidx = sh.hist2;
       for (int i = tid; i < (int)total; i += SEL_THREADS)
         if (ckey[i] == T) {
