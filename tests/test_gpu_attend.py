@@ -79,3 +79,33 @@ def test_single_selected_row_reproduces_v():
     for g in range(4):
         assert np.array_equal(o[0, g], V[0, 0, 17])
         assert np.array_equal(o[0, 4 + g], V[0, 1, 93])
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_attend_interleaved_invalid_entries_and_growing_logits(G):
+    # invalid entries (-1, other negatives, positions at or past n) sit between valid
+    # ones inside every batch of rows, and the query is scaled up so that later rows
+    # raise the softmax reference again and again (the rescale path)
+    say(f"attend interleaved invalid entries G={G}")
+    B, H, n, k = 1, 2, 3000, 700
+    wl = workloads.gaussian(B, H, G, 128, 16, n, k, seed=31, device="cuda")
+    rng = np.random.default_rng(32)
+    idx = rng.integers(0, n, size=(B, H, k)).astype(np.int32)
+    idx[..., 1::3] = -1
+    idx[..., 2::7] = -7
+    idx[..., 5::11] = n + rng.integers(0, 50)
+    idx[0, 0, :] = np.sort(idx[0, 0, :])            # ascending, as the selection writes them
+    q = wl.q.float() * 2.0
+    wl.q.copy_(q.to(torch.bfloat16))
+    # unit (0, 0): the K rows grow with the position, so its logits keep rising along
+    # the (ascending) list; unit (0, 1) walks its rows in random order
+    Kf = wl.K.float()
+    Kf[0, 0] *= torch.linspace(0.5, 4.0, n, device="cuda")[:, None]
+    wl.K.copy_(Kf.to(torch.bfloat16))
+    idx_t = torch.from_numpy(idx).cuda()
+    qb, Kb, Vb = bits(wl.q), bits(wl.K), bits(wl.V)
+    s = jssa.default_sm_scale(128)
+    ref = _ref(qb, Kb, Vb, idx, [n], G, s)
+    out = sj.attend(wl.q, wl.K, wl.V, idx_t, wl.seq_len, out_f32=True)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= OUT_TOL_F32
