@@ -353,7 +353,7 @@ __device__ __forceinline__ void strided_rank(const bool (&f)[NE], uint32_t (&ran
 // keys equal to T (all of them when all_eq). out[0 .. kept) receives the kept
 // positions in list order (slots at or past `limit` are not written). Returns the
 // kept count.
-__device__ uint32_t compact_candidates(const uint32_t* key_l, const int32_t* pos_l, int cnt, uint32_t T,
+__device__ __forceinline__ uint32_t compact_candidates(const uint32_t* key_l, const int32_t* pos_l, int cnt, uint32_t T,
                                        uint32_t needT, bool all_eq, int32_t* out, uint32_t limit,
                                        SelShared& sh) {
   const int tid = threadIdx.x;
@@ -394,7 +394,7 @@ __device__ uint32_t compact_candidates(const uint32_t* key_l, const int32_t* pos
 }
 
 // Exact top-kk of a dense score row of n >= kk >= 1 entries -> out[0..kk).
-__device__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, SelShared& sh) {
+__device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, SelShared& sh) {
   const int tid = threadIdx.x;
   const int64_t last4 = ((n - 1) >> 2) << 2;     // last float4 start inside the row
   int32_t* listA = reinterpret_cast<int32_t*>(sh.buf);
