@@ -232,3 +232,25 @@ def test_outliers_between_sampled_rows(k):
             assert np.isin(rows, ix[0, h]).all()
         else:
             assert np.isin(ix[0, h], rows).all()
+
+
+def test_many_equal_keys_at_the_boundary_with_shifted_keys():
+    # projected rows c * sign(q_hat): the score grows with c. Most rows take c spread
+    # over [0.1, 4] (a wide key range, so the candidates' relative keys are shifted),
+    # 200 identical rows take c = 2 and the budget ends halfway through them: the
+    # selection meets 200 entries on one relative key and ranks them by exact key,
+    # then by position
+    say("step many equal keys at the boundary")
+    n = 20000
+    wl = workloads.gaussian(1, 1, 4, 128, 16, n, 64, seed=33, device="cuda")
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    qhat = jssa.project_query(jssa.mean_query(q[0, 0:4]), M[0]).astype(np.float64)
+    from oracle.numerics import round_to_bf16, bf16_to_f32 as b2f
+    rng = np.random.default_rng(34)
+    c = b2f(round_to_bf16(rng.uniform(0.1, 4.0, size=n))).astype(np.float64)
+    cluster = np.sort(rng.choice(n, size=200, replace=False))
+    c[cluster] = 2.0
+    kp = round_to_bf16(np.sign(qhat)[None, :] * c[:, None])[None, None]
+    k = int(np.sum(c > 2.0)) + 100
+    _ties_check(wl, np.ascontiguousarray(kp), k, "equal keys at the boundary")
