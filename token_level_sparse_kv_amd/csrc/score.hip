@@ -321,7 +321,7 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
 #pragma unroll
       for (int i = 0; i < LPR; ++i) {
         const int sidx = min(64 * (wave + (t0 + t) * SCORE_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
-        w[t][i] = ld16(base + sample_row<NS>(sidx, n) * R * KB);
+        w[t][i] = ld16_stream(base + sample_row<NS>(sidx, n) * R * KB);
       }
     }
 #pragma unroll
