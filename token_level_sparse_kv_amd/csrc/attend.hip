@@ -62,8 +62,9 @@ __device__ __forceinline__ void row_bcast_heads(float v, float* out, std::intege
 // Transposed sum over the 16 lanes of a DPP row; lane t gets the full sum of value t.
 // Lane t keeps its share of value i ^ ((t >> 2) << 2) in slot i (its caller permutes
 // the upper two index bits by the lane's own), so the first two exchange rounds
-// (partners t ^ 8 and t ^ 7, which flip bit 3, resp. bit 2, of t >> 2) add the
-// partner's upper half of the slots to the lane's lower half without selects; the
+// (partners t ^ 8 and t ^ 7, whose t >> 2 differs from the lane's in bit 1, resp.
+// bit 0) add the partner's upper half of the slots to the lane's lower half without
+// selects; the
 // last two (partners t ^ 2 and t ^ 1) keep the half whose index bit matches the
 // lane's. 15 additions instead of the 64 of sixteen full row sums.
 __device__ __forceinline__ float row16_transpose_sum(const float (&v)[16], int t) {
