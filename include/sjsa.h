@@ -35,9 +35,9 @@
  *     failed check returns a negative status and enqueues nothing. A launch
  *     failure reported by the HIP runtime returns SJSA_ERR_HIP.
  *   - Calls that share a workspace must not overlap (use one stream or order
- *     them). The library's only global mutable state is a launch counter that
- *     tags what the prep workgroups of a fused launch hand to its scan
- *     workgroups, and that hand-over's wait limit (see sjsa_prep_scan).
+ *     them). The library keeps no global mutable state: what one call hands to
+ *     the next (a unit's step count, the candidates of the scan) lives in the
+ *     caller's workspace.
  *   - Results are deterministic: identical inputs give bit-identical outputs.
  */
 #ifndef SJSA_H
@@ -77,6 +77,7 @@ typedef enum sjsa_status {
 #define SJSA_MAX_CAPACITY ((int64_t)1 << 30)
 #define SJSA_MAX_SELECT_UNITS 4096   /* unit (block) budget of the gated and block-sparse steps */
 #define SJSA_MAX_BLOCK_SIZE 4096     /* positions per key block of the block-sparse step */
+#define SJSA_MAX_FUSED_WAIT_US 1000000  /* largest sjsa_shape.fused_wait_us */
 
 typedef struct sjsa_shape {
   int32_t batch;      /* B >= 1 */
@@ -86,6 +87,10 @@ typedef struct sjsa_shape {
   int32_t rank;       /* r: 16, 32 or 64 */
   int32_t flags;      /* 0 or SJSA_FLAG_* bits */
   int64_t capacity;   /* cap: token slots per (b, h) in K, V, Kproj; 1 .. SJSA_MAX_CAPACITY */
+  int32_t fused_wait_us; /* longest wait, in microseconds, of a scan workgroup of the fused
+                            prep + scan launch for what its unit's prep publishes (see
+                            sjsa_prep_scan): 0 = the default 200, negative = no wait, at
+                            most SJSA_MAX_FUSED_WAIT_US. Results never depend on it. */
 } sjsa_shape;
 
 /*
@@ -181,26 +186,22 @@ int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len
 /* Stages 1+2 as the decode steps run them: sjsa_prep (or, with k_new non-NULL,
  * sjsa_prep_append with k_new, v_new, pos, K, V as there) and sjsa_scan in one
  * launch, whose scan workgroups take q_hat, the threshold and the appended row
- * from the prep workgroups as soon as each is published (a workgroup that waits
- * more than about 200 us marks its tile unusable and sjsa_select then handles
- * that unit exactly). Results are those of the separate calls. It must be
- * followed by sjsa_select on the same workspace before the next call of this
- * function there (the workspace carries each unit's step count between calls,
- * which sjsa_select advances; it needs no initialisation). With
- * SJSA_FLAG_WRITE_SCORES it makes the two separate launches.
+ * from the prep workgroups as soon as each is published. A scan workgroup waits
+ * at most shape->fused_wait_us for them (200 us by default; a negative value
+ * means no wait); past that it marks its tile unusable and sjsa_select handles
+ * that unit exactly, so results never depend on the limit. Results are those of
+ * the separate calls. The published words are tagged with each unit's step count,
+ * kept in the workspace and advanced by sjsa_select: every call of this function
+ * must therefore be followed by sjsa_select on the same workspace before the next
+ * call of this function there (the decode steps always pair them). The workspace
+ * needs no initialisation. With SJSA_FLAG_WRITE_SCORES it makes the two separate
+ * launches.
  * Errors: as sjsa_prep_append (K, V, Kproj and pos are checked only when k_new is
  * non-NULL). */
 int sjsa_prep_scan(const sjsa_shape* shape, const void* q, const float* M, void* Kproj,
                    const int32_t* seq_len, int32_t k, const void* k_new, const void* v_new,
                    const int32_t* pos, void* K, void* V, void* workspace, size_t workspace_bytes,
                    void* stream);
-/* The longest a scan workgroup of sjsa_prep_scan (and of the decode steps, which
- * use it) waits for what its unit's prep publishes, in microseconds, for launches
- * made after the call (default 200; negative values count as 0). Past the limit
- * the tile is marked unusable and sjsa_select recomputes the unit exactly, so
- * results never depend on it; 0 exercises that path. Returns the previous limit.
- * Process-wide; safe to call from any thread. */
-int32_t sjsa_set_fused_wait_us(int32_t microseconds);
 
 /* Stage 3: top-k per (b, h) from what sjsa_score left in the workspace -> idx
  * [B, H_kv, k] (Kproj is read again only for a unit whose sampled threshold
@@ -245,8 +246,11 @@ int64_t sjsa_workspace_score_stride(const sjsa_shape* shape);
  *   q [B, H_q, d] bf16; K, V [B, H_kv, cap, d] bf16; seq_len [B] int32
  *   gate_scores [B, H_kv, gate_stride] fp32: the selector's score u of every unit
  *     (gate_stride >= ceil(cap/unit_size)); the gates are g = softmax(u) over the
- *     U_b units of the sequence. Scores should be finite (NaN ranks lowest; the
- *     output is then unspecified).
+ *     U_b units of the sequence. Scores are finite or -inf: a score of -inf gives
+ *     its unit a gate of 0, so its positions get zero weight (lambda = 0 drops the
+ *     gate term altogether); a query head whose kept positions all have zero weight
+ *     gets a zero output. Each sequence with n_b > 0 needs one finite score. NaN and
+ *     +inf are not supported (NaN ranks lowest; the output is then unspecified).
  *   Kept units: every unit when U_b <= k_units, else the current unit plus the
  *     k_units - 1 other units with the largest scores (equal scores: lower unit).
  *   idx [B, H_kv, k_units*unit_size]: the kept units' positions below n_b,

@@ -31,7 +31,11 @@ Readings taken where the page is silent (each is also listed in the design notes
     path, and the gate term is added after scaling: logit = sm_scale*q.k + lambda*ln g;
   * the selected tokens are listed in ascending position, padded with -1 to
     k_units*unit_size entries; n = 0 selects nothing and gives a zero output;
-  * the gate scores u are finite fp32 values (the page's gates lie in (0, 1]).
+  * the gate scores u are fp32 values, finite or -inf; a score of -inf gives its unit
+    the gate softmax assigns it, exactly 0, so its tokens get zero weight (ln g = -inf);
+    each non-empty sequence has at least one finite score. lambda = 0 drops the gate
+    term (lambda * ln g is taken as 0 even where g = 0). When every selected token of a
+    query head has zero weight the output is zero, as for an empty selection.
 """
 from __future__ import annotations
 
@@ -99,6 +103,9 @@ def attend_gated(q_heads_bits, K_bits, V_bits, idx, bias, sm_scale) -> np.ndarra
     out = np.empty((G, d), dtype=np.float64)
     for g in range(G):
         z = (Kd @ qd[g]) * scale + b
+        if not np.isfinite(z.max()):              # every weight is zero (all gates 0)
+            out[g] = 0.0
+            continue
         z = z - z.max()
         p = np.exp(z)
         out[g] = (p / p.sum()) @ Vd
@@ -116,6 +123,7 @@ def gated_decode_unit(q_heads_bits, K_bits, V_bits, u, n, unit_size, k_units, la
     lg = log_gates(np.asarray(u[:U], dtype=np.float32))
     bias = np.zeros(idx.size, dtype=np.float64)
     valid = idx >= 0
-    bias[valid] = float(np.float32(lam)) * lg[idx[valid] // unit_size]
+    if float(np.float32(lam)) != 0.0:
+        bias[valid] = float(np.float32(lam)) * lg[idx[valid] // unit_size]
     out = attend_gated(q_heads_bits, K_bits[:n], V_bits[:n], idx, bias, sm_scale)
     return out, idx, units

@@ -27,10 +27,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def _shape(**kw):
-    base = dict(batch=2, n_kv_heads=8, group=4, head_dim=128, rank=32, capacity=1000, flags=0)
+    base = dict(batch=2, n_kv_heads=8, group=4, head_dim=128, rank=32, capacity=1000, flags=0, fused_wait_us=0)
     base.update(kw)
     s = sj.make_shape(base["batch"], base["n_kv_heads"], base["group"], base["head_dim"], base["rank"],
-                      base["capacity"])
+                      base["capacity"], fused_wait_us=base["fused_wait_us"])
     s.flags = base["flags"]
     return s
 
@@ -67,7 +67,7 @@ def _step(shape, k=16, ws_bytes=1 << 30, ptrs=None, sm_scale=0.0):
     (dict(head_dim=64), -3), (dict(rank=24), -3), (dict(group=3), -3), (dict(group=16), -3),
     (dict(flags=8), -3),
     (dict(batch=0), -2), (dict(capacity=0), -2), (dict(capacity=(1 << 30) + 1), -2),
-    (dict(batch=1000, n_kv_heads=100), -2),
+    (dict(batch=1000, n_kv_heads=100), -2), (dict(fused_wait_us=1000001), -2),
 ])
 def test_bad_shapes(kw, status):
     assert _step(_shape(**kw)) == status
@@ -193,3 +193,24 @@ def test_block_validation():
     assert L.sjsa_block_keys(ctypes.byref(s), 64, f, None, f, None, None, None) == -1  # no seq_len
     assert L.sjsa_block_append(ctypes.byref(s), 64, f, f, 0, f, f, f, f, None, None, None) == -2
     assert L.sjsa_block_append(ctypes.byref(s), 64, f, f, 1, None, f, f, f, None, None, None) == -1
+
+
+def test_shape_struct_layout_matches_the_header(tmp_path):
+    # the binding's ctypes struct has the C layout of sjsa_shape (size and every field
+    # offset), as a C compiler lays it out from include/sjsa.h
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in sj.Shape._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"sjsa.h\"\nint main(void) {\n"
+                   + f'  printf("%zu\\n", sizeof(sjsa_shape));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(sjsa_shape, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(sj.Shape)
+    assert got[1:] == [getattr(sj.Shape, f).offset for f in fields]

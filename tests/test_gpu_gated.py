@@ -127,3 +127,21 @@ def test_gated_toy_by_hand_on_gpu():
         o = out.cpu().numpy()[0]
         assert np.max(np.abs(o[:, :4] - gv.matrix(c["out"]))) < 1e-5
         assert np.all(o[:, 4:] == 0)
+
+
+@pytest.mark.parametrize("unit,k_units", [(64, 32), (1, 300)])
+def test_gated_minus_inf_scores(unit, k_units):
+    # scores of -inf (gate 0), among them the current unit's and the first units' (which
+    # are a thread's first scores in the running softmax sum): the positions they hold get
+    # zero weight, checked against the oracle; (1, 300) runs the separate selection kernel
+    say(f"gated -inf scores unit={unit} k_units={k_units}")
+    seq = [3000, 2049, 640]
+    wl = workloads.gated(3, 2, 4, 3000, unit, k_units, seed=95, device="cuda", capacity=3003, seq_len=seq)
+    gates = wl.extra["gate_scores"].clone()
+    gates[:, :, :3] = -float("inf")
+    gates[:, 0, 5::7] = -float("inf")
+    for b, n in enumerate(seq):
+        gates[b, 1, (n + unit - 1) // unit - 1] = -float("inf")      # the current unit of head 1
+    for lam in (1.0, 0.0):
+        out, _ = _check(wl, unit, k_units, lam, tag=f"-inf scores lam={lam}", gates=gates)
+        assert torch.isfinite(out).all()

@@ -25,13 +25,15 @@ def _cache(wl, fp8):
     return Kp
 
 
-def _step(wl, Kp, q, seq_len, k, mode, new=None, ws=None):
+def _step(wl, Kp, q, seq_len, k, mode, new=None, ws=None, wait_us=0):
     """One step on copies of the caches through the stage calls: mode "separate" (prep
-    or prep_append, then scan) or "fused" (prep_scan); then select and attend.
-    Returns the caches after the step, idx and the fp32 output."""
+    or prep_append, then scan) or "fused" (prep_scan, its scan workgroups waiting at
+    most wait_us for the prep; 0 = the default, negative = no wait); then select and
+    attend. Returns the caches after the step, idx and the fp32 output."""
     fp8 = Kp.dtype == torch.uint8
     K, V, P = wl.K.clone(), wl.V.clone(), Kp.clone()
-    shape = sj.make_shape(wl.batch, wl.n_kv_heads, wl.group, 128, wl.rank, wl.capacity, kproj_fp8=fp8)
+    shape = sj.make_shape(wl.batch, wl.n_kv_heads, wl.group, 128, wl.rank, wl.capacity, kproj_fp8=fp8,
+                          fused_wait_us=wait_us)
     if ws is None:
         ws = sj.alloc_workspace(shape, k)
     if mode == "separate":
@@ -187,8 +189,9 @@ def test_graph_replay_with_new_queries():
 
 
 def test_zero_wait_limit_falls_back_exactly():
-    # scan workgroups that give up waiting mark their tiles unusable; the selection then
-    # recomputes those units exactly, so the results do not change
+    # scan workgroups that do not wait (a negative limit in the shape) mark their tiles
+    # unusable; the selection then recomputes those units exactly, so the results do
+    # not change
     say("prep_scan: zero wait limit")
     wl = workloads.gaussian(4, 2, 4, 128, 32, 30000, 700, seed=85, capacity=30720, device="cuda",
                             seq_len=[30000, 17, 12345, 4096])
@@ -198,12 +201,7 @@ def test_zero_wait_limit_falls_back_exactly():
     k_new, v_new = workloads.new_token(wl, seed=86, T=1)
     new = (k_new, v_new, seq_len - 1)
     ref = _step(wl, Kp, wl.q, seq_len, 700, "separate", new)
-    old = sj.set_fused_wait_us(0)
-    try:
-        got = _step(wl, Kp, wl.q, seq_len, 700, "fused", new)
-    finally:
-        sj.set_fused_wait_us(old)
-    assert old == 200
+    got = _step(wl, Kp, wl.q, seq_len, 700, "fused", new, wait_us=-1)
     _same(ref, got, "zero wait")
     _oracle(wl, got, wl.q, seq, 700, False, "zero wait", [(0, 0), (2, 1), (3, 0)])
 

@@ -145,3 +145,33 @@ def test_empty_and_short_sequences():
     # a single token: the output is its V row
     out, idx, units = sas.gated_decode_unit(q, K, V, u, 1, 8, 3, 1.0, 0.25)
     assert np.max(np.abs(out - bf16_to_f32(V[0]).astype(np.float64)[None])) < 1e-15
+
+
+def test_minus_inf_score_is_a_zero_gate():
+    # softmax gives a score of -inf the gate 0, so that unit's tokens carry no weight:
+    # the output equals the attention over the other selected units' tokens alone (with
+    # lambda = 1 their log gates differ from renormalized ones by one common constant,
+    # which the softmax cancels). The current unit is kept even with a zero gate.
+    rng = np.random.default_rng(7)
+    n, unit, k_units = 200, 16, 5
+    q, K, V = _rand_unit(rng, n)
+    U = sas.n_units(n, unit)
+    u = rng.standard_normal(U).astype(np.float32)
+    u[[0, 3, U - 1]] = -np.inf                      # a kept unit, a dropped one, the current one
+    u[1] = np.float32(5.0)                          # unit 1 is surely kept
+    out, idx, units = sas.gated_decode_unit(q, K, V, u, n, unit, k_units, 1.0, 0.25)
+    assert U - 1 in units and 1 in units and 3 not in units
+    live = [int(i) for i in units if np.isfinite(u[i])]
+    toks = np.concatenate([np.arange(i * unit, min((i + 1) * unit, n)) for i in live])
+    lg = np.log(scipy.special.softmax(u[live].astype(np.float64)))
+    bias = np.repeat(lg, [min((i + 1) * unit, n) - i * unit for i in live])
+    ref = sas.attend_gated(q, K, V, toks, bias, 0.25)
+    assert np.all(np.isfinite(out)) and np.max(np.abs(out - ref)) < 1e-12
+    # lambda = 0 drops the gate term: plain attention over every selected token
+    out0, idx0, _ = sas.gated_decode_unit(q, K, V, u, n, unit, k_units, 0.0, 0.25)
+    assert np.max(np.abs(out0 - jssa.attend(q, K, V, idx0, 0.25))) < 1e-12
+    # every selected unit with gate 0 (only the current unit kept): zero output
+    u2 = np.full(U, -np.inf, dtype=np.float32)
+    u2[0] = 1.0
+    out2, idx2, units2 = sas.gated_decode_unit(q, K, V, u2, n, unit, 1, 1.0, 0.25)
+    assert list(units2) == [U - 1] and np.all(out2 == 0.0)

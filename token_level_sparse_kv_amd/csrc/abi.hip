@@ -26,6 +26,7 @@ int check_shape(const sjsa_shape* s, bool with_rank = true) {
   if (with_rank && s->rank != 16 && s->rank != 32 && s->rank != 64) return SJSA_ERR_UNSUPPORTED;
   if (s->group != 1 && s->group != 2 && s->group != 4 && s->group != 8) return SJSA_ERR_UNSUPPORTED;
   if (s->flags & ~(SJSA_FLAG_OUT_F32 | SJSA_FLAG_WRITE_SCORES | SJSA_FLAG_KPROJ_FP8)) return SJSA_ERR_UNSUPPORTED;
+  if (s->fused_wait_us > SJSA_MAX_FUSED_WAIT_US) return SJSA_ERR_DIMS;
   return SJSA_OK;
 }
 
@@ -293,8 +294,6 @@ int sjsa_prep_scan(const sjsa_shape* shape, const void* q, const float* M, void*
   return status_of(launch_prep_scan(*shape, L, (const uint16_t*)q, M, (const void*)Kproj, seq_len, k,
                                     (unsigned char*)workspace, (hipStream_t)stream, k_new ? &ap : nullptr));
 }
-
-int32_t sjsa_set_fused_wait_us(int32_t microseconds) { return set_fused_wait_us(microseconds); }
 
 int sjsa_select(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len, int32_t k, int32_t* idx,
                 void* workspace, size_t workspace_bytes, void* stream) {

@@ -168,8 +168,12 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       const float x = ug[i];
       gs.su[i] = x;
       const float nm = fmaxf(tm, x);
-      ts = ts * exp2f((tm - nm) * GATE_LOG2E) + exp2f((x - nm) * GATE_LOG2E);   // tm = -inf: ts = 0
-      tm = nm;
+      // a score of -inf (gate 0) adds nothing; skipping it while nothing else has
+      // been seen also keeps (-inf) - (-inf) out of the sum (tm = -inf: ts = 0)
+      if (nm != -INFINITY) {
+        ts = ts * exp2f((tm - nm) * GATE_LOG2E) + exp2f((x - nm) * GATE_LOG2E);
+        tm = nm;
+      }
     }
     const float wm = wave_max_f32(tm);
     float ws = wm == -INFINITY ? 0.f : ts * exp2f((tm - wm) * GATE_LOG2E);
@@ -200,7 +204,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         const int64_t pos = (int64_t)ku * ga.unit_size + (e - sl * ga.unit_size);
         if (pos < n) {
           p = (int32_t)pos;
-          bt = ga.lam * ((gs.su[ku] - mx) * GATE_LOG2E - lse2);
+          // lambda = 0 drops the gate term (also for a gate of 0: 0 * -inf)
+          bt = ga.lam == 0.f ? 0.f : ga.lam * ((gs.su[ku] - mx) * GATE_LOG2E - lse2);
         }
       }
       sidx[i] = p;

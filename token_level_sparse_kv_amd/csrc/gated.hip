@@ -50,8 +50,12 @@ __global__ __launch_bounds__(SEL_UNIT_THREADS) void gate_select_kernel(
     const float x = ug[i];
     if (staged) su[i] = x;
     const float nm = fmaxf(tm, x);
-    ts = ts * exp2f((tm - nm) * GATE_LOG2E) + exp2f((x - nm) * GATE_LOG2E);   // tm = -inf: ts = 0
-    tm = nm;
+    // a score of -inf (gate 0) adds nothing; skipping it while nothing else has
+    // been seen also keeps (-inf) - (-inf) out of the sum (tm = -inf: ts = 0)
+    if (nm != -INFINITY) {
+      ts = ts * exp2f((tm - nm) * GATE_LOG2E) + exp2f((x - nm) * GATE_LOG2E);
+      tm = nm;
+    }
   }
   const float wm = wave_max_f32(tm);
   float ws = wm == -INFINITY ? 0.f : ts * exp2f((tm - wm) * GATE_LOG2E);
@@ -74,7 +78,8 @@ __global__ __launch_bounds__(SEL_UNIT_THREADS) void gate_select_kernel(
   const uint32_t nsel = select_kept_units(
       U, all, k_units - 1, score, [&](int i) { return i == cur; }, [&](int i) { return i < cur; }, sh);
   for (int s = tid; s < (int)nsel; s += SEL_UNIT_THREADS)
-    sel_bias[s] = lam * ((score(sh.kept[s]) - mx) * GATE_LOG2E - lse2);
+    // lambda = 0 drops the gate term (also for a gate of 0, where lambda * ln g is 0 * -inf)
+    sel_bias[s] = lam == 0.f ? 0.f : lam * ((score(sh.kept[s]) - mx) * GATE_LOG2E - lse2);
   __syncthreads();
 
   float* ob = bias + (size_t)unit * ktok;

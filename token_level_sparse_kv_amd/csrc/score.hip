@@ -23,8 +23,6 @@
 // 64-bit words; the scan workgroups read q_hat as soon as it is published, stream
 // and score their whole tile, and only then need the threshold, so the prep runs
 // under the scan's memory stream instead of before it.
-#include <atomic>
-
 #include "key_proj.h"
 
 namespace sjsa {
@@ -43,21 +41,23 @@ constexpr int PREP_SAMPLES = 2048;
 constexpr int PREP_PASS = 1;         // sample batches per load pass (bounds the registers)
 constexpr int PREP_BINS = 4096;      // linear score bins of the threshold histogram
 constexpr uint32_t TAG_MULT = 0x9E3779B1u;
-// A scan wave waits at most this long for a published word (microseconds; 200 by
-// default, far above a prep's duration); past it the tile reports TILE_OVERFLOW and
-// the selection recomputes the unit exactly. The device's real-time counter runs at
-// 100 MHz.
-std::atomic<int32_t> g_wait_us{200};
+constexpr uint32_t TAG_ADD = 0x7F4A7C15u;
+// A scan wave waits at most sjsa_shape.fused_wait_us for a published word (200 us
+// when the field is 0, far above a prep's duration); past it the tile reports
+// TILE_OVERFLOW and the selection recomputes the unit exactly. The device's
+// real-time counter runs at 100 MHz.
+constexpr int32_t DEFAULT_WAIT_US = 200;
 constexpr uint64_t TICKS_PER_US = 100;
 
 static_assert(SEG_ROWS == GROUP_ROWS * SCORE_UNROLL, "one wave iteration covers one segment");
 static_assert(SEGS_PER_TILE <= 64, "one wave scans the segment counts");
 
-// Tag of the words one launch publishes for a unit: the step count of the unit on
-// this workspace (advanced by the selection) and a per-launch number from the host,
-// so words left by an earlier launch never carry the current tag.
-__device__ __forceinline__ uint32_t launch_tag(const uint32_t* epoch, int unit, uint32_t nonce) {
-  return (epoch[unit] + 1u) * TAG_MULT + nonce;
+// Tag of the words one launch publishes for a unit: a function of the unit's step
+// count on this workspace, which the selection that follows every fused launch
+// advances by one, so words left by the previous launch (or an earlier replay of a
+// captured graph) never carry the current tag. Distinct counts give distinct tags.
+__device__ __forceinline__ uint32_t launch_tag(const uint32_t* epoch, int unit) {
+  return (epoch[unit] + 1u) * TAG_MULT + TAG_ADD;
 }
 
 __device__ __forceinline__ void publish(uint64_t* w, uint32_t tag, uint32_t v) {
@@ -695,17 +695,17 @@ constexpr int fused_waves() { return R <= 32 ? (KB == 2 ? 8 : 7) : (KB == 2 ? 5 
 template <int R, int KB, bool APPEND>
 __global__ __launch_bounds__(SCORE_THREADS) __attribute__((amdgpu_waves_per_eu(fused_waves<R, KB>()))) void prep_scan_kernel(PrepArgs pa, PrepAppend ap, ScanArgs sa,
                                                                   uint64_t* sync, const uint32_t* epoch,
-                                                                  int units, uint32_t nonce, uint64_t wait_ticks) {
+                                                                  int units, uint64_t wait_ticks) {
   __shared__ ScoreShared sh;
   const int64_t bid = blockIdx.x;
   if (bid < units) {
     const int unit = (int)bid;
-    prep_body<R, KB, APPEND, true>(sh.p, unit, pa, ap, sync, launch_tag(epoch, unit, nonce));
+    prep_body<R, KB, APPEND, true>(sh.p, unit, pa, ap, sync, launch_tag(epoch, unit));
   } else {
     const int64_t id = bid - units;
     const int unit = (int)(id / sa.ntile_cap);
     const int tile = (int)(id - (int64_t)unit * sa.ntile_cap);
-    scan_body<R, KB, false, true>(sh.s, unit, tile, sa, sync, launch_tag(epoch, unit, nonce),
+    scan_body<R, KB, false, true>(sh.s, unit, tile, sa, sync, launch_tag(epoch, unit),
                                   APPEND ? ap.pos : nullptr, wait_ticks);
   }
 }
@@ -801,8 +801,6 @@ hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t
     hipError_t e = launch_prep(s, L, q, M, kproj_v, seq_len, k, ws, st, ap);
     return e == hipSuccess ? launch_score(s, L, kproj_v, seq_len, ws, st) : e;
   }
-  static std::atomic<uint32_t> launches{1u};
-  const uint32_t nonce = launches.fetch_add(1u, std::memory_order_relaxed);
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
   const unsigned char* kproj = static_cast<const unsigned char*>(kproj_v);
   const PrepArgs pa = prep_args(s, L, q, M, kproj, seq_len, k, ws);
@@ -812,10 +810,11 @@ hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t
   const dim3 grid((unsigned)blocks), block(SCORE_THREADS);
   const PrepAppend none{};
   const int units = (int)L.units;
-  const uint64_t wait = (uint64_t)g_wait_us.load(std::memory_order_relaxed) * TICKS_PER_US;
+  const int32_t wait_us = s.fused_wait_us == 0 ? DEFAULT_WAIT_US : (s.fused_wait_us < 0 ? 0 : s.fused_wait_us);
+  const uint64_t wait = (uint64_t)wait_us * TICKS_PER_US;
 #define SJSA_PS2(RR, KB)                                                                                     \
-  if (ap) prep_scan_kernel<RR, KB, true><<<grid, block, 0, st>>>(pa, *ap, sa, sync, epoch, units, nonce, wait); \
-  else prep_scan_kernel<RR, KB, false><<<grid, block, 0, st>>>(pa, none, sa, sync, epoch, units, nonce, wait)
+  if (ap) prep_scan_kernel<RR, KB, true><<<grid, block, 0, st>>>(pa, *ap, sa, sync, epoch, units, wait); \
+  else prep_scan_kernel<RR, KB, false><<<grid, block, 0, st>>>(pa, none, sa, sync, epoch, units, wait)
 #define SJSA_PS(RR) if (fp8) { SJSA_PS2(RR, 1); } else { SJSA_PS2(RR, 2); }
   switch (s.rank) {
     case 16: SJSA_PS(16); break;
@@ -827,7 +826,5 @@ hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t
 #undef SJSA_PS2
   return hipGetLastError();
 }
-
-int32_t set_fused_wait_us(int32_t us) { return g_wait_us.exchange(us < 0 ? 0 : us); }
 
 }  // namespace sjsa

@@ -87,8 +87,6 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj,
 hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
                             const void* kproj, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
                             const PrepAppend* ap = nullptr);
-// Wait limit of the fused launch's scan workgroups (microseconds); returns the old one.
-int32_t set_fused_wait_us(int32_t us);
 // scores == nullptr: select from the scan's candidates in the workspace (recomputing a
 // unit's scores from kproj/qhat when needed); else exact top-k of the given dense scores.
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,

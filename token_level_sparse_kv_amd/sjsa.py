@@ -39,6 +39,7 @@ class Shape(ctypes.Structure):
         ("rank", ctypes.c_int32),
         ("flags", ctypes.c_int32),
         ("capacity", ctypes.c_int64),
+        ("fused_wait_us", ctypes.c_int32),
     ]
 
 
@@ -60,7 +61,6 @@ _SIGS = {
     "sjsa_scan": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_size_t, _P]),
     "sjsa_prep_scan": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
-    "sjsa_set_fused_wait_us": (ctypes.c_int32, [ctypes.c_int32]),
     "sjsa_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
     "sjsa_attend": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_float,
                                    _P, _P, ctypes.c_size_t, _P]),
@@ -108,10 +108,13 @@ def _check(status: int):
 
 
 def make_shape(batch, n_kv_heads, group, head_dim, rank, capacity, out_f32=False, write_scores=False,
-               kproj_fp8=False) -> Shape:
+               kproj_fp8=False, fused_wait_us=0) -> Shape:
+    """fused_wait_us: how long a scan workgroup of the fused prep + scan launch waits for
+    its unit's prep (0: the library default of 200 us; negative: no wait, so every unit
+    takes the exact path)."""
     flags = ((SJSA_FLAG_OUT_F32 if out_f32 else 0) | (SJSA_FLAG_WRITE_SCORES if write_scores else 0)
              | (SJSA_FLAG_KPROJ_FP8 if kproj_fp8 else 0))
-    return Shape(batch, n_kv_heads, group, head_dim, rank, flags, capacity)
+    return Shape(batch, n_kv_heads, group, head_dim, rank, flags, capacity, fused_wait_us)
 
 
 def kproj_is_fp8(Kproj: torch.Tensor) -> bool:
@@ -330,11 +333,6 @@ def prep_scan(shape: Shape, q, M, Kproj, seq_len, k, workspace, k_new=None, v_ne
     _check(lib().sjsa_prep_scan(ctypes.byref(shape), _ptr(q), _ptr(M), _ptr(Kproj), _ptr(seq_len), int(k),
                                 _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(K), _ptr(V), _ptr(workspace),
                                 workspace.numel(), _stream(stream)))
-
-
-def set_fused_wait_us(microseconds: int) -> int:
-    """Wait limit of the fused prep + scan launch's scan workgroups; returns the old one."""
-    return int(lib().sjsa_set_fused_wait_us(int(microseconds)))
 
 
 def select(shape: Shape, Kproj, seq_len, k, workspace, idx=None, stream=None):
