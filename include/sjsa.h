@@ -58,7 +58,8 @@ typedef enum sjsa_status {
   SJSA_ERR_K = -4,           /* k < 1 or above SJSA_MAX_K */
   SJSA_ERR_WORKSPACE = -5,   /* workspace smaller than the size query returns */
   SJSA_ERR_HIP = -6,         /* the HIP runtime reported a launch error */
-  SJSA_ERR_ALIGN = -7        /* a pointer is not aligned as required */
+  SJSA_ERR_ALIGN = -7,       /* a pointer is not aligned as required */
+  SJSA_ERR_SCRATCH = -8      /* the step needs more than the static scratch array holds */
 } sjsa_status;
 
 /* sjsa_shape.flags bits.
@@ -153,6 +154,29 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
                             const float* M, const int32_t* seq_len, int32_t k, float sm_scale,
                             void* out, int32_t* idx, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * sjsa_decode_step_append with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. The step's scratch memory is a static array
+ * inside the library, SJSA_NOALLOC_SCRATCH_BYTES on each GPU the library is loaded
+ * on, held until the process ends; the call itself allocates and frees nothing.
+ * A shape whose workspace (sjsa_decode_workspace_size(shape, k)) is larger is
+ * rejected with SJSA_ERR_SCRATCH before anything is enqueued (with 131072 token
+ * slots, r = 32 and k = 4096 that allows up to 56 (sequence, KV head) pairs; one
+ * sequence of 32768 tokens with 8 KV heads and k = 2048 needs 2.5 MiB).
+ * Every call on one GPU uses that GPU's one array, which keeps the previous call's
+ * contents (the step, like a fresh workspace, needs nothing cleared): calls that
+ * overlap on one GPU (on different streams, or from host threads without ordering)
+ * race and give undefined results. `stream` must belong to the current device.
+ * Arguments and results as sjsa_decode_step_append, bit for bit.
+ * Errors: as sjsa_decode_step_append, and SJSA_ERR_SCRATCH.
+ */
+#define SJSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sjsa_decode_step_append_noalloc(const sjsa_shape* shape, const void* k_new, const void* v_new,
+                                    const int32_t* pos, const void* q, void* K, void* V, void* Kproj,
+                                    const float* M, const int32_t* seq_len, int32_t k, float sm_scale,
+                                    void* out, int32_t* idx, void* stream);
 
 /*
  * Stage 1+2 of the step: scoring prep (q_bar, q_hat; section 打分误差的定义)

@@ -214,3 +214,19 @@ def test_shape_struct_layout_matches_the_header(tmp_path):
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     assert got[0] == ctypes.sizeof(sj.Shape)
     assert got[1:] == [getattr(sj.Shape, f).offset for f in fields]
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    # the allocation-free step checks the shape's workspace against its static scratch
+    # array before touching the device: 16 x 8 units at 131072 slots need ~136 MiB
+    big = sj.make_shape(16, 8, 4, 128, 32, 131072)
+    assert sj.workspace_size(big, 4096) > sj.NOALLOC_SCRATCH_BYTES
+    L = sj.lib()
+    p = [ctypes.c_void_p(FAKE)] * 12
+    st = L.sjsa_decode_step_append_noalloc(ctypes.byref(big), *p[:9], 4096, 0.0, p[9], p[10], None)
+    assert st == -8
+    assert "static array" in L.sjsa_status_string(-8).decode()
+    # invalid shapes and budgets are reported as for the workspace form
+    assert L.sjsa_decode_step_append_noalloc(ctypes.byref(_shape(rank=24)), *p[:9], 16, 0.0, p[9], p[10],
+                                             None) == -3
+    assert L.sjsa_decode_step_append_noalloc(ctypes.byref(_shape()), *p[:9], 0, 0.0, p[9], p[10], None) == -4

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "sjsa_internal.h"
 
 namespace sjsa {
@@ -153,6 +155,8 @@ const char* sjsa_status_string(int status) {
     case SJSA_ERR_WORKSPACE: return "workspace is smaller than required";
     case SJSA_ERR_HIP: return "the HIP runtime reported a launch error";
     case SJSA_ERR_ALIGN: return "a pointer is not aligned as required";
+    case SJSA_ERR_SCRATCH:
+      return "the step needs more scratch memory than the library's static array holds (SJSA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -391,6 +395,54 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
     e = launch_attend(*shape, L, (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, idx, k, seq_len,
                       resolve_scale(sm_scale), out, ws, s);
   return status_of(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch memory of sjsa_decode_step_append_noalloc: a static device array, one copy
+// per GPU the library is loaded on. In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the device address from hipGetSymbolAddress, taken
+// once per device (with that device current) and kept here.
+__device__ __align__(256) unsigned char scratch[SJSA_NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current device's scratch array (null on failure). Threads
+// that race on a device's first call both store the same address.
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sjsa_decode_step_append_noalloc(const sjsa_shape* shape, const void* k_new, const void* v_new,
+                                    const int32_t* pos, const void* q, void* K, void* V, void* Kproj,
+                                    const float* M, const int32_t* seq_len, int32_t k, float sm_scale,
+                                    void* out, int32_t* idx, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (make_layout(*shape, k).total > SJSA_NOALLOC_SCRATCH_BYTES) return SJSA_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SJSA_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess || sdev != dev) return SJSA_ERR_HIP;
+  }
+  void* ws = scratch_ptr(dev);
+  if (!ws) return SJSA_ERR_HIP;
+  return sjsa_decode_step_append(shape, k_new, v_new, pos, q, K, V, Kproj, M, seq_len, k, sm_scale, out, idx, ws,
+                                 SJSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t sjsa_gated_workspace_size(const sjsa_shape* shape, int32_t unit_size, int32_t k_units) {

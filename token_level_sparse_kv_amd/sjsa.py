@@ -53,6 +53,8 @@ _SIGS = {
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "sjsa_decode_step_append": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                ctypes.c_int32, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sjsa_decode_step_append_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                       _P, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "sjsa_prep_append": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                         _P, ctypes.c_size_t, _P]),
     "sjsa_score": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t,
@@ -266,6 +268,26 @@ def decode_step_append(k_new, v_new, pos, q, K, V, Kproj, M, seq_len, k, sm_scal
                                          float(sm_scale), _ptr(out), _ptr(idx), _ptr(workspace),
                                          workspace.numel(), _stream(stream)))
     return out, idx
+
+
+def decode_step_append_noalloc(k_new, v_new, pos, q, K, V, Kproj, M, seq_len, k, out, idx, sm_scale=0.0,
+                               out_f32=False, stream=None):
+    """decode_step_append with the library's static scratch array instead of a
+    workspace: the call allocates nothing (out and idx must be given). Shapes whose
+    workspace exceeds the array are rejected (SjsaError, SJSA_ERR_SCRATCH). Calls that
+    overlap on one GPU race. Returns (out, idx)."""
+    _step_checks(q, K, V, Kproj, M, seq_len)
+    _append_one_checks(k_new, v_new, pos, K, M)
+    shape = shape_of(q, K, M, out_f32, Kproj)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, q.shape)
+    _need(idx, "idx", torch.int32, (shape.batch, shape.n_kv_heads, int(k)))
+    _check(lib().sjsa_decode_step_append_noalloc(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(q),
+                                                 _ptr(K), _ptr(V), _ptr(Kproj), _ptr(M), _ptr(seq_len), int(k),
+                                                 float(sm_scale), _ptr(out), _ptr(idx), _stream(stream)))
+    return out, idx
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def score(q, Kproj, M, seq_len, k, workspace, write_scores=False, stream=None):
