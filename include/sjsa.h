@@ -90,8 +90,10 @@ typedef struct sjsa_shape {
   int64_t capacity;   /* cap: token slots per (b, h) in K, V, Kproj; 1 .. SJSA_MAX_CAPACITY */
   int32_t fused_wait_us; /* longest wait, in microseconds, of a scan workgroup of the fused
                             prep + scan launch for what its unit's prep publishes (see
-                            sjsa_prep_scan): 0 = the default 200, negative = no wait, at
-                            most SJSA_MAX_FUSED_WAIT_US. Results never depend on it. */
+                            sjsa_prep_scan): 0 = the default 200; negative = the scan
+                            workgroups do not take what the prep publishes at all, so every
+                            unit is selected by the exact path (for testing and measuring
+                            it); at most SJSA_MAX_FUSED_WAIT_US. Results never depend on it. */
 } sjsa_shape;
 
 /*
@@ -183,9 +185,11 @@ int sjsa_decode_step_append_noalloc(const sjsa_shape* shape, const void* k_new, 
  * and the full-context score scan over Kproj (section 原理详解(二): scoring
  * still scans every candidate position). The scan keeps, per (b, h), only the
  * positions whose score reaches a threshold placed by the prep stage from a
- * sample of 2048 evenly spaced rows, low enough that the exact top k is among
- * them in all but misjudged cases (which sjsa_select detects and resolves
- * exactly); hence the budget k is an argument. With SJSA_FLAG_WRITE_SCORES the
+ * sample of 2048 rows (one adjacent pair in each of 1024 equal strata, at an
+ * offset drawn anew for every unit and step), low enough that the exact top k is
+ * among them in all but misjudged cases (which sjsa_select detects and resolves
+ * exactly: it then recomputes the unit's scores and selects over all of them);
+ * hence the budget k is an argument. With SJSA_FLAG_WRITE_SCORES the
  * scan also stores every fp32 score: that of (b, h, j) is at float offset
  * sjsa_workspace_scores_offset(shape)/4 + (b*H_kv + h)*stride + j, stride =
  * sjsa_workspace_score_stride(shape).
@@ -212,8 +216,8 @@ int sjsa_scan(const sjsa_shape* shape, const void* Kproj, const int32_t* seq_len
  * launch, whose scan workgroups take q_hat, the threshold and the appended row
  * from the prep workgroups as soon as each is published. A scan workgroup waits
  * at most shape->fused_wait_us for them (200 us by default; a negative value
- * means no wait); past that it marks its tile unusable and sjsa_select handles
- * that unit exactly, so results never depend on the limit. Results are those of
+ * means it never takes them); past that it marks its tile unusable and
+ * sjsa_select handles that unit exactly, so results never depend on the limit. Results are those of
  * the separate calls. The published words are tagged with each unit's step count,
  * kept in the workspace and advanced by sjsa_select: every call of this function
  * must therefore be followed by sjsa_select on the same workspace before the next

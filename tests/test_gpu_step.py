@@ -254,3 +254,57 @@ def test_many_equal_keys_at_the_boundary_with_shifted_keys():
     kp = round_to_bf16(np.sign(qhat)[None, :] * c[:, None])[None, None]
     k = int(np.sum(c > 2.0)) + 100
     _ties_check(wl, np.ascontiguousarray(kp), k, "equal keys at the boundary")
+
+
+def test_saturated_boundary_ties_resolve_by_position():
+    # 300 outliers between the sampled rows (their candidate keys saturate) in four groups
+    # of identical rows: the budget of 100 takes the whole top group and part of the
+    # next, so the selection meets 300 entries on the saturated relative key, ranks them
+    # by exact key and breaks the ties by position, exactly as the oracle does
+    say("step saturated boundary with ties")
+    n, k = 40000, 100
+    wl = workloads.gaussian(1, 1, 4, 128, 16, n, k, seed=36, device="cuda")
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    kp = kproj_oracle(bits(wl.K), M)
+    from oracle.numerics import round_to_bf16
+    starts = 2 * ((np.arange(1024, dtype=np.int64) * n) // 2048)
+    rows = (starts + 7)[:300]
+    assert not np.isin(rows, np.concatenate([starts, starts + 1])).any()
+    qhat = jssa.project_query(jssa.mean_query(q[0, 0:4]), M[0]).astype(np.float64)
+    mag = np.array([64.0, 80.0, 96.0, 112.0])[np.random.default_rng(37).integers(0, 4, size=300)]
+    kp[0, 0, rows] = round_to_bf16(np.sign(qhat)[None, :] * mag[:, None])
+    assert np.sum(mag == 112.0) < k < np.sum(mag >= 96.0)
+    _ties_check(wl, kp, k, "saturated boundary ties")
+
+
+def test_units_on_different_paths_in_one_launch():
+    # one launch where unit (0,0) has every row identical (its 20001 candidates overflow
+    # the lists), (1,0) has the first row of every sampled pair scoring high (1024
+    # candidates, fewer than k) and (0,1), (1,1) are ordinary: the exact-path units are
+    # recomputed by two workgroups each (over lengths that split unevenly), the others
+    # select from their candidates
+    say("step units on different paths")
+    n, k = 20001, 1500
+    seq = [20001, 18000]
+    wl = workloads.gaussian(2, 2, 4, 128, 16, n, k, seed=38, device="cuda", capacity=20001, seq_len=seq)
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    kp = kproj_oracle(bits(wl.K), M)
+    kp[0, 0, :] = kp[0, 0, :1]
+    qhat = jssa.project_query(jssa.mean_query(q[1, 0:4]), M[0]).astype(np.float64)
+    from oracle.numerics import round_to_bf16
+    first_of_pair = 2 * ((np.arange(1024, dtype=np.int64) * 18000) // 2048)
+    kp[1, 0, :] = kp[1, 0, :1]
+    kp[1, 0, first_of_pair] = round_to_bf16(np.sign(qhat) * 4.0)
+    _ties_check(wl, np.ascontiguousarray(kp), k, "mixed paths")
+
+
+def test_blind_spot_input_takes_the_exact_path():
+    # the sampled rows are the quietest of every sequence (keys x 1/16): the threshold
+    # falls far below the k-th score, every unit's candidates exceed the lists and the
+    # exact path selects; every unit against the oracle
+    say("step sampler blind spot")
+    wl = workloads.long_batched_blind_spot(batch=2, n=32768, k=2048, device="cuda")
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    _run_and_check(wl, kp, 2048, out_f32=False, tag="blind spot")

@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsjsa.so")
+# the benchmark's read-bandwidth probe, kept out of the decode library
+MEMBW_SRC = "membw.hip"
+MEMBW_LIB = os.path.join(LIBDIR, "libsjsa_membw.so")
 OBJDIR = os.path.join(ROOT, "_build", "sjsa")
 
 SOURCES = ["abi.hip", "append.hip", "score.hip", "select.hip", "attend.hip", "gated.hip", "blocks.hip", "calib.hip"]
@@ -49,15 +52,16 @@ def build(jobs: int = 5, verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+        objs = list(ex.map(_compile, SOURCES + [MEMBW_SRC]))
+    for lib, parts in ((LIB, objs[:-1]), (MEMBW_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *parts]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

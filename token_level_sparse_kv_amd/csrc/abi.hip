@@ -67,6 +67,10 @@ Layout make_layout(const sjsa_shape& s, int k) {
   off = align_up(off + (size_t)L.units * SYNC_WORDS * sizeof(uint64_t), WS_ALIGN);
   L.off_counts = off;
   off = align_up(off + (size_t)L.units * L.ntile_cap * sizeof(uint64_t), WS_ALIGN);
+  L.off_arrive = off;
+  off = align_up(off + (size_t)L.units * sizeof(uint32_t), WS_ALIGN);
+  L.off_parthist = off;
+  off = align_up(off + (size_t)L.units * EXACT_WGS * HIST_BINS * sizeof(uint32_t), WS_ALIGN);
   L.off_cand = off;
   off = align_up(off + (size_t)L.units * L.cand_stride * sizeof(uint32_t), WS_ALIGN);
   L.off_scores = off;

@@ -9,7 +9,7 @@
 //
 // prep  (one workgroup per (b, h)): q_bar in fp32 (sum in head order, then divide
 //       by G), q_hat = M_h q_bar (fp32), and the unit's candidate threshold, placed
-//       from the scores of evenly spaced sample rows.
+//       from the scores of sample rows (one adjacent pair in each of 1024 strata).
 // scan  (one workgroup per 4096-row tile of a unit): streams Kproj rows with
 //       128-bit coalesced loads, each lane holding 8 of a row's r values; the
 //       partial dots of the r/8 lanes of a row are reduced with DPP lane moves in a
@@ -126,13 +126,31 @@ __device__ uint32_t prep_block_scan(uint32_t v, uint32_t* scan_lds, uint32_t* to
   return inc + before;
 }
 
+// MurmurHash3's 32-bit finalizer (fmix32): a bijective avalanche mix of a 32-bit word.
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
 // Row of sample s (0 <= s < min(NS, n)): every row when n <= NS; else the samples
-// come in adjacent pairs (2i, 2i + 1 share a 128-byte cache line whenever a
-// projected row is at most 64 bytes), the pairs evenly spaced over the sequence.
+// come in adjacent pairs (2j, 2j + 1 share a 128-byte cache line whenever a projected
+// row is at most 64 bytes), one pair in each of NS/2 equal strata of the sequence
+// (stratum i holds the pairs floor(i n / NS) .. floor((i+1) n / NS) - 1), at an offset
+// inside its stratum drawn from `seed` (which changes from unit to unit and step to
+// step): stratified like evenly spaced samples, but a fixed arrangement of the keys
+// cannot keep its largest scores out of the sample step after step.
 template <int NS>
-__device__ __forceinline__ int64_t sample_row(int s, int64_t n) {
+__device__ __forceinline__ int64_t sample_row(int s, int64_t n, uint32_t seed) {
   if (n <= NS) return s;
-  return 2 * (((int64_t)(s >> 1) * n) / NS) + (s & 1);
+  const int64_t i = s >> 1;
+  const int64_t a = (i * n) / NS, w = ((i + 1) * n) / NS - a;      // w >= 1 pairs in the stratum
+  const uint32_t h = fmix32(seed ^ ((uint32_t)i * 0x9E3779B9u));
+  const int64_t j = (int64_t)(((uint64_t)h * (uint64_t)w) >> 32);  // uniform in [0, w)
+  return 2 * (a + j) + (s & 1);
 }
 
 struct PrepArgs {
@@ -143,6 +161,8 @@ struct PrepArgs {
   int k;
   float* qhat;
   uint32_t* tlow;
+  uint32_t* arrive;           // the unit's exact-path arrival counter, reset here each step
+  const uint32_t* epoch;      // the unit's step count (seeds the sample positions)
   int n_kv_heads;
   int group;
   int64_t cap;
@@ -151,8 +171,9 @@ struct PrepArgs {
 // Prep of one unit (b, h), 256 threads.
 //  * q_bar in fp32 (sum in head order, then divide by G) and q_hat = M_h q_bar: output
 //    i is split over 16 lanes of 8 channels each (fp32 partial dots, DPP row sum).
-//  * Threshold for the scan: the scores of NS rows (evenly spaced pairs of adjacent
-//    rows; all rows when n <= NS) are binned linearly between their least and
+//  * Threshold for the scan: the scores of NS rows (pairs of adjacent rows, one pair
+//    per stratum at a drawn offset, see sample_row; all rows when n <= NS) are
+//    binned linearly between their least and
 //    greatest finite value (+inf in the top bin, -inf and NaN left out); the bin
 //    that holds the sample of rank m (see below) is found, and the least key in it
 //    becomes the unit's candidate threshold, so at least m samples reach it. The
@@ -244,7 +265,11 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
     sh.qraw[tid >> 4][part * 4 + 3] = qw.w;
   }
   for (int i = tid; i < PREP_BINS; i += SCORE_THREADS) sh.hist[i] = 0u;
-  if (tid == 0) { sh.misc[0] = 0xffffffffu; sh.misc[2] = 0u; }
+  if (tid == 0) {
+    sh.misc[0] = 0xffffffffu;
+    sh.misc[2] = 0u;
+    a.arrive[unit] = 0u;      // the selection launch that follows counts its exact-path workgroups here
+  }
   __syncthreads();
   if constexpr (APPEND && PUBLISH) {
     if (tid < RW) publish(sw + SYNC_ROW + tid, tag, sh.row[tid]);
@@ -300,8 +325,9 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
   }
   __syncthreads();                                    // sh.qh complete
   const int S = (int)min((int64_t)NS, n);
+  const uint32_t seed = fmix32((uint32_t)unit * 0x632BE5ABu + a.epoch[unit] * 0x85157AF5u);
 
-  // sample s sits in row pos(s) (evenly spaced); wave-wide loads as in the scan: in
+  // sample s sits in row sample_row(s) (one adjacent pair per stratum); wave-wide loads as in the scan: in
   // batch t a wave covers samples sb .. sb + 63 (sb = 64 * (wave + t * waves)), load
   // i reading 16 bytes (lane column p) of sample sb + i * RPL + rs, so the LPR lanes
   // of a sample read its row contiguously; the lane is left the score of sample
@@ -321,7 +347,7 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
 #pragma unroll
       for (int i = 0; i < LPR; ++i) {
         const int sidx = min(64 * (wave + (t0 + t) * SCORE_WAVES) + i * RPL + rs, S - 1);   // clamped: not binned
-        w[t][i] = ld16_stream(base + sample_row<NS>(sidx, n) * R * KB);
+        w[t][i] = ld16_stream(base + sample_row<NS>(sidx, n, seed) * R * KB);
       }
     }
 #pragma unroll
@@ -541,7 +567,7 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
       u32x4 w[SCORE_UNROLL][LPR];
       load_seg(g0, w);
       uint32_t v;
-      ok = poll_words(sw, R, tag, deadline, v);
+      ok = wait_ticks != 0 && poll_words(sw, R, tag, deadline, v);   // 0: never take them
       if (ok) {
         if (lane < R) sh.words[wave][lane] = v;
 #pragma unroll
@@ -720,6 +746,8 @@ PrepArgs prep_args(const sjsa_shape& s, const Layout& L, const uint16_t* q, cons
   a.k = k;
   a.qhat = reinterpret_cast<float*>(ws + L.off_qhat);
   a.tlow = reinterpret_cast<uint32_t*>(ws + L.off_tlow);
+  a.arrive = reinterpret_cast<uint32_t*>(ws + L.off_arrive);
+  a.epoch = reinterpret_cast<const uint32_t*>(ws + L.off_epoch);
   a.n_kv_heads = s.n_kv_heads;
   a.group = s.group;
   a.cap = s.capacity;

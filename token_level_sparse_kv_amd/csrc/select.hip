@@ -393,8 +393,11 @@ __device__ __forceinline__ uint32_t compact_candidates(const uint32_t* key_l, co
   return baseS;
 }
 
-// Exact top-kk of a dense score row of n >= kk >= 1 entries -> out[0..kk).
-__device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, SelShared& sh) {
+// Exact top-kk of a dense score row of n >= kk >= 1 entries -> out[0..kk). With
+// hist_ready the caller has already counted the row's keys by their top 12 bits into
+// sh.hist (the first radix digit).
+__device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk, int32_t* out, SelShared& sh,
+                                             bool hist_ready = false) {
   const int tid = threadIdx.x;
   const int64_t last4 = ((n - 1) >> 2) << 2;     // last float4 start inside the row
   int32_t* listA = reinterpret_cast<int32_t*>(sh.buf);
@@ -402,15 +405,23 @@ __device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk
   int32_t* cpos = reinterpret_cast<int32_t*>(sh.buf + A_CAP + C_CAP);
 
   // first digit: histogram of the top 12 key bits
-  for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
-  __syncthreads();
-  for (int64_t c = (int64_t)tid * EPT; c < n; c += SUB) {
-    const f32x4 v = load4(row, c, last4);
+  if (!hist_ready) {
+    for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
+    __syncthreads();
+    constexpr int HU = 8;                         // float4 loads in flight per thread
+    for (int64_t c0 = (int64_t)tid * EPT; c0 < n; c0 += (int64_t)SUB * HU) {
+      f32x4 v[HU];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if (c + e < n) atomicAdd(&sh.hist[score_key(v[e]) >> HIST_SHIFT], 1u);
+      for (int u = 0; u < HU; ++u) v[u] = load4(row, c0 + (int64_t)u * SUB, last4);
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+          if (c0 + (int64_t)u * SUB + e < n) atomicAdd(&sh.hist[score_key(v[u][e]) >> HIST_SHIFT], 1u);
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   find_bucket(sh.hist, HIST_BINS, (uint32_t)kk, sh);
   const uint32_t b1 = (uint32_t)sh.misc[0];
   const int cntA = sh.misc[1];
@@ -576,27 +587,86 @@ __device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk
   }
 }
 
-// Recompute a unit's dense scores (bit-identical to the scan) into row[0..n).
+// Recompute a unit's dense scores over rows [row0, row1) into row[] with the scan's
+// lane layout and arithmetic, so every key is bit-identical to the scan's: a wave-wide
+// 16-byte load covers 64 / LPR consecutive rows (LPR lanes per row), the chunk dots are
+// summed by the same transposed reduction, after which each lane holds one row's score.
+// Each wave keeps RU such groups of 64 rows in flight (LOADS loads per lane), and waves
+// take consecutive 64*RU-row blocks in turn. The keys are also counted by their first
+// radix digit (top 12 bits) into sh.hist, for select_dense. Scores are staged in the
+// list storage (LDS) and written out once per STAGE rows: a store in the load loop
+// would hold up the next loads, which wait on one in-order counter with it.
 template <int R, int KB>
-__device__ void recompute_scores(const unsigned char* kproj_unit, const float* qhat_unit, int64_t n, float* row) {
-  float q[R];
+__device__ void recompute_scores(const unsigned char* kproj_unit, const float* qhat_unit, int64_t row0, int64_t row1,
+                                 float* row, SelShared& sh) {
+  constexpr int LPR = R * KB / 16;                 // lanes per projected row (16 bytes each)
+  constexpr int VPC = 16 / KB;                     // values per 16-byte chunk
+  constexpr int RPL = 64 / LPR;                    // rows per wave-wide load
+  constexpr int LOADS = KB == 2 ? 16 : 8;          // 16-byte loads in flight per lane (FP8: its
+                                                   // decode needs more registers)
+  constexpr int RU = LPR >= LOADS ? 1 : LOADS / LPR;   // 64-row groups in flight per wave
+  constexpr int STEP = SEL_WAVES * RU * 64;        // rows of one pass of all waves
+  constexpr int STAGE = LDS_WORDS;                 // rows staged in LDS between writes
+  static_assert(STAGE % STEP == 0, "a stage holds whole passes");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = lane % LPR, rs = lane / LPR;
+  float* stage = reinterpret_cast<float*>(sh.buf);
+  float qh[VPC];
 #pragma unroll
-  for (int i = 0; i < R; ++i) q[i] = qhat_unit[i];
-  for (int64_t j = threadIdx.x; j < n; j += SEL_THREADS) row[j] = row_score<R, KB>(q, kproj_unit + j * R * KB);
+  for (int e = 0; e < VPC; ++e) qh[e] = qhat_unit[p * VPC + e];
+  for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
   __syncthreads();
+  const unsigned char* base = kproj_unit + p * 16;
+  const int64_t last = row1 - 1;
+  for (int64_t s0 = row0; s0 < row1; s0 += STAGE) {
+    const int64_t s1 = min(s0 + STAGE, row1);
+    for (int64_t g0 = s0 + (int64_t)wave * RU * 64; g0 < s1; g0 += STEP) {
+      u32x4 w[RU][LPR];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+#pragma unroll
+        for (int i = 0; i < LPR; ++i)              // rows past the range read its last row
+          w[u][i] = ld16_stream(base + (size_t)min(g0 + u * 64 + i * RPL + rs, last) * R * KB);
+      }
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        float d[LPR];
+#pragma unroll
+        for (int i = 0; i < LPR; ++i) d[i] = dot_chunk<KB>(qh, w[u][i]);
+        const float sc = transpose_reduce<LPR>(d, p);
+        const int64_t j = g0 + u * 64 + p * RPL + rs;
+        if (j < s1) {
+          stage[j - s0] = sc;
+          atomicAdd(&sh.hist[score_key(sc) >> HIST_SHIFT], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    // the staged scores to row[s0, s1), as device-scope stores: they go through to
+    // memory rather than stay dirty in this XCD's L2, so the release before the
+    // hand-over to the last part has nothing to write back
+    const int len = (int)(s1 - s0);
+    for (int i = tid; i < len; i += SEL_THREADS)
+      __hip_atomic_store(row + s0 + i, stage[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
 }
 
-// grid = B * H_kv. scores != nullptr: dense selection over caller scores (stride
-// `stride`). Otherwise: take-all, candidate path, or recompute + dense selection.
+// grid = (B * H_kv, parts). scores != nullptr (parts = 1): dense selection over caller
+// scores (stride `stride`). Otherwise (parts = EXACT_WGS): take-all, the candidate path
+// (part 0 alone), or the exact path: every part recomputes its share of the unit's
+// scores and the last part to finish runs the dense selection.
 template <int R, int KB>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
     int n_kv_heads, int64_t cap, int k, int32_t* __restrict__ idx, const unsigned char* __restrict__ kproj,
     const float* __restrict__ qhat, const uint32_t* __restrict__ tlow, const uint32_t* __restrict__ cand,
     const uint64_t* __restrict__ counts, float* __restrict__ dense, int64_t dense_stride, int64_t ntile_cap,
-    int64_t cand_stride, uint32_t* __restrict__ epoch) {
+    int64_t cand_stride, uint32_t* __restrict__ epoch, uint32_t* __restrict__ arrive,
+    uint32_t* __restrict__ parthist) {
   __shared__ SelShared sh;
   const int unit = blockIdx.x;
+  const int part = blockIdx.y;                    // 0: the unit's selector; > 0: exact-path helpers
   const int b = unit / n_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -631,8 +701,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     }
   };
   const bool cand_path = scores == nullptr;
+  const bool helper = part > 0;
   uint32_t tkey = 0, tshift = 0;
-  if (cand_path) {
+  if (cand_path && !helper) {
     // one more step of this unit done on this workspace: the next prep publishes
     // under a new tag
     if (tid == 0) epoch[unit] += 1u;
@@ -647,15 +718,37 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const int kk = (int)min((int64_t)k, n);
   int32_t* out = idx + (size_t)unit * k;
 
-  for (int i = kk + tid; i < k; i += SEL_THREADS) out[i] = -1;
+  if (!helper)
+    for (int i = kk + tid; i < k; i += SEL_THREADS) out[i] = -1;
   if (kk == 0) return;
   if (!cand_path) {
     select_dense(scores + (size_t)unit * stride, n, kk, out, sh);
     return;
   }
   if ((int64_t)kk == n) {
-    for (int i = tid; i < kk; i += SEL_THREADS) out[i] = i;
+    if (!helper)
+      for (int i = tid; i < kk; i += SEL_THREADS) out[i] = i;
     return;
+  }
+  const int64_t ntiles = (n + TILE_ROWS - 1) / TILE_ROWS;
+  // a tile that could not keep its candidates counts OVF_MARK in the chunk's scan (a
+  // tile holds at most TILE_ROWS candidates, so 32 marks and 32 counts cannot collide)
+  constexpr uint32_t OVF_MARK = 1u << 24;
+  static_assert(CHUNK_T * TILE_ROWS < OVF_MARK && (uint64_t)CHUNK_T * OVF_MARK < (1ull << 32), "marks apart");
+  uint32_t total = 0;
+  bool exact = false;                             // block-uniform: take the exact path
+  if (helper) {
+    // the same decision as part 0's gather, from the count words alone: the exact path
+    // when a tile overflowed, or the candidates exceed the lists or fall short of kk
+    for (int64_t t0 = 0; t0 < ntiles && !exact; t0 += CHUNK_T) {
+      const bool own = tid < CHUNK_T && t0 + tid < ntiles;
+      const uint32_t c = own ? (uint32_t)cnt_u[t0 + tid] : 0u;
+      uint32_t chunk_total;
+      block_incl_scan(c == TILE_OVERFLOW ? OVF_MARK : c, sh.scan, &chunk_total);
+      if (chunk_total >= OVF_MARK || total + chunk_total > (uint32_t)CAND_CAP) exact = true;
+      total += chunk_total;
+    }
+    if (!exact && total >= (uint32_t)kk) return;   // part 0 selects from the candidates
   }
 
   uint32_t* ckey = sh.buf;
@@ -665,16 +758,18 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   // the threshold's first two histograms start from zero
   for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
   for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) sh.hist2[i] = 0u;
-  const int64_t ntiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-  uint32_t total = 0;
-  bool ovf = false;
-  for (int64_t t0 = 0; t0 < ntiles; t0 += CHUNK_T) {
+  for (int64_t t0 = 0; t0 < ntiles && !helper; t0 += CHUNK_T) {
     if (t0 > 0) load_chunk(t0, ntiles);
     const uint32_t c = (uint32_t)cw;
     const bool own = tid < CHUNK_T && t0 + tid < ntiles;
-    ovf = ovf || (own && c == TILE_OVERFLOW);
     uint32_t chunk_total;
-    const uint32_t incl = block_incl_scan(own && c != TILE_OVERFLOW ? c : 0u, sh.scan, &chunk_total);
+    const uint32_t incl = block_incl_scan(own ? (c == TILE_OVERFLOW ? OVF_MARK : c) : 0u, sh.scan, &chunk_total);
+    // an overflowed tile, or more candidates than the lists hold: the exact path,
+    // decided from the counts alone, before any candidate is placed
+    if (chunk_total >= OVF_MARK || total + chunk_total > (uint32_t)CAND_CAP) {
+      exact = true;
+      break;
+    }
     if (tid < CHUNK_T) toff[tid + 1] = incl;
     if (tid == 0) toff[0] = 0u;
     __syncthreads();
@@ -707,8 +802,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     __syncthreads();
   }
 
-  const bool overflowed = __syncthreads_or(ovf) != 0;
-  if (!overflowed && total >= (uint32_t)kk && total <= (uint32_t)CAND_CAP) {
+  if (!helper && !exact && total >= (uint32_t)kk) {
     // threshold on the relative keys over their whole range [0, CAND_REL_MAX]: the
     // gather has counted them by their top HIST1_BITS bits already
     uint32_t needT;
@@ -768,20 +862,56 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       __syncthreads();
       const uint32_t lo = T << CAND_ROW_BITS;
       T = lds_threshold_range(ckey, (int)total, lo, lo | CAND_ROW_MASK, needT, sh, &needT, &all_eq);
+    } else if (!all_eq && needT > 0) {
+      // many boundary entries on the saturated relative key (their exact keys may lie
+      // anywhere above its range): those entries take their exact keys, every other
+      // entry 0, below them all (entries under the boundary are never taken, and none
+      // lies above it); the needT largest exact keys are then taken, equal keys by
+      // list order, i.e. by position
+      for (int i = tid; i < (int)total; i += SEL_THREADS)
+        ckey[i] = ckey[i] == T ? score_key(row_score<R, KB>(sh.qh, kp_unit + (size_t)cpos[i] * R * KB)) : 0u;
+      for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
+      for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) sh.hist2[i] = 0u;
+      __syncthreads();
+      T = lds_threshold_range(ckey, (int)total, 0u, 0xffffffffu, needT, sh, &needT, &all_eq);
+      if (needT == 0xffffffffu) all_eq = true;
     }
-    if (!(!all_eq && needT > 0 && nb > 64 && T >= CAND_REL_MAX)) {
-      // compact in place in LDS, then write the result with coalesced stores
-      compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, out, (uint32_t)kk, sh);
-      return;
+    // compact in place in LDS, then write the result with coalesced stores
+    compact_candidates(ckey, cpos, (int)total, T, needT, all_eq, out, (uint32_t)kk, sh);
+    return;
+  }
+  // Exact path (the sampled threshold misjudged this unit, a scan tile overflowed, or
+  // k exceeds the candidate lists): every part recomputes its share of the unit's
+  // scores (bit-identical to the scan) into the dense row and counts their first radix
+  // digit; the part that finishes last adds the other parts' counts and selects over
+  // the whole row. The hand-over is an arrival counter (reset by the prep each step):
+  // each part's stores are released before it arrives, and the last one acquires
+  // them, so no part ever waits for another.
+  float* row = dense + (size_t)unit * dense_stride;
+  const int parts = (int)gridDim.y;
+  const int64_t blk = (int64_t)SEL_THREADS * 4;  // part boundaries on 4096-row multiples
+  const int64_t nblk = (n + blk - 1) / blk;
+  const int64_t r0 = min(n, nblk * part / parts * blk), r1 = min(n, nblk * (part + 1) / parts * blk);
+  recompute_scores<R, KB>(kproj + (size_t)unit * cap * R * KB, qhat + (size_t)unit * QHAT_STRIDE, r0, r1, row, sh);
+  if (parts > 1) {
+    uint32_t* ph = parthist + ((size_t)unit * parts + part) * HIST_BINS;
+    for (int i = tid; i < HIST_BINS; i += SEL_THREADS)
+      __hip_atomic_store(ph + i, sh.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this part's rows and counts, released
+    __syncthreads();
+    if (tid == 0) sh.misc[7] = (int32_t)atomicAdd(arrive + unit, 1u);
+    __syncthreads();
+    if (sh.misc[7] != parts - 1) return;          // another part is still recomputing
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other parts' rows and counts
+    for (int i = tid; i < HIST_BINS; i += SEL_THREADS) {
+      uint32_t c = sh.hist[i];
+      for (int q = 0; q < parts; ++q)
+        if (q != part) c += parthist[((size_t)unit * parts + q) * HIST_BINS + i];
+      sh.hist[i] = c;
     }
-    // (many entries on a saturated relative key: their exact order does not fit the
-    // packed keys; the exact selection below handles the unit)
     __syncthreads();
   }
-  // the sampled threshold misjudged this unit: exact selection over recomputed scores
-  float* row = dense + (size_t)unit * dense_stride;
-  recompute_scores<R, KB>(kproj + (size_t)unit * cap * R * KB, qhat + (size_t)unit * QHAT_STRIDE, n, row);
-  select_dense(row, n, kk, out, sh);
+  select_dense(row, n, kk, out, sh, true);
 }
 
 }  // namespace
@@ -795,13 +925,15 @@ hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scor
   const uint32_t* tlow = reinterpret_cast<const uint32_t*>(ws + L.off_tlow);
   float* dense = reinterpret_cast<float*>(ws + L.off_scores);
   uint32_t* epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
-  const dim3 grid((unsigned)L.units), block(SEL_THREADS);
+  uint32_t* arrive = reinterpret_cast<uint32_t*>(ws + L.off_arrive);
+  uint32_t* parthist = reinterpret_cast<uint32_t*>(ws + L.off_parthist);
+  const dim3 grid((unsigned)L.units, scores ? 1u : (unsigned)EXACT_WGS), block(SEL_THREADS);
   const unsigned char* kp = static_cast<const unsigned char*>(kproj);
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
 #define SJSA_SEL(RR, KB)                                                                                \
   select_kernel<RR, KB><<<grid, block, 0, st>>>(scores, stride, seq_len, s.n_kv_heads, s.capacity, k, idx, \
                                                 kp, qhat, tlow, cand, counts, dense, L.score_stride,      \
-                                                L.ntile_cap, L.cand_stride, epoch)
+                                                L.ntile_cap, L.cand_stride, epoch, arrive, parthist)
   switch (s.rank) {
     case 16: if (fp8) SJSA_SEL(16, 1); else SJSA_SEL(16, 2); break;
     case 32: if (fp8) SJSA_SEL(32, 1); else SJSA_SEL(32, 2); break;

@@ -43,6 +43,10 @@ __host__ __device__ constexpr uint32_t cand_entry(uint32_t rel, int row) {
 constexpr int TLOW_SHIFT_POS = 8;
 constexpr int CAND_HEADROOM = 2;      // log2 of the relative keys' span over the sampled range
 constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
+// Workgroups of the selection launch per unit: the first selects from the candidates;
+// when the unit takes the exact path (scores recomputed from the projected cache), all
+// of them recompute one part of its rows and the last to finish selects.
+constexpr int EXACT_WGS = 2;
 
 struct Layout {
   int64_t units = 0;          // B * H_kv
@@ -54,6 +58,8 @@ struct Layout {
   size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
   size_t off_sync = 0;        // SYNC_WORDS 64-bit words per unit
   size_t off_epoch = 0;       // one u32 per unit: steps completed on this workspace
+  size_t off_arrive = 0;      // one u32 per unit: workgroups of its exact path done (reset by the prep)
+  size_t off_parthist = 0;    // [units, EXACT_WGS, HIST_BINS] u32: the exact path's partial histograms
   size_t off_bias = 0;        // gated step: per-position logit terms
   size_t scores_end = 0, total = 0;
 };

@@ -144,13 +144,15 @@ def tiny_single_head(seed: int = 1, device="cpu", n_calib: int = 512) -> Workloa
 
 
 def rope_gqa(batch, n_kv_heads, group, n, rank, k, *, seed, device="cpu", heavy_frac=0.0,
-             head_dim=128, capacity=None, name="rope-gqa", n_q_sets=1) -> Workload:
+             head_dim=128, capacity=None, name="rope-gqa", n_q_sets=1, quiet=None) -> Workload:
     """LLaMA-3.1-8B-shaped decode layer: K, V ~ N(0,1) bf16 with rotate-half RoPE
     (base 500000, no frequency scaling) applied to K at positions 0..n-1 and to q at
     position n-1; a random orthonormal basis per KV head. With heavy_frac > 0, a
     seeded round(heavy_frac*n) positions per (b, h) get their key scaled by 4 (norm x4,
     V unchanged). n_q_sets > 1 draws that many independent query sets, stacked as
-    extra["q_sets"] [n_q_sets, B, H_q, d]; q is the first.
+    extra["q_sets"] [n_q_sets, B, H_q, d]; q is the first. quiet = (period, rows, scale)
+    scales the keys at positions p with p % period < rows by `scale` (after RoPE and
+    the heavy hitters; a power of two keeps the bf16 values exact).
 
     K and V are drawn one sequence at a time on `device`, so the fp32 staging stays
     at one sequence's size.
@@ -179,6 +181,9 @@ def rope_gqa(batch, n_kv_heads, group, n, rank, k, *, seed, device="cpu", heavy_
                 sel = torch.randperm(n, generator=g, device=device)[:n_heavy]
                 kb[h, sel] *= 4.0
                 hb.append(sel)
+        if quiet is not None:
+            period, rows, scale = quiet
+            kb[:, (pos % period) < rows] *= scale
         K[b, :, :n] = kb.to(torch.bfloat16)
         del kb
         V[b, :, :n] = torch.randn(n_kv_heads, n, d, generator=g, device=device).to(torch.bfloat16)
@@ -206,6 +211,16 @@ def long_batched(seed: int = 3, device="cpu", n_q_sets: int = 1, batch: int = 16
     """B=16, 32/8 heads, d=128, n=131072, r=32, k=4096, RoPE keys plus 1% heavy hitters."""
     return rope_gqa(batch, 8, 4, n, 32, 4096, seed=seed, device=device, heavy_frac=0.01,
                     name=f"long-batched-b{batch}-n{n}-r32-k4096", n_q_sets=n_q_sets)
+
+
+def long_batched_blind_spot(seed: int = 13, device="cpu", batch: int = 16, n: int = 131072,
+                            k: int = 4096) -> Workload:
+    """long_batched with the keys at positions p % (n/1024) < 2 scaled by 1/16 (n a
+    multiple of 1024): the rows an evenly spaced sampler of 1024 adjacent pairs reads
+    are the quietest of the sequence, so such a sample places any score threshold far
+    below the true k-th score. The top-k lies entirely where the sample does not look."""
+    return rope_gqa(batch, 8, 4, n, 32, k, seed=seed, device=device, heavy_frac=0.01,
+                    name=f"long-batched-blind-spot-b{batch}-n{n}-r32-k{k}", quiet=(n // 1024, 2, 1.0 / 16.0))
 
 
 def gated(batch, n_kv_heads, group, n, unit_size, k_units, *, seed, device="cpu", capacity=None,
