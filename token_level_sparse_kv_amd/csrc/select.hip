@@ -594,8 +594,9 @@ __device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk
 // Each wave keeps RU such groups of 64 rows in flight (LOADS loads per lane), and waves
 // take consecutive 64*RU-row blocks in turn. The keys are also counted by their first
 // radix digit (top 12 bits) into sh.hist, for select_dense. Scores are staged in the
-// list storage (LDS) and written out once per STAGE rows: a store in the load loop
-// would hold up the next loads, which wait on one in-order counter with it.
+// list storage (LDS) and written out once per STAGE rows with coalesced 16-byte stores:
+// a store in the load loop would hold up the next loads, which wait on one in-order
+// counter with it.
 template <int R, int KB>
 __device__ void recompute_scores(const unsigned char* kproj_unit, const float* qhat_unit, int64_t row0, int64_t row1,
                                  float* row, SelShared& sh) {
@@ -642,12 +643,13 @@ __device__ void recompute_scores(const unsigned char* kproj_unit, const float* q
       }
     }
     __syncthreads();
-    // the staged scores to row[s0, s1), as device-scope stores: they go through to
-    // memory rather than stay dirty in this XCD's L2, so the release before the
-    // hand-over to the last part has nothing to write back
+    // the staged scores to row[s0, s1): 16-byte stores where the row is 16-byte aligned
+    // (s0 is a multiple of 4096 and the row starts 256-byte aligned), then the tail
     const int len = (int)(s1 - s0);
-    for (int i = tid; i < len; i += SEL_THREADS)
-      __hip_atomic_store(row + s0 + i, stage[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int len4 = len & ~3;
+    for (int i = tid * 4; i < len4; i += SEL_THREADS * 4)
+      *reinterpret_cast<f32x4*>(row + s0 + i) = *reinterpret_cast<const f32x4*>(stage + i);
+    for (int i = len4 + tid; i < len; i += SEL_THREADS) row[s0 + i] = stage[i];
     __syncthreads();
   }
 }
@@ -895,14 +897,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   recompute_scores<R, KB>(kproj + (size_t)unit * cap * R * KB, qhat + (size_t)unit * QHAT_STRIDE, r0, r1, row, sh);
   if (parts > 1) {
     uint32_t* ph = parthist + ((size_t)unit * parts + part) * HIST_BINS;
-    for (int i = tid; i < HIST_BINS; i += SEL_THREADS)
-      __hip_atomic_store(ph + i, sh.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this part's rows and counts, released
+    for (int i = tid; i < HIST_BINS; i += SEL_THREADS) ph[i] = sh.hist[i];
+    // the workgroup's rows and counts, made visible to thread 0 by the barrier, are
+    // released at agent scope by thread 0's fence (one L2 write-back per workgroup)
+    // before it arrives; the last part's thread 0 acquires them, and the barrier
+    // passes them on to its other threads
     __syncthreads();
-    if (tid == 0) sh.misc[7] = (int32_t)atomicAdd(arrive + unit, 1u);
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t before = atomicAdd(arrive + unit, 1u);
+      if (before == (uint32_t)parts - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      sh.misc[7] = (int32_t)before;
+    }
     __syncthreads();
     if (sh.misc[7] != parts - 1) return;          // another part is still recomputing
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other parts' rows and counts
     for (int i = tid; i < HIST_BINS; i += SEL_THREADS) {
       uint32_t c = sh.hist[i];
       for (int q = 0; q < parts; ++q)
