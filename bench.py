@@ -269,18 +269,36 @@ def fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps, 
     idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
     out = torch.empty(B, Hkv * G, d, dtype=torch.bfloat16, device=dev)
 
-    def step(i):
+    def step(i, ev=None):
         q = q_sets[i % q_sets.shape[0]]
+        if ev is not None:
+            ev[0].record()
         sj.prep_scan(shape, q, M, Kp8, seq_len, k, ws, k_new=k_new, v_new=v_new, pos=pos_new, K=K, V=V)
+        if ev is not None:
+            ev[1].record()
         sj.select(shape, Kp8, seq_len, k, ws, idx=idx)
+        if ev is not None:
+            ev[2].record()
         sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
+        if ev is not None:
+            ev[3].record()
 
     us = back_to_back_us(step, steps, warmup)
+    evs = [[_ev() for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stages = {nm: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps * 1000.0, 2)
+              for j, nm in enumerate(["append+prep+scan", "select", "attend"])}
     tb = step_bytes(B, Hkv, G, d, r, n, k, kb=1)
     gbs = tb["total"] / (us * 1e-6) / 1e9
+    scan_bytes = tb["scan_kproj"] + tb["q"] + tb["M"] + tb["append"]
     res = {"kproj_dtype": "fp8_e4m3", "value": round(1e6 / us, 2), "unit": "steps/s",
            "ms_per_step": round(us / 1000.0, 5), "algorithmic_bytes_per_step": tb["total"], "hbm_gbs": round(gbs, 1),
-           "hbm_frac_of_peak": round(gbs / peak, 4), "graph_us_per_step": round(graph_us(step, 8, steps), 2)}
+           "hbm_frac_of_peak": round(gbs / peak, 4), "stage_us": stages,
+           "scan_hbm_frac_of_peak": round(scan_bytes / (stages["append+prep+scan"] * 1e-6) / 1e9 / peak, 4),
+           "graph_us_per_step": round(graph_us(step, 8, steps), 2)}
+    say(f"fp8: {us:.1f} us/step, stages {stages}")
     if cpu is not None:
         from oracle import jssa
         units = [(b, h) for b in range(B) for h in range(Hkv)]
@@ -423,17 +441,17 @@ def block_variant(sj, workloads, steps, warmup, peak, int4, cpu=None):
 
 CALIB_WORKLOAD = ("calibration accumulation: one 131072-token prefill, 32 query / 8 KV heads (G=4), d=128; "
                   "second-moment sums of the group-mean query and of the key per KV head")
-# fp32 FMA peak for non-packed instructions: 256 CUs x 64 FMA lanes per clock x 2 flops x
-# 2.4 GHz. The published 157.3 TFLOP/s counts packed FP32 (two FMAs per lane per
-# instruction), which this build does not emit.
-FP32_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
-FP32_PACKED_PEAK_TFLOPS = 157.3
+# Published dense matrix-core peaks: fp32 (the mean-query moment's products) and bf16
+# (the key moment's products, exact in fp32).
+MFMA_FP32_PEAK_TFLOPS = 157.3
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def calib_variant(sj, reps, warmup, cpu=None):
     """Second-moment accumulation over one prefill of 131072 tokens (the pages'
     calibration sequence length), timed over repeated calls."""
     import torch
+    from token_level_sparse_kv_amd.perfmodel import MI355X_HBM_PEAK_GBS
     g = torch.Generator(device="cuda")
     g.manual_seed(11)
     T, Hkv, G = 131072, 8, 4
@@ -444,13 +462,18 @@ def calib_variant(sj, reps, warmup, cpu=None):
     ws = sj.calib_workspace(q, k)
     us = back_to_back_us(lambda i: sj.calib_accumulate(q, k, SQ, SK, workspace=ws), reps, warmup)
     ms = us / 1000.0
-    flops = 2 * Hkv * T * 128 * 128 * 2            # both moment matrices, multiply + add per element
-    tf = flops / (ms * 1e-3) / 1e12
+    in_bytes = q.numel() * 2 + k.numel() * 2
+    gbs = in_bytes / (ms * 1e-3) / 1e9
+    # products formed on the matrix cores: the 36 upper-triangle 16 x 16 tiles of each
+    # 128 x 128 moment, one multiply-add per element per position
+    tri_flops = Hkv * T * 36 * 256 * 2
+    floor_us = (tri_flops / (MFMA_FP32_PEAK_TFLOPS * 1e12) + tri_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     res = {"workload": CALIB_WORKLOAD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
-           "ms_per_prefill": round(ms, 4), "bound": "alu", "achieved_tflops": round(tf, 2),
-           "peak_tflops": round(FP32_PEAK_TFLOPS, 2), "frac": round(tf / FP32_PEAK_TFLOPS, 4),
-           "packed_fp32_peak_tflops": FP32_PACKED_PEAK_TFLOPS,
-           "input_bytes": q.numel() * 2 + k.numel() * 2}
+           "ms_per_prefill": round(ms, 4), "bound": "hbm", "achieved_gbps": round(gbs, 1),
+           "peak_gbps": MI355X_HBM_PEAK_GBS, "frac": round(gbs / MI355X_HBM_PEAK_GBS, 4), "input_bytes": in_bytes,
+           "mfma": {"query_fp32_gflop": round(tri_flops / 1e9, 2), "key_bf16_gflop": round(tri_flops / 1e9, 2),
+                    "peak_fp32_tflops": MFMA_FP32_PEAK_TFLOPS, "peak_bf16_tflops": MFMA_BF16_PEAK_TFLOPS,
+                    "floor_us": round(floor_us, 1), "frac_of_floor": round(floor_us / us, 4)}}
     if cpu is not None:
         from oracle import calib
         P = 4096                                    # positions per sampled KV head
@@ -516,7 +539,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--headline-only", action="store_true", help="time the headline step only (for profiling)")
+    ap.add_argument("--only", choices=["headline", "fp8", "exact", "gated", "block", "calib"],
+                    help="run one measurement only, for profiling: the headline step's passes (one JSON line, no "
+                         "variants), or one variant (its JSON object alone)")
     ap.add_argument("--no-fp8-variant", action="store_true", help="skip the FP8 scoring-cache measurement")
     ap.add_argument("--no-gated-variant", action="store_true", help="skip the gated-logit step measurement")
     ap.add_argument("--no-block-variant", action="store_true", help="skip the block-sparse step measurements")
@@ -525,6 +550,7 @@ def main():
                     help="skip the exact-fallback and sampler blind-spot measurements")
     args = ap.parse_args()
 
+    only = args.only
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this build measures the "
               f"single-GPU path)", file=sys.stderr)
@@ -542,8 +568,19 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cpu = None if args.no_cpu_baseline else host_info()
+    cpu = None if args.no_cpu_baseline or only else host_info()
     steps, warmup = args.steps, args.warmup
+    if only == "gated":
+        print(json.dumps({"gated_variant": gated_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS)}))
+        return
+    if only == "block":
+        print(json.dumps({"block_variant": block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, False),
+                          "block_int4_variant": block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS,
+                                                              True)}))
+        return
+    if only == "calib":
+        print(json.dumps({"calib_variant": calib_variant(sj, max(2, steps // 20), 1)}))
+        return
     t_setup = time.time()
     wl = workloads.long_batched(device=dev, n_q_sets=8)
     B, Hkv, G, d, r, n, k = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim, wl.rank, wl.capacity, wl.k
@@ -558,6 +595,12 @@ def main():
 
     q_sets = wl.extra["q_sets"]
     K, V, M, seq_len = wl.K, wl.V, wl.M, wl.seq_len
+    if only == "fp8":
+        k_new, v_new = workloads.new_token(wl, seed=99)
+        pos_new = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+        print(json.dumps({"kproj_fp8_variant": fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new,
+                                                           steps, warmup, step_bytes, MI355X_HBM_PEAK_GBS)}))
+        return
     Kp = kproj_cache(K, V, M)
     k_new, v_new = workloads.new_token(wl, seed=99)
     pos_new = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
@@ -597,6 +640,13 @@ def main():
                 for j, nm in enumerate(names)}
 
     step = make_step(shape, ws, K, V, Kp, q_sets)
+    if only == "exact":
+        # every unit on the exact path (no scan workgroup takes what its prep publishes)
+        shape_fb = sj.make_shape(B, Hkv, G, d, r, n, fused_wait_us=-1)
+        step_fb = make_step(shape_fb, sj.alloc_workspace(shape_fb, k, dev), K, V, Kp, q_sets)
+        fb = back_to_back_us(step_fb, steps, warmup)
+        print(json.dumps({"fallback_variant": {"us_per_step": round(fb, 2), "stage_us": stage_us(step_fb)}}))
+        return
     # throughput: K whole steps back to back, bracketed by one pair of events (an event
     # between two kernels delays the second by several microseconds, so the steps
     # themselves carry none)
@@ -655,7 +705,7 @@ def main():
         "setup_s": round(t_setup, 2),
     }
 
-    if not args.headline_only:
+    if not only:
         # two full input sets alternated, so no step finds the previous one's rows cached
         wl2 = workloads.long_batched(seed=13, device=dev, n_q_sets=8)
         K2, V2 = wl2.K, wl2.V
@@ -669,7 +719,7 @@ def main():
         torch.cuda.empty_cache()
         say(f"rotated: {rot:.1f} us/step")
 
-    if not args.headline_only and not args.no_fallback_variants:
+    if not only and not args.no_fallback_variants:
         # every scan workgroup gives up at once (no wait), so every unit is recomputed
         # and selected exactly by the selection kernel
         shape_fb = sj.make_shape(B, Hkv, G, d, r, n, fused_wait_us=-1)
@@ -717,14 +767,14 @@ def main():
         del wb, Kb_, Vb_, Kpb, wsb, step_b
         torch.cuda.empty_cache()
 
-    if not args.headline_only and not args.no_gated_variant:
+    if not only and not args.no_gated_variant:
         line["gated_variant"] = gated_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, cpu=cpu)
-    if not args.headline_only and not args.no_block_variant:
+    if not only and not args.no_block_variant:
         line["block_variant"] = block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, False, cpu=cpu)
         line["block_int4_variant"] = block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, True, cpu=cpu)
-    if not args.headline_only and not args.no_calib_variant:
+    if not only and not args.no_calib_variant:
         line["calib_variant"] = calib_variant(sj, max(2, steps // 20), 1, cpu=cpu)
-    if not args.headline_only and not args.no_fp8_variant:
+    if not only and not args.no_fp8_variant:
         line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps,
                                                 warmup, step_bytes, MI355X_HBM_PEAK_GBS, cpu=cpu)
         torch.cuda.empty_cache()

@@ -7,15 +7,26 @@
 // head), section 迹归一化 (each moment normalized to unit trace) and section 闭式谱解
 // (the basis rows are the top-r eigenvectors of the sum of the normalized moments).
 //
-// calib_partial_kernel: grid (nwg, H_kv, 2), 256 threads. Workgroup w of (head h,
-// matrix m) takes a contiguous slice of the B*T positions; m = 0 stages the
-// group-mean query of each position (fp32 sum of the G bf16 heads in head order,
-// divided by G), m = 1 the bf16 key, 32 positions at a time in LDS. Thread (ty, tx)
-// owns the 8x8 output block rows 8ty.., columns 8tx..; it accumulates x_i x_j in
-// fp32 and folds the fp32 sums into fp64 every 256 positions, so the fp32 rounding
-// covers at most 256 products per element. The fp64 partials go to the workspace
-// and calib_reduce_kernel adds them, in workgroup order, into the caller's fp64
-// accumulators (deterministic).
+// calib_mfma_kernel: grid (nwg_q + nwg_k, H_kv), 256 threads (4 waves), one workgroup
+// per CU (its LDS). Workgroups [0, nwg_q) accumulate the group-mean query's moment
+// (fp32 sum of the G bf16 heads in head order, divided by G), the rest the bf16 key's;
+// each takes a contiguous slice of the B*T positions. Only the upper triangle of the
+// symmetric 128 x 128 moment is formed: its 36 tiles of 16 x 16 (tile row bi <= tile
+// column bj), 9 per wave, each a sum over positions p of x_p[16 bi ..] x_p[16 bj ..]^T
+// on the matrix cores. Positions are staged transposed in LDS (dim-major), 64 query
+// or 256 key positions at a time, so a lane's operand fragment (one dim x 4 or 8
+// positions of the instruction's K) is one 16-byte read, and each wave reads one
+// fragment per 16-dim block it touches (4 or 6) for its 9 tiles:
+//  * keys: v_mfma_f32_16x16x32_bf16, 32 positions per instruction; products of two
+//    bf16 values are exact in fp32;
+//  * mean queries: v_mfma_f32_16x16x4_f32, 4 positions per instruction.
+// The next stage is loaded (each wave instruction reads 64-byte pieces of 16 rows;
+// the four waves complete them) while the current one is multiplied. The fp32 tile
+// sums are folded into fp64 tile sums kept in LDS every 256 key positions and every
+// 128 query positions (whose products are rounded), so no element's fp32 run exceeds
+// 256 rounding steps. At the end each workgroup writes its fp64 tiles to the
+// workspace; calib_reduce_kernel adds them in workgroup order (deterministic) into the
+// caller's fp64 accumulators, mirroring the upper triangle into the lower one.
 #include <math.h>
 #include <string.h>
 
@@ -28,126 +39,352 @@ namespace sjsa {
 namespace {
 
 constexpr int CAL_THREADS = 256;
-constexpr int CAL_ROWS = 32;          // positions staged per LDS tile
-constexpr int CAL_FOLD_TILES = 8;     // fp32 sums folded into fp64 every 8 tiles (256 positions)
-constexpr int CAL_LD = HEAD_DIM + 4;  // padded LDS row
+constexpr int CAL_TILES = 36;             // upper-triangle 16 x 16 tiles of a 128 x 128 moment
+constexpr int CAL_TPW = CAL_TILES / (CAL_THREADS / 64);   // tiles per wave
+constexpr int CAL_PQ = 64;                // query positions staged at a time
+constexpr int CAL_PK = 256;               // key positions staged at a time
+constexpr int CAL_LDF = CAL_PQ + 4;       // fp32 row pitch of the staged queries (floats)
+constexpr int CAL_LDB = CAL_PK + 8;       // bf16 row pitch of the staged keys (halves)
+constexpr int CAL_FOLD_Q = 128;           // query positions per fp32 run
+constexpr int CAL_FOLD_K = 256;           // key positions per fp32 run
+constexpr int CAL_STAGE_BYTES =
+    HEAD_DIM * CAL_LDF * 4 > HEAD_DIM * CAL_LDB * 2 ? HEAD_DIM * CAL_LDF * 4 : HEAD_DIM * CAL_LDB * 2;
+static_assert(CAL_TILES % (CAL_THREADS / 64) == 0, "tiles split evenly over the waves");
+static_assert(CAL_FOLD_Q % CAL_PQ == 0 && CAL_FOLD_K % CAL_PK == 0, "runs hold whole stages");
 
-template <int G>
-__global__ __launch_bounds__(CAL_THREADS) void calib_partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int n_kv_heads, int64_t T, int64_t rows,
-    int64_t chunk, double* __restrict__ part) {
-  __shared__ float X[CAL_ROWS][CAL_LD];
-  const int h = blockIdx.y;
-  const int mat = blockIdx.z;
-  const int wg = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  const int64_t r0 = (int64_t)wg * chunk;
-  const int64_t r1 = min(r0 + chunk, rows);
-  const int n_q_heads = n_kv_heads * G;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-  float a32[8][8];
-  double a64[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { a32[i][j] = 0.f; a64[i][j] = 0.0; }
+// Tile t of the upper triangle, row-major over (bi, bj), bi <= bj < 8.
+__host__ __device__ constexpr int tile_index(int bi, int bj) { return bi * 8 - bi * (bi - 1) / 2 + (bj - bi); }
 
-  int tiles = 0;
-  for (int64_t base = r0; base < r1; base += CAL_ROWS) {
-    // stage 32 positions: 16 lanes x 8 values per position row
-    for (int c = tid; c < CAL_ROWS * 16; c += CAL_THREADS) {
-      const int rr = c >> 4, part8 = (c & 15) * 8;
-      const int64_t r = base + rr;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (r < r1) {
-        const int64_t b = r / T, t = r - b * T;
-        if (mat == 0) {
+// The four waves' tiles, 9 each, chosen so that a wave's tiles touch few 16-dim
+// blocks: one operand fragment per block is read from LDS per instruction step and
+// reused by all the wave's tiles in that block (4 or 6 reads per 9 products instead of
+// 18). Wave 0: the upper triangle of blocks 0..3 without (3, 3); wave 1: that of
+// blocks 4..7 without (7, 7); wave 2: blocks 0..3 x 4..5 and (3, 3); wave 3: blocks
+// 0..3 x 6..7 and (7, 7).
+template <int W>
+struct WaveTiles;
+template <>
+struct WaveTiles<0> {
+  static constexpr int nb = 4;
+  static constexpr int blk[6] = {0, 1, 2, 3, 0, 0};
+  static constexpr int ta[CAL_TPW] = {0, 0, 0, 0, 1, 1, 1, 2, 2};
+  static constexpr int tb[CAL_TPW] = {0, 1, 2, 3, 1, 2, 3, 2, 3};
+};
+template <>
+struct WaveTiles<1> {
+  static constexpr int nb = 4;
+  static constexpr int blk[6] = {4, 5, 6, 7, 0, 0};
+  static constexpr int ta[CAL_TPW] = {0, 0, 0, 0, 1, 1, 1, 2, 2};
+  static constexpr int tb[CAL_TPW] = {0, 1, 2, 3, 1, 2, 3, 2, 3};
+};
+template <>
+struct WaveTiles<2> {
+  static constexpr int nb = 6;
+  static constexpr int blk[6] = {0, 1, 2, 3, 4, 5};
+  static constexpr int ta[CAL_TPW] = {0, 1, 2, 3, 0, 1, 2, 3, 3};
+  static constexpr int tb[CAL_TPW] = {4, 4, 4, 4, 5, 5, 5, 5, 3};
+};
+template <>
+struct WaveTiles<3> {
+  static constexpr int nb = 6;
+  static constexpr int blk[6] = {0, 1, 2, 3, 6, 7};
+  static constexpr int ta[CAL_TPW] = {0, 1, 2, 3, 0, 1, 2, 3, 5};
+  static constexpr int tb[CAL_TPW] = {4, 4, 4, 4, 5, 5, 5, 5, 5};
+};
+
+struct CalShared {
+  __attribute__((aligned(16))) float stage[CAL_STAGE_BYTES / 4];   // staged positions, dim-major
+  double acc[CAL_TILES * 256];                                     // fp64 tile sums
+};
+
+constexpr bool wave_tiles_cover_once() {
+  int seen[CAL_TILES] = {};
+  const int* tabs[4][3] = {{WaveTiles<0>::blk, WaveTiles<0>::ta, WaveTiles<0>::tb},
+                           {WaveTiles<1>::blk, WaveTiles<1>::ta, WaveTiles<1>::tb},
+                           {WaveTiles<2>::blk, WaveTiles<2>::ta, WaveTiles<2>::tb},
+                           {WaveTiles<3>::blk, WaveTiles<3>::ta, WaveTiles<3>::tb}};
+  for (int w = 0; w < 4; ++w)
+    for (int u = 0; u < CAL_TPW; ++u) {
+      const int bi = tabs[w][0][tabs[w][1][u]], bj = tabs[w][0][tabs[w][2][u]];
+      if (bi > bj) return false;
+      ++seen[tile_index(bi, bj)];
+    }
+  for (int t = 0; t < CAL_TILES; ++t)
+    if (seen[t] != 1) return false;
+  return true;
+}
+static_assert(wave_tiles_cover_once(), "the waves' tiles are the upper triangle, each once");
+
+// One stage's products for wave W: per instruction step, one fragment per block of the
+// wave (lane (lg, li): dim 16 blk + li at the step's positions 4 lg .. 4 lg + 3 for the
+// fp32 queries, 8 lg .. 8 lg + 7 for the bf16 keys), then the wave's 9 tiles.
+template <int W, bool IS_Q, int P>
+__device__ __forceinline__ void calib_products(const float* XF, const uint16_t* XB, int li, int lg,
+                                               f32x4_t (&acc)[CAL_TPW]) {
+  using WT = WaveTiles<W>;
+  if constexpr (IS_Q) {
+#pragma unroll 1
+    for (int c0 = 0; c0 < P; c0 += 16) {
+      f32x4_t f[WT::nb];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const u32x4 w = ld16(q + (((size_t)b * n_q_heads + (size_t)h * G + g) * T + t) * HEAD_DIM + part8);
-            v[0] += bf_lo(w.x); v[1] += bf_hi(w.x); v[2] += bf_lo(w.y); v[3] += bf_hi(w.y);
-            v[4] += bf_lo(w.z); v[5] += bf_hi(w.z); v[6] += bf_lo(w.w); v[7] += bf_hi(w.w);
-          }
+      for (int b = 0; b < WT::nb; ++b)
+        f[b] = *reinterpret_cast<const f32x4_t*>(&XF[(16 * WT::blk[b] + li) * CAL_LDF + c0 + 4 * lg]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = v[e] / (float)G;
-        } else {
-          const u32x4 w = ld16(k + (((size_t)b * n_kv_heads + h) * T + t) * HEAD_DIM + part8);
-          v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
-          v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
-        }
+      for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+        for (int u = 0; u < CAL_TPW; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(f[WT::ta[u]][s4], f[WT::tb[u]][s4], acc[u], 0, 0, 0);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) X[rr][part8 + e] = v[e];
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int rr = 0; rr < CAL_ROWS; ++rr) {
-      float xi[8], xj[8];
-      const float4 i0 = *reinterpret_cast<const float4*>(&X[rr][8 * ty]);
-      const float4 i1 = *reinterpret_cast<const float4*>(&X[rr][8 * ty + 4]);
-      const float4 j0 = *reinterpret_cast<const float4*>(&X[rr][8 * tx]);
-      const float4 j1 = *reinterpret_cast<const float4*>(&X[rr][8 * tx + 4]);
-      xi[0] = i0.x; xi[1] = i0.y; xi[2] = i0.z; xi[3] = i0.w; xi[4] = i1.x; xi[5] = i1.y; xi[6] = i1.z; xi[7] = i1.w;
-      xj[0] = j0.x; xj[1] = j0.y; xj[2] = j0.z; xj[3] = j0.w; xj[4] = j1.x; xj[5] = j1.y; xj[6] = j1.z; xj[7] = j1.w;
+  } else {
+#pragma unroll 2
+    for (int c0 = 0; c0 < P; c0 += 32) {
+      bf16x8_t f[WT::nb];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int b = 0; b < WT::nb; ++b)
+        f[b] = *reinterpret_cast<const bf16x8_t*>(&XB[(16 * WT::blk[b] + li) * CAL_LDB + c0 + 8 * lg]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a32[i][j] = fmaf(xi[i], xj[j], a32[i][j]);
-    }
-    __syncthreads();
-    if (++tiles == CAL_FOLD_TILES) {
-      tiles = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { a64[i][j] += (double)a32[i][j]; a32[i][j] = 0.f; }
+      for (int u = 0; u < CAL_TPW; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[WT::ta[u]], f[WT::tb[u]], acc[u], 0, 0, 0);
     }
   }
-  double* out = part + (((size_t)h * 2 + mat) * gridDim.x + wg) * HEAD_DIM * HEAD_DIM;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) out[(size_t)(8 * ty + i) * HEAD_DIM + 8 * tx + j] = a64[i][j] + (double)a32[i][j];
 }
 
-// grid (HEAD_DIM * HEAD_DIM / 256, H_kv, 2): acc[h][i][j] += sum over workgroups.
-__global__ __launch_bounds__(256) void calib_reduce_kernel(const double* __restrict__ part, int nwg,
+// Adds wave W's fp32 tile sums into the fp64 ones and clears them. Lane (lg, li) holds
+// rows 4 lg + v, column li of each of the wave's tiles; no two lanes (and no two waves)
+// share an element, so this needs no synchronisation.
+template <int W>
+__device__ __forceinline__ void calib_fold(double* shacc, int li, int lg, f32x4_t (&acc)[CAL_TPW]) {
+  using WT = WaveTiles<W>;
+#pragma unroll
+  for (int u = 0; u < CAL_TPW; ++u) {
+    double* o = shacc + tile_index(WT::blk[WT::ta[u]], WT::blk[WT::tb[u]]) * 256 + (4 * lg) * 16 + li;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v * 16] += (double)acc[u][v];
+    acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One workgroup's slice: IS_Q selects the mean query's moment (G heads per position)
+// or the key's. Thread tid stages the 8-dim chunk c = tid / 16 of the position groups
+// j = tid % 16 + 16 i (4 consecutive positions each); a load instruction of a wave so
+// reads 64 bytes of each of 16 rows, the four waves the rest of those rows, and each
+// LDS write (4 positions of one dim) falls on its own banks.
+template <int G, bool IS_Q>
+__device__ __forceinline__ void calib_body(CalShared& sh, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k, int n_kv_heads, int64_t T, int64_t rows,
+                                           int wg, int64_t chunk, double* __restrict__ out) {
+  constexpr int P = IS_Q ? CAL_PQ : CAL_PK;      // positions per stage
+  constexpr int NG = P / 64;                    // position groups per thread
+  constexpr int NH = IS_Q ? G : 1;              // head rows loaded per position
+  float* XF = sh.stage;
+  uint16_t* XB = reinterpret_cast<uint16_t*>(sh.stage);
+  const int h = blockIdx.y;
+  const int64_t r0 = (int64_t)wg * chunk;
+  const int64_t r1 = min(r0 + chunk, rows);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_q_heads = n_kv_heads * G;
+  const int li = lane & 15, lg = lane >> 4;
+  const int c = tid >> 4;
+
+  f32x4_t acc[CAL_TPW];
+#pragma unroll
+  for (int u = 0; u < CAL_TPW; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = tid; i < CAL_TILES * 256; i += CAL_THREADS) sh.acc[i] = 0.0;
+  __syncthreads();
+  auto fold = [&]() {
+    switch (wave) {
+      case 0: calib_fold<0>(sh.acc, li, lg, acc); break;
+      case 1: calib_fold<1>(sh.acc, li, lg, acc); break;
+      case 2: calib_fold<2>(sh.acc, li, lg, acc); break;
+      default: calib_fold<3>(sh.acc, li, lg, acc); break;
+    }
+  };
+
+  u32x4 raw[NG][4][NH];                         // [group][position in group][head]
+  // (sequence, position) of a row from the stage's first row by one division per stage:
+  // a stage spans fewer than T rows unless T < P
+  auto load_stage = [&](int64_t base) {
+    const int64_t b0 = base / T, t0 = base - b0 * T;
+    const int64_t last = r1 - 1 - base;          // rows past the slice read its last row (unused)
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int64_t off = 4 * ((tid & 15) + 16 * i) + s4;
+        int64_t t = t0 + (off < last ? off : last), b = b0;
+        if (t >= T) {
+          if (T >= P) {
+            t -= T;
+            ++b;
+          } else {
+            const int64_t w = t / T;
+            b += w;
+            t -= w * T;
+          }
+        }
+        if constexpr (IS_Q) {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            raw[i][s4][g] = ld16(q + (((size_t)b * n_q_heads + (size_t)h * G + g) * T + t) * HEAD_DIM + 8 * c);
+        } else {
+          raw[i][s4][0] = ld16(k + (((size_t)b * n_kv_heads + h) * T + t) * HEAD_DIM + 8 * c);
+        }
+      }
+    }
+  };
+  auto store_stage = [&](int64_t base) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int p0 = 4 * ((tid & 15) + 16 * i);
+      bool valid[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) valid[s4] = base + p0 + s4 < r1;
+      if constexpr (IS_Q) {
+        float v[4][8];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[s4][e] = 0.f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const u32x4 w = raw[i][s4][g];
+            v[s4][0] += bf_lo(w.x); v[s4][1] += bf_hi(w.x); v[s4][2] += bf_lo(w.y); v[s4][3] += bf_hi(w.y);
+            v[s4][4] += bf_lo(w.z); v[s4][5] += bf_hi(w.z); v[s4][6] += bf_lo(w.w); v[s4][7] += bf_hi(w.w);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          f32x4_t o;
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) o[s4] = valid[s4] ? v[s4][e] / (float)G : 0.f;
+          *reinterpret_cast<f32x4_t*>(&XF[(8 * c + e) * CAL_LDF + p0]) = o;
+        }
+      } else {
+        uint32_t w[4][4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const u32x4 x = raw[i][s4][0];
+          w[s4][0] = valid[s4] ? x.x : 0u; w[s4][1] = valid[s4] ? x.y : 0u;
+          w[s4][2] = valid[s4] ? x.z : 0u; w[s4][3] = valid[s4] ? x.w : 0u;
+        }
+        // dims 8 c + 2 e (low halves) and 8 c + 2 e + 1 (high halves), positions p0 .. p0 + 3
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint2 lo = make_uint2((w[0][e] & 0xffffu) | (w[1][e] << 16), (w[2][e] & 0xffffu) | (w[3][e] << 16));
+          const uint2 hi = make_uint2((w[0][e] >> 16) | (w[1][e] & 0xffff0000u),
+                                      (w[2][e] >> 16) | (w[3][e] & 0xffff0000u));
+          *reinterpret_cast<uint2*>(&XB[(8 * c + 2 * e) * CAL_LDB + p0]) = lo;
+          *reinterpret_cast<uint2*>(&XB[(8 * c + 2 * e + 1) * CAL_LDB + p0]) = hi;
+        }
+      }
+    }
+  };
+
+  int staged = 0;                               // positions in the current fp32 run
+  if (r0 < r1) load_stage(r0);
+  for (int64_t base = r0; base < r1; base += P) {
+    __syncthreads();                            // the previous stage's operand reads are done
+    store_stage(base);
+    __syncthreads();
+    if (base + P < r1) load_stage(base + P);    // in flight during the products
+    switch (wave) {
+      case 0: calib_products<0, IS_Q, P>(XF, XB, li, lg, acc); break;
+      case 1: calib_products<1, IS_Q, P>(XF, XB, li, lg, acc); break;
+      case 2: calib_products<2, IS_Q, P>(XF, XB, li, lg, acc); break;
+      default: calib_products<3, IS_Q, P>(XF, XB, li, lg, acc); break;
+    }
+    // fp32 runs of at most 128 query positions (rounded products) or 256 key positions
+    staged += P;
+    if (staged == (IS_Q ? CAL_FOLD_Q : CAL_FOLD_K)) { fold(); staged = 0; }
+  }
+  fold();
+  __syncthreads();
+  for (int i = tid; i < CAL_TILES * 256; i += CAL_THREADS) out[i] = sh.acc[i];
+}
+
+template <int G>
+__global__ __launch_bounds__(CAL_THREADS) void calib_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int n_kv_heads, int64_t T, int64_t rows,
+    int nwg_q, int64_t chunk_q, int64_t chunk_k, double* __restrict__ part) {
+  __shared__ CalShared sh;
+  double* out = part + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * CAL_TILES * 256;
+  if ((int)blockIdx.x < nwg_q)
+    calib_body<G, true>(sh, q, k, n_kv_heads, T, rows, (int)blockIdx.x, chunk_q, out);
+  else
+    calib_body<G, false>(sh, q, k, n_kv_heads, T, rows, (int)blockIdx.x - nwg_q, chunk_k, out);
+}
+
+// grid (HEAD_DIM * HEAD_DIM / 256, H_kv, 2): acc[h][i][j] += the workgroups' tile sums
+// in workgroup order; element (i, j) of the lower triangle takes (j, i) of the upper.
+__global__ __launch_bounds__(256) void calib_reduce_kernel(const double* __restrict__ part, int nwg_q, int nwg_k,
                                                            double* __restrict__ SQ, double* __restrict__ SK) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y, mat = blockIdx.z;
-  const double* p = part + ((size_t)h * 2 + mat) * nwg * HEAD_DIM * HEAD_DIM + e;
+  int i = e / HEAD_DIM, j = e % HEAD_DIM;
+  if (i / 16 > j / 16) { const int x = i; i = j; j = x; }
+  const int t = tile_index(i / 16, j / 16);
+  const int nwg = nwg_q + nwg_k;
+  const int w0 = mat == 0 ? 0 : nwg_q, w1 = mat == 0 ? nwg_q : nwg;
+  const double* p = part + ((size_t)h * nwg) * CAL_TILES * 256 + (size_t)t * 256 + (i % 16) * 16 + (j % 16);
+  constexpr int RU = 8;                          // loads in flight; the sum stays in workgroup order
   double s = 0.0;
-  for (int w = 0; w < nwg; ++w) s += p[(size_t)w * HEAD_DIM * HEAD_DIM];
+  for (int w = w0; w < w1; w += RU) {
+    double x[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) x[u] = w + u < w1 ? p[(size_t)(w + u) * CAL_TILES * 256] : 0.0;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) s += x[u];
+  }
   double* dst = (mat == 0 ? SQ : SK) + (size_t)h * HEAD_DIM * HEAD_DIM + e;
   *dst += s;
 }
 
 }  // namespace
 
-int calib_groups(const sjsa_shape& s, int64_t rows) {
-  const int64_t per_matrix = (512 + 2 * s.n_kv_heads - 1) / (2 * s.n_kv_heads);
-  const int64_t by_rows = (rows + 255) / 256;
-  int64_t n = per_matrix < by_rows ? per_matrix : by_rows;
-  return (int)(n < 1 ? 1 : n);
+// Workgroups per KV head: one workgroup fits a CU, so about 256 in all, three quarters
+// of them for the mean queries (their fp32 products are most of the work); never more
+// than one per 256 positions.
+void calib_groups(const sjsa_shape& s, int64_t rows, int* nwg_q, int* nwg_k) {
+  auto limit = [&](int64_t want) {
+    const int64_t by_rows = (rows + 255) / 256;
+    const int64_t n = want < by_rows ? want : by_rows;
+    return (int)(n < 1 ? 1 : n);
+  };
+  const int64_t per_head = (256 + s.n_kv_heads - 1) / s.n_kv_heads;
+  *nwg_q = limit((per_head * 3 + 3) / 4);
+  *nwg_k = limit(per_head / 4 > 0 ? per_head / 4 : 1);
+}
+
+size_t calib_part_bytes(const sjsa_shape& s, int64_t rows) {
+  int nq, nk;
+  calib_groups(s, rows, &nq, &nk);
+  return (size_t)s.n_kv_heads * (nq + nk) * CAL_TILES * 256 * sizeof(double);
 }
 
 hipError_t launch_calib(const sjsa_shape& s, const uint16_t* q, const uint16_t* k, int64_t T, double* SQ,
                         double* SK, unsigned char* ws, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * T;
-  const int nwg = calib_groups(s, rows);
-  const int64_t chunk = (rows + nwg - 1) / nwg;
+  int nwg_q, nwg_k;
+  calib_groups(s, rows, &nwg_q, &nwg_k);
+  const int64_t chunk_q = ((rows + nwg_q - 1) / nwg_q + CAL_PQ - 1) / CAL_PQ * CAL_PQ;
+  const int64_t chunk_k = ((rows + nwg_k - 1) / nwg_k + CAL_PK - 1) / CAL_PK * CAL_PK;
   double* part = reinterpret_cast<double*>(ws);
-  const dim3 grid((unsigned)nwg, (unsigned)s.n_kv_heads, 2);
+  const dim3 grid((unsigned)(nwg_q + nwg_k), (unsigned)s.n_kv_heads);
   switch (s.group) {
-    case 1: calib_partial_kernel<1><<<grid, dim3(CAL_THREADS), 0, st>>>(q, k, s.n_kv_heads, T, rows, chunk, part); break;
-    case 2: calib_partial_kernel<2><<<grid, dim3(CAL_THREADS), 0, st>>>(q, k, s.n_kv_heads, T, rows, chunk, part); break;
-    case 4: calib_partial_kernel<4><<<grid, dim3(CAL_THREADS), 0, st>>>(q, k, s.n_kv_heads, T, rows, chunk, part); break;
-    case 8: calib_partial_kernel<8><<<grid, dim3(CAL_THREADS), 0, st>>>(q, k, s.n_kv_heads, T, rows, chunk, part); break;
+#define SJSA_CAL(GG) \
+    case GG: calib_mfma_kernel<GG><<<grid, dim3(CAL_THREADS), 0, st>>>(q, k, s.n_kv_heads, T, rows, nwg_q, chunk_q, \
+                                                                    chunk_k, part); break;
+    SJSA_CAL(1) SJSA_CAL(2) SJSA_CAL(4) SJSA_CAL(8)
+#undef SJSA_CAL
     default: return hipErrorInvalidValue;
   }
   calib_reduce_kernel<<<dim3(HEAD_DIM * HEAD_DIM / 256, (unsigned)s.n_kv_heads, 2), dim3(256), 0, st>>>(
-      part, nwg, SQ, SK);
+      part, nwg_q, nwg_k, SQ, SK);
   return hipGetLastError();
 }
 
@@ -204,8 +441,7 @@ extern "C" {
 size_t sjsa_calib_workspace_size(const sjsa_shape* shape, int64_t n_tokens) {
   if (!shape || shape->batch < 1 || shape->n_kv_heads < 1 || shape->head_dim != HEAD_DIM || n_tokens < 1) return 0;
   if (shape->group != 1 && shape->group != 2 && shape->group != 4 && shape->group != 8) return 0;
-  const int nwg = calib_groups(*shape, (int64_t)shape->batch * n_tokens);
-  return (size_t)shape->n_kv_heads * 2 * nwg * HEAD_DIM * HEAD_DIM * sizeof(double);
+  return calib_part_bytes(*shape, (int64_t)shape->batch * n_tokens);
 }
 
 int sjsa_calib_accumulate(const sjsa_shape* shape, const void* q, const void* k, int64_t n_tokens, double* SQ,
