@@ -54,8 +54,11 @@ Layout make_layout(const sjsa_shape& s, int k) {
   if (chunk > ATT_MAX_CHUNK) chunk = ATT_MAX_CHUNK;
   L.chunk = (int)chunk;
   L.nsplit = (int)((k + chunk - 1) / chunk);
-  L.ntile_cap = (s.capacity + TILE_ROWS - 1) / TILE_ROWS;
-  L.cand_stride = (s.capacity + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
+  L.tile_rows = tile_rows(s.rank * ((s.flags & SJSA_FLAG_KPROJ_FP8) != 0 ? 1 : 2));
+  L.ntile = (s.capacity + L.tile_rows - 1) / L.tile_rows;
+  const int64_t rows_min = tile_rows(s.rank * 2);
+  L.ntile_cap = (s.capacity + rows_min - 1) / rows_min;
+  L.cand_stride = (s.capacity + TILE_ROWS_MAX - 1) / TILE_ROWS_MAX * TILE_ROWS_MAX;
   size_t off = 0;
   L.off_qhat = off;
   off = align_up(off + (size_t)L.units * QHAT_STRIDE * sizeof(float), WS_ALIGN);

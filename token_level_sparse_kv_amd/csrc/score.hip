@@ -10,7 +10,7 @@
 // prep  (one workgroup per (b, h)): q_bar in fp32 (sum in head order, then divide
 //       by G), q_hat = M_h q_bar (fp32), and the unit's candidate threshold, placed
 //       from the scores of sample rows (one adjacent pair in each of 1024 strata).
-// scan  (one workgroup per 4096-row tile of a unit): streams Kproj rows with
+// scan  (one workgroup per tile of a unit, about 128 KB of rows): streams Kproj rows with
 //       128-bit coalesced loads, each lane holding 8 of a row's r values; the
 //       partial dots of the r/8 lanes of a row are reduced with DPP lane moves in a
 //       transposed pattern, so that after the reduction each lane owns the full
@@ -32,8 +32,8 @@ constexpr int SCORE_THREADS = 256;
 constexpr int SCORE_WAVES = SCORE_THREADS / 64;
 constexpr int GROUP_ROWS = 64;       // rows covered by r/8 wave-wide 16-byte loads
 constexpr int SCORE_UNROLL = 2;      // groups per segment
-constexpr int SEGS_PER_TILE = TILE_ROWS / SEG_ROWS;
-constexpr int STASH = TILE_ROWS / SCORE_WAVES;    // keys of one wave's rows of a tile
+constexpr int SEGS_MAX = TILE_ROWS_MAX / SEG_ROWS;
+constexpr int STASH = TILE_ROWS_MAX / SCORE_WAVES;    // keys of one wave's rows of a tile
 // rows scored by the prep to place the threshold: more samples give a tighter
 // threshold (fewer candidates) but cost the prep about as much time as the later
 // stages save (measured with 4096 at the 128K batch-16 shape)
@@ -50,7 +50,7 @@ constexpr int32_t DEFAULT_WAIT_US = 200;
 constexpr uint64_t TICKS_PER_US = 100;
 
 static_assert(SEG_ROWS == GROUP_ROWS * SCORE_UNROLL, "one wave iteration covers one segment");
-static_assert(SEGS_PER_TILE <= 64, "one wave scans the segment counts");
+static_assert(SEGS_MAX <= 64, "one wave scans the segment counts");
 
 // Tag of the words one launch publishes for a unit: a function of the unit's step
 // count on this workspace, which the selection that follows every fused launch
@@ -94,9 +94,9 @@ struct PrepShared {
 
 struct ScanShared {
   uint32_t stash[SCORE_WAVES][STASH];   // a wave's keys, then its candidates (compacted in place)
-  uint32_t segcnt[SEGS_PER_TILE];
-  uint32_t segoff[SEGS_PER_TILE + 1];
-  uint32_t sstart[SEGS_PER_TILE];
+  uint32_t segcnt[SEGS_MAX];
+  uint32_t segoff[SEGS_MAX + 1];
+  uint32_t sstart[SEGS_MAX];
   uint32_t overflow[SCORE_WAVES];
   uint32_t wmax[SCORE_WAVES];
   alignas(16) uint32_t words[SCORE_WAVES][64];  // published words, as each wave read them
@@ -458,11 +458,12 @@ struct ScanArgs {
   int n_kv_heads;
   int64_t cap;
   int64_t stride;
-  int64_t ntile_cap;
+  int64_t ntile;             // tiles per unit
+  int64_t ntile_cap;         // count words per unit
   int64_t cand_stride;
 };
 
-// Scan of tile `tile` (rows [tile*TILE_ROWS, +TILE_ROWS)) of one unit, 256 threads.
+// Scan of tile `tile` (rows [tile*TR, +TR), TR = tile_rows(R*KB)) of one unit, 256 threads.
 // A segment is the SEG_ROWS = 128 rows one wave covers in one iteration
 // (SCORE_UNROLL groups of 64); the waves take the tile's segments in turn (wave w:
 // segments w, w + 4, ...), so the workgroup streams one contiguous region. Loads are
@@ -479,7 +480,7 @@ struct ScanArgs {
 // lane). The candidates are compacted in place over the stash (a segment's entries
 // land no later than its own keys, which are read first). At the end the workgroup
 // writes the tile's candidates, in position order, to its region of the candidate
-// buffer (entries [x*TILE_ROWS, ...) for tile x), and to counts[x] their number (low
+// buffer (entries [x*TR, ...) for tile x), and to counts[x] their number (low
 // word; TILE_OVERFLOW when a published word did not arrive in time) and their
 // greatest key (high word; 0 when there are none); writes in the middle of the
 // stream cost far more HBM time than their size. With WRITE_DENSE every score is
@@ -496,11 +497,13 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
   constexpr int VPC = 16 / KB;          // values per 16-byte word
   constexpr int RPL = 64 / LPR;         // rows per wave-wide load
   constexpr int RW = R * KB / 4;        // 32-bit words of a projected row
+  constexpr int TR = tile_rows(R * KB);
+  constexpr int SEGS = TR / SEG_ROWS;   // segments per tile
   const int b = unit / a.n_kv_heads;
   const int n = (int)min((int64_t)max(a.seq_len[b], 0), a.cap);      // cap < 2^30
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int seg0 = tile * SEGS_PER_TILE;
+  const int seg0 = tile * SEGS;
   if (seg0 * SEG_ROWS >= n) return;            // the whole tile lies past the end
   const bool take_all = POLL ? a.k >= n : (a.tlow[unit * 2 + 1] & 1u) != 0u;
   if (take_all && !WRITE_DENSE) return;
@@ -520,7 +523,7 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
     deadline = __builtin_readsteadycounter() + wait_ticks;
     if (apos_b) {
       const int64_t ap = apos_b[b];
-      if (ap >= (int64_t)tile * TILE_ROWS && ap < (int64_t)(tile + 1) * TILE_ROWS && ap < a.cap) apos = (int)ap;
+      if (ap >= (int64_t)tile * TR && ap < (int64_t)(tile + 1) * TR && ap < a.cap) apos = (int)ap;
     }
   } else {
 #pragma unroll
@@ -579,7 +582,7 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
     }
   }
   if (ok) {
-    for (; j < SEGS_PER_TILE; j += SCORE_WAVES, ++nseg) {
+    for (; j < SEGS; j += SCORE_WAVES, ++nseg) {
       const int g0 = (seg0 + j) * SEG_ROWS;
       if (g0 >= n) break;
       u32x4 w[SCORE_UNROLL][LPR];
@@ -641,7 +644,8 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
         const bool c = row < n && key[u] >= tkey;
         const uint64_t m = __ballot(c);
         if (c) {
-          stash[wcount + count + (uint32_t)__popcll(m & earlier)] = cand_entry(cand_rel(key[u], tkey, tshift), row);
+          stash[wcount + count + (uint32_t)__popcll(m & earlier)] =
+              cand_entry(cand_rel(key[u], tkey, tshift), row - seg0 * SEG_ROWS);   // offset in the tile
           kmax = max(kmax, key[u]);
         }
         count += (uint32_t)__popcll(m);
@@ -652,7 +656,7 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
   }
   kmax = wave_max_u32(kmax);
   if (lane == 0) {
-    for (int j = wave + filtered * SCORE_WAVES; j < SEGS_PER_TILE; j += SCORE_WAVES) sh.segcnt[j] = 0u;
+    for (int j = wave + filtered * SCORE_WAVES; j < SEGS; j += SCORE_WAVES) sh.segcnt[j] = 0u;
     sh.overflow[wave] = ok ? 0u : 1u;
     sh.wmax[wave] = kmax;
   }
@@ -661,9 +665,9 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
   // segoff[jj] (the counts of segments 0 .. jj-1) in the output and at sstart[jj]
   // (the counts of the same wave's earlier segments) in its wave's stash
   if (wave == 0) {
-    const uint32_t c = lane < SEGS_PER_TILE ? sh.segcnt[lane] : 0u;
+    const uint32_t c = lane < SEGS ? sh.segcnt[lane] : 0u;
     const uint32_t inc = wave_incl_scan(c);
-    if (lane < SEGS_PER_TILE) {
+    if (lane < SEGS) {
       sh.segoff[lane + 1] = inc;
       uint32_t st = 0;
       for (int q = lane % SCORE_WAVES; q < lane; q += SCORE_WAVES) st += sh.segcnt[q];
@@ -675,12 +679,12 @@ __device__ __forceinline__ void scan_body(ScanShared& sh, int unit, int tile, co
   bool ovf = false;
 #pragma unroll
   for (int v = 0; v < SCORE_WAVES; ++v) ovf = ovf || sh.overflow[v] != 0u;
-  const uint32_t tot = sh.segoff[SEGS_PER_TILE];
+  const uint32_t tot = sh.segoff[SEGS];
   if (!ovf) {
     // every thread writes entries e, e + 256, ...: coalesced, streamed past the caches
-    uint32_t* wtile = a.cand + (size_t)unit * a.cand_stride + (size_t)tile * TILE_ROWS;
+    uint32_t* wtile = a.cand + (size_t)unit * a.cand_stride + (size_t)tile * TR;
     for (uint32_t e = threadIdx.x; e < tot; e += SCORE_THREADS) {
-      int lo = 0, hi = SEGS_PER_TILE;            // the segment holding entry e
+      int lo = 0, hi = SEGS;                     // the segment holding entry e
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (sh.segoff[mid] <= e) lo = mid; else hi = mid;
@@ -703,7 +707,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void prep_kernel(PrepArgs a, PrepApp
   prep_body<R, KB, APPEND, false>(sh, blockIdx.x, a, ap, nullptr, 0u);
 }
 
-// grid = (ceil(cap / TILE_ROWS), B * H_kv)
+// grid = (ntile_cap, B * H_kv)
 template <int R, int KB, bool WRITE_DENSE>
 __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(ScanArgs a) {
   __shared__ ScanShared sh;
@@ -716,7 +720,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(ScanArgs a) {
 template <int R, int KB>
 constexpr int fused_waves() { return R <= 32 ? (KB == 2 ? 8 : 7) : (KB == 2 ? 5 : 6); }
 
-// grid = B*H_kv + B*H_kv * ntile_cap, one-dimensional: workgroups [0, units) are the
+// grid = B*H_kv + B*H_kv * ntile, one-dimensional: workgroups [0, units) are the
 // preps (dispatched first), then the scan tiles unit by unit.
 template <int R, int KB, bool APPEND>
 __global__ __launch_bounds__(SCORE_THREADS) __attribute__((amdgpu_waves_per_eu(fused_waves<R, KB>()))) void prep_scan_kernel(PrepArgs pa, PrepAppend ap, ScanArgs sa,
@@ -729,8 +733,8 @@ __global__ __launch_bounds__(SCORE_THREADS) __attribute__((amdgpu_waves_per_eu(f
     prep_body<R, KB, APPEND, true>(sh.p, unit, pa, ap, sync, launch_tag(epoch, unit));
   } else {
     const int64_t id = bid - units;
-    const int unit = (int)(id / sa.ntile_cap);
-    const int tile = (int)(id - (int64_t)unit * sa.ntile_cap);
+    const int unit = (int)(id / sa.ntile);
+    const int tile = (int)(id - (int64_t)unit * sa.ntile);
     scan_body<R, KB, false, true>(sh.s, unit, tile, sa, sync, launch_tag(epoch, unit),
                                   APPEND ? ap.pos : nullptr, wait_ticks);
   }
@@ -768,6 +772,7 @@ ScanArgs scan_args(const sjsa_shape& s, const Layout& L, const unsigned char* kp
   a.n_kv_heads = s.n_kv_heads;
   a.cap = s.capacity;
   a.stride = L.score_stride;
+  a.ntile = L.ntile;
   a.ntile_cap = L.ntile_cap;
   a.cand_stride = L.cand_stride;
   return a;
@@ -801,7 +806,7 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj_
                         unsigned char* ws, hipStream_t st) {
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
   const ScanArgs a = scan_args(s, L, static_cast<const unsigned char*>(kproj_v), seq_len, 0, ws);
-  const dim3 grid((unsigned)L.ntile_cap, (unsigned)L.units), block(SCORE_THREADS);
+  const dim3 grid((unsigned)L.ntile, (unsigned)L.units), block(SCORE_THREADS);
   const bool dense = (s.flags & SJSA_FLAG_WRITE_SCORES) != 0;
 #define SJSA_SCAN2(RR, KB, DD) score_kernel<RR, KB, DD><<<grid, block, 0, st>>>(a)
 #define SJSA_SCAN(RR)                                              \
@@ -824,7 +829,7 @@ hipError_t launch_score(const sjsa_shape& s, const Layout& L, const void* kproj_
 hipError_t launch_prep_scan(const sjsa_shape& s, const Layout& L, const uint16_t* q, const float* M,
                             const void* kproj_v, const int32_t* seq_len, int k, unsigned char* ws, hipStream_t st,
                             const PrepAppend* ap) {
-  const int64_t blocks = L.units * (L.ntile_cap + 1);
+  const int64_t blocks = L.units * (L.ntile + 1);
   if ((s.flags & SJSA_FLAG_WRITE_SCORES) != 0 || blocks > 0x7fffffff) {
     hipError_t e = launch_prep(s, L, q, M, kproj_v, seq_len, k, ws, st, ap);
     return e == hipSuccess ? launch_score(s, L, kproj_v, seq_len, ws, st) : e;

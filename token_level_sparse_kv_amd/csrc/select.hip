@@ -53,7 +53,7 @@ struct SelShared {
   uint32_t hist[HIST_BINS];
   uint32_t buf[LDS_WORDS];
   uint32_t hist2[HIST2_BINS];
-  uint32_t toff[64];                 // candidate path: tile output offsets of a chunk
+  uint32_t toff[144];                // candidate path: tile output offsets of a chunk
   float qh[64];                      // candidate path: q_hat, for exact scores at the boundary
   uint32_t wtot[2][2 * SEL_WAVES];   // [buffer][A totals of waves | C totals of waves]
   uint32_t scan[SEL_WAVES];
@@ -673,8 +673,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  // Candidates. Scan tile x (rows [x*TILE_ROWS, +TILE_ROWS)) left its candidates, in
-  // position order, at entries [x*TILE_ROWS, ...) as (the key relative to the
+  // Candidates. Scan tile x (rows [x*TR, +TR)) left its candidates, in
+  // position order, at entries [x*TR, ...) as (the key relative to the
   // threshold, cand_rel, in CAND_KEY_BITS bits; the row offset in the tile); counts[x]
   // holds their number (TILE_OVERFLOW when it could not keep them all) and their
   // greatest key. Every candidate key is at least the scan's threshold key, so no
@@ -682,12 +682,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   // it places them. Tiles are
   // gathered in chunks of CHUNK_T; wave w owns TPW consecutive tiles of a chunk and
   // loads their first SPEC*64 entries unconditionally (entries past the count are
-  // never used) together with the counts, so one memory round trip serves a chunk.
+  // never used) together with the counts, so one memory round trip serves a chunk
+  // (64 tiles of 2048 rows, or 32 of 4096, cover a 131072-row sequence).
   // The first chunk's loads are issued before the sequence length is known (tiles
   // clamped to the capacity), so they overlap the kernel's first load; later chunks
   // clamp to the sequence.
-  constexpr int TPW = 2;
-  constexpr int SPEC = 5;
+  constexpr int TR = tile_rows(R * KB);
+  constexpr int TPW = 8192 / TR;
+  constexpr int SPEC = TR >= 4096 ? 5 : (TR >= 2048 ? 3 : 2);
   constexpr int CHUNK_T = SEL_WAVES * TPW;
   const uint64_t* cnt_u = counts + (size_t)unit * ntile_cap;
   const uint32_t* cand_u = cand + (size_t)unit * cand_stride;
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     for (int i = 0; i < TPW; ++i) {
       const int64_t t = min(t0 + wave * TPW + i, tiles - 1);
 #pragma unroll
-      for (int e = 0; e < SPEC; ++e) v[i][e] = __builtin_nontemporal_load(cand_u + t * TILE_ROWS + 64 * e + lane);
+      for (int e = 0; e < SPEC; ++e) v[i][e] = __builtin_nontemporal_load(cand_u + t * TR + 64 * e + lane);
     }
   };
   const bool cand_path = scores == nullptr;
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     if (tid == 0) epoch[unit] += 1u;
     tkey = tlow[unit * 2];
     tshift = tlow[unit * 2 + 1] >> TLOW_SHIFT_POS;
-    load_chunk(0, ntile_cap);
+    load_chunk(0, (cap + TR - 1) / TR);            // the scan's tiles at capacity
     if (tid < R) sh.qh[tid] = qhat[(size_t)unit * QHAT_STRIDE + tid];
     if (tid == 0) sh.misc[6] = 0;                 // boundary entry counter (read after many barriers)
   }
@@ -732,11 +734,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
       for (int i = tid; i < kk; i += SEL_THREADS) out[i] = i;
     return;
   }
-  const int64_t ntiles = (n + TILE_ROWS - 1) / TILE_ROWS;
+  const int64_t ntiles = (n + TR - 1) / TR;
   // a tile that could not keep its candidates counts OVF_MARK in the chunk's scan (a
-  // tile holds at most TILE_ROWS candidates, so 32 marks and 32 counts cannot collide)
+  // tile holds at most TR candidates, so a chunk's marks and counts cannot collide)
   constexpr uint32_t OVF_MARK = 1u << 24;
-  static_assert(CHUNK_T * TILE_ROWS < OVF_MARK && (uint64_t)CHUNK_T * OVF_MARK < (1ull << 32), "marks apart");
+  static_assert(CHUNK_T * TR < OVF_MARK && (uint64_t)CHUNK_T * OVF_MARK < (1ull << 32), "marks apart");
   uint32_t total = 0;
   bool exact = false;                             // block-uniform: take the exact path
   if (helper) {
@@ -756,7 +758,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   uint32_t* ckey = sh.buf;
   int32_t* cpos = reinterpret_cast<int32_t*>(sh.buf + CAND_CAP);
   uint32_t* toff = sh.toff;                       // CHUNK_T + 1 output offsets
-  static_assert(CHUNK_T + 1 <= 64, "toff holds a chunk's offsets");
+  static_assert(CHUNK_T + 1 <= 144, "toff holds a chunk's offsets");
   // the threshold's first two histograms start from zero
   for (int i = tid; i < HIST_BINS; i += SEL_THREADS) sh.hist[i] = 0u;
   for (int i = tid; i < HIST2_BINS; i += SEL_THREADS) sh.hist2[i] = 0u;
@@ -786,16 +788,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         const uint32_t dst = total + o + j;
         if (j < ct && dst < (uint32_t)CAND_CAP) {
           ckey[dst] = v[i][e] >> CAND_ROW_BITS;
-          cpos[dst] = (int32_t)((t0 + tl) * TILE_ROWS + (v[i][e] & CAND_ROW_MASK));
+          cpos[dst] = (int32_t)((t0 + tl) * TR + (v[i][e] & CAND_ROW_MASK));
           atomicAdd(&sh.hist[v[i][e] >> (32 - HIST1_BITS)], 1u);
         }
       }
       for (uint32_t j = SPEC * 64 + lane; j < ct; j += 64) {     // tiles with many candidates
         const uint32_t dst = total + o + j;
         if (dst < (uint32_t)CAND_CAP) {
-          const uint32_t x = __builtin_nontemporal_load(cand_u + (t0 + tl) * TILE_ROWS + j);
+          const uint32_t x = __builtin_nontemporal_load(cand_u + (t0 + tl) * TR + j);
           ckey[dst] = x >> CAND_ROW_BITS;
-          cpos[dst] = (int32_t)((t0 + tl) * TILE_ROWS + (x & CAND_ROW_MASK));
+          cpos[dst] = (int32_t)((t0 + tl) * TR + (x & CAND_ROW_MASK));
           atomicAdd(&sh.hist[x >> (32 - HIST1_BITS)], 1u);
         }
       }

@@ -14,7 +14,16 @@ constexpr int HIST_BINS = 4096;      // first radix digit: top 12 bits of the sc
 constexpr int HIST_SHIFT = 20;
 constexpr int QHAT_STRIDE = 64;      // floats reserved per unit for q_hat (r <= 64)
 constexpr int SEG_ROWS = 128;        // rows per scan segment (one wave iteration)
-constexpr int TILE_ROWS = 4096;      // rows per scan workgroup; one candidate region
+// Rows per scan workgroup (one candidate region each): about 128 KB of projected rows
+// per tile, between 1024 and 4096 rows. Longer tiles leave a longer end of the launch
+// in which few workgroups still run; shorter ones add per-workgroup cost.
+constexpr int TILE_BYTES = 128 * 1024;
+constexpr int TILE_ROWS_MIN = 1024;
+constexpr int TILE_ROWS_MAX = 4096;
+__host__ __device__ constexpr int tile_rows(int row_bytes) {
+  return row_bytes <= 0 || TILE_BYTES / row_bytes > TILE_ROWS_MAX ? TILE_ROWS_MAX
+         : (TILE_BYTES / row_bytes < TILE_ROWS_MIN ? TILE_ROWS_MIN : TILE_BYTES / row_bytes);
+}
 constexpr uint32_t TILE_OVERFLOW = 0xffffffffu;   // tile count: the tile's candidates are not usable
 // Words a unit's prep hands to the scan workgroups of the same launch when the two
 // run as one kernel: 64-bit words (tag << 32 | value), the tag naming the launch.
@@ -23,7 +32,7 @@ constexpr int SYNC_THR = 64;         // word: threshold key ([0, r) hold q_hat)
 constexpr int SYNC_ROW = 96;         // words: the appended token's projected row (r*KB/4 <= 32)
 // A candidate entry holds its key relative to the unit's threshold key,
 // rel = (key - threshold) >> shift clamped to CAND_KEY_BITS bits, above the row's
-// offset inside its scan tile (TILE_ROWS = 2^CAND_ROW_BITS rows). The prep picks the
+// offset inside its scan tile (at most 2^CAND_ROW_BITS rows). The prep picks the
 // unit's shift so that four times the sampled keys' range above the threshold fits
 // the CAND_KEY_BITS bits (shift <= CAND_ROW_BITS, since keys have 32 bits): the
 // selection ranks by rel and recomputes the exact score only of the entries that
@@ -32,7 +41,7 @@ constexpr int CAND_ROW_BITS = 12;
 constexpr int CAND_KEY_BITS = 32 - CAND_ROW_BITS;
 constexpr uint32_t CAND_ROW_MASK = (1u << CAND_ROW_BITS) - 1u;
 constexpr uint32_t CAND_REL_MAX = (1u << CAND_KEY_BITS) - 1u;
-static_assert(TILE_ROWS == 1 << CAND_ROW_BITS, "a tile offset fills the entry's low bits");
+static_assert(TILE_ROWS_MAX == 1 << CAND_ROW_BITS, "a tile offset fits the entry's low bits");
 __host__ __device__ constexpr uint32_t cand_rel(uint32_t key, uint32_t tkey, uint32_t shift) {
   return key <= tkey ? 0u : ((key - tkey) >> shift < CAND_REL_MAX ? (key - tkey) >> shift : CAND_REL_MAX);
 }
@@ -53,8 +62,13 @@ struct Layout {
   int64_t score_stride = 0;   // floats per unit row of the score buffer
   int nsplit = 1;             // attention splits per unit
   int chunk = 0;              // selected indices per split
-  int64_t ntile_cap = 0;      // scan tiles per unit (capacity / TILE_ROWS, rounded up)
-  int64_t cand_stride = 0;    // 4-byte candidate entries per unit (capacity rounded up to TILE_ROWS)
+  // The workspace's offsets do not depend on the projected cache's format (stage calls
+  // that do not name it share one workspace): count words and candidate regions are
+  // sized for the format with the most tiles.
+  int64_t tile_rows = 0;      // rows per scan tile of this shape's format
+  int64_t ntile = 0;          // scan tiles per unit of this shape's format (capacity / tile_rows, up)
+  int64_t ntile_cap = 0;      // count words per unit (tiles of the bf16 cache, the most of any format)
+  int64_t cand_stride = 0;    // 4-byte candidate entries per unit (capacity rounded up to TILE_ROWS_MAX)
   size_t off_qhat = 0, off_tlow = 0, off_counts = 0, off_cand = 0, off_scores = 0, off_partials = 0;
   size_t off_sync = 0;        // SYNC_WORDS 64-bit words per unit
   size_t off_epoch = 0;       // one u32 per unit: steps completed on this workspace
