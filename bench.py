@@ -47,7 +47,7 @@ WORKLOAD = ("long-batched decode step: batch 16, 32 query / 8 KV heads (G=4), d=
             "hitters (key x4), random orthonormal basis per KV head, 8 query sets cycled")
 PMC_FILE = os.path.join(ROOT, "profiles", "prep_scan_kernel_long_batched_pmc.json")
 SCAN_SOURCES = [os.path.join(ROOT, "token_level_sparse_kv_amd", "csrc", f)
-                for f in ("score.hip", "sjsa_device.h", "key_proj.h")]
+                for f in ("score.hip", "sjsa_device.h", "key_proj.h", "sjsa_internal.h")]
 MEMBW_LIB = os.path.join(ROOT, "token_level_sparse_kv_amd", "lib", "libsjsa_membw.so")
 
 

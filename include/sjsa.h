@@ -35,9 +35,10 @@
  *     failed check returns a negative status and enqueues nothing. A launch
  *     failure reported by the HIP runtime returns SJSA_ERR_HIP.
  *   - Calls that share a workspace must not overlap (use one stream or order
- *     them). The library keeps no global mutable state: what one call hands to
- *     the next (a unit's step count, the candidates of the scan) lives in the
- *     caller's workspace.
+ *     them). What one call hands to the next (a unit's step count, the
+ *     candidates of the scan) lives in the caller's workspace; the only
+ *     process-wide state is the device address of the static scratch array of
+ *     sjsa_decode_step_append_noalloc, looked up once per device and kept.
  *   - Results are deterministic: identical inputs give bit-identical outputs.
  */
 #ifndef SJSA_H
@@ -131,6 +132,11 @@ size_t sjsa_decode_workspace_size(const sjsa_shape* shape, int32_t k);
  * idx[b,h] holds the min(k, n_b) selected positions in ascending order, then -1.
  * Ranking: larger score first, equal scores by lower position, -0 == +0, NaN
  * last. out is zero where n_b = 0.
+ * Cost: a unit whose scan candidates cannot be used (more than 16384 of them,
+ * which is always so for k > 16384 and n_b > k; fewer than k; or a scan
+ * workgroup that gave up waiting, see fused_wait_us) has its scores recomputed
+ * and selected exactly: the same result, at about 1.4 times the step's time when
+ * every unit of the 128K-token batch-16 step takes that path.
  * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _K, _WORKSPACE, _ALIGN, _HIP.
  */
 int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, const void* V,
