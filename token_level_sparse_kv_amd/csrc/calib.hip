@@ -7,26 +7,25 @@
 // head), section 迹归一化 (each moment normalized to unit trace) and section 闭式谱解
 // (the basis rows are the top-r eigenvectors of the sum of the normalized moments).
 //
-// calib_mfma_kernel: grid (nwg_q + nwg_k, H_kv), 256 threads (4 waves), one workgroup
-// per CU (its LDS). Workgroups [0, nwg_q) accumulate the group-mean query's moment
-// (fp32 sum of the G bf16 heads in head order, divided by G), the rest the bf16 key's;
-// each takes a contiguous slice of the B*T positions. Only the upper triangle of the
-// symmetric 128 x 128 moment is formed: its 36 tiles of 16 x 16 (tile row bi <= tile
-// column bj), 9 per wave, each a sum over positions p of x_p[16 bi ..] x_p[16 bj ..]^T
-// on the matrix cores. Positions are staged transposed in LDS (dim-major), 64 query
-// or 256 key positions at a time, so a lane's operand fragment (one dim x 4 or 8
-// positions of the instruction's K) is one 16-byte read, and each wave reads one
-// fragment per 16-dim block it touches (4 or 6) for its 9 tiles:
+// calib_mfma_kernel: grid (nwg_q + nwg_k, H_kv), 512 threads, one workgroup per CU (its
+// LDS). Workgroups [0, nwg_q) accumulate the group-mean query's moment (fp32 sum of the
+// G bf16 heads in head order, divided by G), the rest the bf16 key's; each takes a
+// contiguous slice of the B*T positions. Only the upper triangle of the symmetric
+// 128 x 128 moment is formed: its 36 tiles of 16 x 16 (tile row bi <= tile column bj),
+// each a sum over positions p of x_p[16 bi ..] x_p[16 bj ..]^T on the matrix cores:
 //  * keys: v_mfma_f32_16x16x32_bf16, 32 positions per instruction; products of two
 //    bf16 values are exact in fp32;
 //  * mean queries: v_mfma_f32_16x16x4_f32, 4 positions per instruction.
-// The next stage is loaded (each wave instruction reads 64-byte pieces of 16 rows;
-// the four waves complete them) while the current one is multiplied. The fp32 tile
-// sums are folded into fp64 tile sums kept in LDS every 256 key positions and every
+// Waves 4-7 load the rows (128 query or 256 key positions per stage) and write them
+// transposed (dim-major) into a double-buffered LDS stage, so a lane's operand fragment
+// (one dim x 4 or 8 positions of the instruction's K) is one 16-byte read; waves 0-3
+// take 9 tiles each, chosen so a wave reads one fragment per 16-dim block it touches
+// (4 or 6) and reuses it across its tiles. The fp32 tile sums are folded into fp64
+// sums held in the multiplying lanes' registers every 256 key positions and every
 // 128 query positions (whose products are rounded), so no element's fp32 run exceeds
-// 256 rounding steps. At the end each workgroup writes its fp64 tiles to the
-// workspace; calib_reduce_kernel adds them in workgroup order (deterministic) into the
-// caller's fp64 accumulators, mirroring the upper triangle into the lower one.
+// 256 rounding steps. At the end each workgroup writes its fp64 tiles to the workspace;
+// calib_reduce_kernel adds them in workgroup order (deterministic) into the caller's
+// fp64 accumulators, mirroring the upper triangle into the lower one.
 #include <math.h>
 #include <string.h>
 
@@ -38,19 +37,23 @@
 namespace sjsa {
 namespace {
 
-constexpr int CAL_THREADS = 256;
+constexpr int CAL_THREADS = 512;          // waves 0-3 multiply, waves 4-7 load and stage
+constexpr int CAL_MMA_THREADS = 256;
 constexpr int CAL_TILES = 36;             // upper-triangle 16 x 16 tiles of a 128 x 128 moment
-constexpr int CAL_TPW = CAL_TILES / (CAL_THREADS / 64);   // tiles per wave
-constexpr int CAL_PQ = 64;                // query positions staged at a time
+constexpr int CAL_TPW = CAL_TILES / (CAL_MMA_THREADS / 64);   // tiles per product wave
 constexpr int CAL_PK = 256;               // key positions staged at a time
-constexpr int CAL_LDF = CAL_PQ + 4;       // fp32 row pitch of the staged queries (floats)
-constexpr int CAL_LDB = CAL_PK + 8;       // bf16 row pitch of the staged keys (halves)
 constexpr int CAL_FOLD_Q = 128;           // query positions per fp32 run
 constexpr int CAL_FOLD_K = 256;           // key positions per fp32 run
-constexpr int CAL_STAGE_BYTES =
-    HEAD_DIM * CAL_LDF * 4 > HEAD_DIM * CAL_LDB * 2 ? HEAD_DIM * CAL_LDF * 4 : HEAD_DIM * CAL_LDB * 2;
-static_assert(CAL_TILES % (CAL_THREADS / 64) == 0, "tiles split evenly over the waves");
-static_assert(CAL_FOLD_Q % CAL_PQ == 0 && CAL_FOLD_K % CAL_PK == 0, "runs hold whole stages");
+// query positions staged at a time: 128 KB of query rows per stage up to G = 4
+template <int G>
+constexpr int cal_pq() { return G <= 4 ? 128 : 64; }
+constexpr int cal_ldf(int p) { return p + 4; }   // fp32 row pitch of staged queries (floats)
+constexpr int cal_ldb(int p) { return p + 8; }   // bf16 row pitch of staged keys (halves)
+constexpr int CAL_STAGE_BYTES = HEAD_DIM * cal_ldf(128) * 4 > HEAD_DIM * cal_ldb(CAL_PK) * 2
+                                    ? HEAD_DIM * cal_ldf(128) * 4
+                                    : HEAD_DIM * cal_ldb(CAL_PK) * 2;
+static_assert(CAL_TILES % (CAL_MMA_THREADS / 64) == 0, "tiles split evenly over the product waves");
+static_assert(CAL_FOLD_K % CAL_PK == 0 && CAL_FOLD_Q % 64 == 0, "runs hold whole stages");
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -58,10 +61,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // Tile t of the upper triangle, row-major over (bi, bj), bi <= bj < 8.
 __host__ __device__ constexpr int tile_index(int bi, int bj) { return bi * 8 - bi * (bi - 1) / 2 + (bj - bi); }
 
-// The four waves' tiles, 9 each, chosen so that a wave's tiles touch few 16-dim
-// blocks: one operand fragment per block is read from LDS per instruction step and
-// reused by all the wave's tiles in that block (4 or 6 reads per 9 products instead of
-// 18). Wave 0: the upper triangle of blocks 0..3 without (3, 3); wave 1: that of
+// The four product waves' tiles, 9 each, chosen so that a wave's tiles touch few
+// 16-dim blocks: one operand fragment per block is read from LDS per instruction step
+// and reused by all the wave's tiles in that block (4 or 6 reads per 9 products instead
+// of 18). Wave 0: the upper triangle of blocks 0..3 without (3, 3); wave 1: that of
 // blocks 4..7 without (7, 7); wave 2: blocks 0..3 x 4..5 and (3, 3); wave 3: blocks
 // 0..3 x 6..7 and (7, 7).
 template <int W>
@@ -96,8 +99,7 @@ struct WaveTiles<3> {
 };
 
 struct CalShared {
-  __attribute__((aligned(16))) float stage[CAL_STAGE_BYTES / 4];   // staged positions, dim-major
-  double acc[CAL_TILES * 256];                                     // fp64 tile sums
+  __attribute__((aligned(16))) float stage[2][CAL_STAGE_BYTES / 4];   // staged positions, dim-major (double buffer)
 };
 
 constexpr bool wave_tiles_cover_once() {
@@ -126,12 +128,13 @@ __device__ __forceinline__ void calib_products(const float* XF, const uint16_t* 
                                                f32x4_t (&acc)[CAL_TPW]) {
   using WT = WaveTiles<W>;
   if constexpr (IS_Q) {
+    constexpr int LD = cal_ldf(P);
 #pragma unroll 1
     for (int c0 = 0; c0 < P; c0 += 16) {
       f32x4_t f[WT::nb];
 #pragma unroll
       for (int b = 0; b < WT::nb; ++b)
-        f[b] = *reinterpret_cast<const f32x4_t*>(&XF[(16 * WT::blk[b] + li) * CAL_LDF + c0 + 4 * lg]);
+        f[b] = *reinterpret_cast<const f32x4_t*>(&XF[(16 * WT::blk[b] + li) * LD + c0 + 4 * lg]);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
@@ -140,12 +143,13 @@ __device__ __forceinline__ void calib_products(const float* XF, const uint16_t* 
       }
     }
   } else {
+    constexpr int LD = cal_ldb(P);
 #pragma unroll 2
     for (int c0 = 0; c0 < P; c0 += 32) {
       bf16x8_t f[WT::nb];
 #pragma unroll
       for (int b = 0; b < WT::nb; ++b)
-        f[b] = *reinterpret_cast<const bf16x8_t*>(&XB[(16 * WT::blk[b] + li) * CAL_LDB + c0 + 8 * lg]);
+        f[b] = *reinterpret_cast<const bf16x8_t*>(&XB[(16 * WT::blk[b] + li) * LD + c0 + 8 * lg]);
 #pragma unroll
       for (int u = 0; u < CAL_TPW; ++u)
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[WT::ta[u]], f[WT::tb[u]], acc[u], 0, 0, 0);
@@ -153,57 +157,39 @@ __device__ __forceinline__ void calib_products(const float* XF, const uint16_t* 
   }
 }
 
-// Adds wave W's fp32 tile sums into the fp64 ones and clears them. Lane (lg, li) holds
-// rows 4 lg + v, column li of each of the wave's tiles; no two lanes (and no two waves)
-// share an element, so this needs no synchronisation.
-template <int W>
-__device__ __forceinline__ void calib_fold(double* shacc, int li, int lg, f32x4_t (&acc)[CAL_TPW]) {
-  using WT = WaveTiles<W>;
-#pragma unroll
-  for (int u = 0; u < CAL_TPW; ++u) {
-    double* o = shacc + tile_index(WT::blk[WT::ta[u]], WT::blk[WT::tb[u]]) * 256 + (4 * lg) * 16 + li;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) o[v * 16] += (double)acc[u][v];
-    acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
 // One workgroup's slice: IS_Q selects the mean query's moment (G heads per position)
-// or the key's. Thread tid stages the 8-dim chunk c = tid / 16 of the position groups
-// j = tid % 16 + 16 i (4 consecutive positions each); a load instruction of a wave so
-// reads 64 bytes of each of 16 rows, the four waves the rest of those rows, and each
-// LDS write (4 positions of one dim) falls on its own banks.
+// or the key's. Waves 0-3 multiply (9 tiles each) and keep the fp64 sums of their
+// tiles in registers (lane (lg, li) owns rows 4 lg + v, column li of each tile);
+// waves 4-7 load the next stage while the current one is multiplied and then write it,
+// transposed, into the other half of a double-buffered LDS stage; one barrier per stage
+// hands a buffer from the loaders to the multipliers. A stage is large (128 KB of query
+// rows at G = 4, 64 KB of key rows), so one stage of loads in flight keeps the CU's
+// share of the HBM stream busy. Loader thread lt stages the 8-dim chunk c = lt / 16 of
+// the position groups j = lt % 16 + 16 i (4 consecutive positions each); a load
+// instruction of a wave so reads 64 bytes of each of 16 rows, the four loader waves
+// the rest of those rows, and each LDS write (4 positions of one dim) falls on its own
+// banks.
 template <int G, bool IS_Q>
 __device__ __forceinline__ void calib_body(CalShared& sh, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ k, int n_kv_heads, int64_t T, int64_t rows,
                                            int wg, int64_t chunk, double* __restrict__ out) {
-  constexpr int P = IS_Q ? CAL_PQ : CAL_PK;      // positions per stage
-  constexpr int NG = P / 64;                    // position groups per thread
+  constexpr int P = IS_Q ? cal_pq<G>() : CAL_PK;  // positions per stage
+  constexpr int NG = P / 64;                    // position groups per loader thread
   constexpr int NH = IS_Q ? G : 1;              // head rows loaded per position
-  float* XF = sh.stage;
-  uint16_t* XB = reinterpret_cast<uint16_t*>(sh.stage);
+  constexpr int LDF = cal_ldf(P), LDB = cal_ldb(P);
+  constexpr int FOLD = IS_Q ? CAL_FOLD_Q : CAL_FOLD_K;
+  static_assert(FOLD % P == 0 && HEAD_DIM * (IS_Q ? LDF * 4 : LDB * 2) <= CAL_STAGE_BYTES, "stage fits");
   const int h = blockIdx.y;
   const int64_t r0 = (int64_t)wg * chunk;
   const int64_t r1 = min(r0 + chunk, rows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool loader = wave >= CAL_MMA_THREADS / 64;
+  const int lt = tid - CAL_MMA_THREADS;         // loader thread index
   const int n_q_heads = n_kv_heads * G;
   const int li = lane & 15, lg = lane >> 4;
-  const int c = tid >> 4;
-
-  f32x4_t acc[CAL_TPW];
-#pragma unroll
-  for (int u = 0; u < CAL_TPW; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int i = tid; i < CAL_TILES * 256; i += CAL_THREADS) sh.acc[i] = 0.0;
-  __syncthreads();
-  auto fold = [&]() {
-    switch (wave) {
-      case 0: calib_fold<0>(sh.acc, li, lg, acc); break;
-      case 1: calib_fold<1>(sh.acc, li, lg, acc); break;
-      case 2: calib_fold<2>(sh.acc, li, lg, acc); break;
-      default: calib_fold<3>(sh.acc, li, lg, acc); break;
-    }
-  };
+  const int c = (lt >> 4) & 15;
+  const int64_t nst = r1 > r0 ? (r1 - r0 + P - 1) / P : 0;
 
   u32x4 raw[NG][4][NH];                         // [group][position in group][head]
   // (sequence, position) of a row from the stage's first row by one division per stage:
@@ -215,7 +201,7 @@ __device__ __forceinline__ void calib_body(CalShared& sh, const uint16_t* __rest
     for (int i = 0; i < NG; ++i) {
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int64_t off = 4 * ((tid & 15) + 16 * i) + s4;
+        const int64_t off = 4 * ((lt & 15) + 16 * i) + s4;
         int64_t t = t0 + (off < last ? off : last), b = b0;
         if (t >= T) {
           if (T >= P) {
@@ -237,10 +223,11 @@ __device__ __forceinline__ void calib_body(CalShared& sh, const uint16_t* __rest
       }
     }
   };
-  auto store_stage = [&](int64_t base) {
+  auto store_stage = [&](int64_t base, float* XF) {
+    uint16_t* XB = reinterpret_cast<uint16_t*>(XF);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int p0 = 4 * ((tid & 15) + 16 * i);
+      const int p0 = 4 * ((lt & 15) + 16 * i);
       bool valid[4];
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) valid[s4] = base + p0 + s4 < r1;
@@ -262,7 +249,7 @@ __device__ __forceinline__ void calib_body(CalShared& sh, const uint16_t* __rest
           f32x4_t o;
 #pragma unroll
           for (int s4 = 0; s4 < 4; ++s4) o[s4] = valid[s4] ? v[s4][e] / (float)G : 0.f;
-          *reinterpret_cast<f32x4_t*>(&XF[(8 * c + e) * CAL_LDF + p0]) = o;
+          *reinterpret_cast<f32x4_t*>(&XF[(8 * c + e) * LDF + p0]) = o;
         }
       } else {
         uint32_t w[4][4];
@@ -278,33 +265,79 @@ __device__ __forceinline__ void calib_body(CalShared& sh, const uint16_t* __rest
           const uint2 lo = make_uint2((w[0][e] & 0xffffu) | (w[1][e] << 16), (w[2][e] & 0xffffu) | (w[3][e] << 16));
           const uint2 hi = make_uint2((w[0][e] >> 16) | (w[1][e] & 0xffff0000u),
                                       (w[2][e] >> 16) | (w[3][e] & 0xffff0000u));
-          *reinterpret_cast<uint2*>(&XB[(8 * c + 2 * e) * CAL_LDB + p0]) = lo;
-          *reinterpret_cast<uint2*>(&XB[(8 * c + 2 * e + 1) * CAL_LDB + p0]) = hi;
+          *reinterpret_cast<uint2*>(&XB[(8 * c + 2 * e) * LDB + p0]) = lo;
+          *reinterpret_cast<uint2*>(&XB[(8 * c + 2 * e + 1) * LDB + p0]) = hi;
         }
       }
     }
   };
 
-  int staged = 0;                               // positions in the current fp32 run
-  if (r0 < r1) load_stage(r0);
-  for (int64_t base = r0; base < r1; base += P) {
-    __syncthreads();                            // the previous stage's operand reads are done
-    store_stage(base);
-    __syncthreads();
-    if (base + P < r1) load_stage(base + P);    // in flight during the products
-    switch (wave) {
-      case 0: calib_products<0, IS_Q, P>(XF, XB, li, lg, acc); break;
-      case 1: calib_products<1, IS_Q, P>(XF, XB, li, lg, acc); break;
-      case 2: calib_products<2, IS_Q, P>(XF, XB, li, lg, acc); break;
-      default: calib_products<3, IS_Q, P>(XF, XB, li, lg, acc); break;
+  // The two roles run separate loops with one barrier per stage each (the same count);
+  // stage s sits in buffer s & 1. Loads past the last stage repeat the last one (never
+  // multiplied), so every iteration issues the same loads.
+  if (loader) {
+    if (nst > 0) {
+      load_stage(r0);
+      store_stage(r0, sh.stage[0]);
+      load_stage(r0 + min((int64_t)1, nst - 1) * P);
     }
-    // fp32 runs of at most 128 query positions (rounded products) or 256 key positions
-    staged += P;
-    if (staged == (IS_Q ? CAL_FOLD_Q : CAL_FOLD_K)) { fold(); staged = 0; }
+    __syncthreads();
+    for (int64_t st = 0; st < nst; ++st) {
+      store_stage(r0 + min(st + 1, nst - 1) * P, sh.stage[(st + 1) & 1]);
+      load_stage(r0 + min(st + 2, nst - 1) * P);
+      __syncthreads();
+    }
+  } else {
+    f32x4_t acc[CAL_TPW];
+    double sum[CAL_TPW][4];
+#pragma unroll
+    for (int u = 0; u < CAL_TPW; ++u) {
+      acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sum[u][v] = 0.0;
+    }
+    auto fold = [&]() {
+#pragma unroll
+      for (int u = 0; u < CAL_TPW; ++u) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum[u][v] += (double)acc[u][v];
+        acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    __syncthreads();
+    int staged = 0;                             // positions in the current fp32 run
+    for (int64_t st = 0; st < nst; ++st) {
+      const float* XF = sh.stage[st & 1];
+      const uint16_t* XB = reinterpret_cast<const uint16_t*>(XF);
+      switch (wave) {
+        case 0: calib_products<0, IS_Q, P>(XF, XB, li, lg, acc); break;
+        case 1: calib_products<1, IS_Q, P>(XF, XB, li, lg, acc); break;
+        case 2: calib_products<2, IS_Q, P>(XF, XB, li, lg, acc); break;
+        default: calib_products<3, IS_Q, P>(XF, XB, li, lg, acc); break;
+      }
+      // fp32 runs of at most 128 query positions (rounded products) or 256 key positions
+      staged += P;
+      if (staged == FOLD) { fold(); staged = 0; }
+      __syncthreads();
+    }
+    fold();
+    // the wave's tiles' fp64 sums, each element written by the lane that owns it
+    auto write = [&](auto wt) {
+      using WT = decltype(wt);
+#pragma unroll
+      for (int u = 0; u < CAL_TPW; ++u) {
+        double* o = out + tile_index(WT::blk[WT::ta[u]], WT::blk[WT::tb[u]]) * 256 + (4 * lg) * 16 + li;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v * 16] = sum[u][v];
+      }
+    };
+    switch (wave) {
+      case 0: write(WaveTiles<0>{}); break;
+      case 1: write(WaveTiles<1>{}); break;
+      case 2: write(WaveTiles<2>{}); break;
+      default: write(WaveTiles<3>{}); break;
+    }
   }
-  fold();
-  __syncthreads();
-  for (int i = tid; i < CAL_TILES * 256; i += CAL_THREADS) out[i] = sh.acc[i];
 }
 
 template <int G>
@@ -371,7 +404,7 @@ hipError_t launch_calib(const sjsa_shape& s, const uint16_t* q, const uint16_t* 
   const int64_t rows = (int64_t)s.batch * T;
   int nwg_q, nwg_k;
   calib_groups(s, rows, &nwg_q, &nwg_k);
-  const int64_t chunk_q = ((rows + nwg_q - 1) / nwg_q + CAL_PQ - 1) / CAL_PQ * CAL_PQ;
+  const int64_t chunk_q = ((rows + nwg_q - 1) / nwg_q + 127) / 128 * 128;   // whole query stages
   const int64_t chunk_k = ((rows + nwg_k - 1) / nwg_k + CAL_PK - 1) / CAL_PK * CAL_PK;
   double* part = reinterpret_cast<double*>(ws);
   const dim3 grid((unsigned)(nwg_q + nwg_k), (unsigned)s.n_kv_heads);
