@@ -53,6 +53,18 @@ def test_workspace_size_and_layout():
     assert L.sjsa_decode_workspace_size(None, 16) == 0
 
 
+@pytest.mark.parametrize("rank,cap", [(16, 1000), (32, 131072), (64, 150001)])
+def test_workspace_layout_does_not_depend_on_the_cache_format(rank, cap):
+    # stage calls that do not name the projected cache's format (attend) share the
+    # workspace of those that do: the FP8 flag changes neither the size nor an offset
+    L = sj.lib()
+    a = _shape(rank=rank, capacity=cap)
+    b = _shape(rank=rank, capacity=cap, flags=4)      # SJSA_FLAG_KPROJ_FP8
+    for k in (256, 4096):
+        assert sj.workspace_size(a, k) == sj.workspace_size(b, k) > 0
+    assert L.sjsa_workspace_scores_offset(ctypes.byref(a)) == L.sjsa_workspace_scores_offset(ctypes.byref(b))
+
+
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation
 
 

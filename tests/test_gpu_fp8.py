@@ -116,6 +116,16 @@ def test_fp8_step_ragged(r, G):
         _check_step(wl, kp, k, tag=f"fp8 ragged r{r} G{G} k{k}", as_float8=(k == 1))
 
 
+def test_fp8_sequence_past_one_gather_chunk():
+    # 150,001 rows: more 4096-row scan tiles per unit than the selection gathers in one
+    # round trip (32), so its second chunk runs
+    say("fp8 step: sequences past one selection gather chunk")
+    seq = [150001, 140000]
+    wl = workloads.gaussian(2, 1, 4, 128, 32, 150001, 1024, seed=333, device="cuda", seq_len=seq, capacity=150001)
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy(), "fp8")
+    _check_step(wl, kp, 1024, tag="fp8 two gather chunks")
+
+
 def test_fp8_step_llama8b_layer():
     say("fp8 step llama8b-shaped layer n=32768 k=2048")
     wl = workloads.llama8b_layer(device="cuda")

@@ -62,6 +62,19 @@ def test_ragged_batches(r, G):
         _run_and_check(wl, kp, k, tag=f"ragged r{r} G{G} k{k}")
 
 
+@pytest.mark.parametrize("r", [32, 64])
+def test_sequence_past_one_gather_chunk(r):
+    # 150,001 rows: more scan tiles per unit than the selection gathers in one round trip
+    # (64 tiles of 2048 rows at r = 32, 128 of 1024 at r = 64), so its later chunks run;
+    # the second sequence ends short of the capacity, inside the second chunk
+    say(f"step: sequences past one selection gather chunk r={r}")
+    seq = [150001, 140000]
+    wl = workloads.gaussian(2, 1, 4, 128, r, 150001, 1024, seed=77 + r, device="cuda", seq_len=seq,
+                            capacity=150001)
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    _run_and_check(wl, kp, 1024, tag=f"two gather chunks r{r}")
+
+
 def test_budget_at_least_context_is_dense():
     say("step k >= n")
     wl = workloads.gaussian(2, 2, 4, 128, 32, 900, 1000, seed=21, device="cuda", seq_len=[900, 333])
