@@ -352,29 +352,33 @@ __global__ __launch_bounds__(CAL_THREADS) void calib_mfma_kernel(
     calib_body<G, false>(sh, q, k, n_kv_heads, T, rows, (int)blockIdx.x - nwg_q, chunk_k, out);
 }
 
-// grid (HEAD_DIM * HEAD_DIM / 256, H_kv, 2): acc[h][i][j] += the workgroups' tile sums
-// in workgroup order; element (i, j) of the lower triangle takes (j, i) of the upper.
+// grid (CAL_TILES, H_kv, 2), 256 threads: thread e of workgroup (t, h, mat) sums tile
+// t's element e over the workgroups' partial tiles, in workgroup order (deterministic),
+// and adds the sum to the caller's accumulator at (i, j) and, off the diagonal tiles,
+// at (j, i) as well (the lower triangle mirrors the upper one).
 __global__ __launch_bounds__(256) void calib_reduce_kernel(const double* __restrict__ part, int nwg_q, int nwg_k,
                                                            double* __restrict__ SQ, double* __restrict__ SK) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int h = blockIdx.y, mat = blockIdx.z;
-  int i = e / HEAD_DIM, j = e % HEAD_DIM;
-  if (i / 16 > j / 16) { const int x = i; i = j; j = x; }
-  const int t = tile_index(i / 16, j / 16);
+  const int t = blockIdx.x, h = blockIdx.y, mat = blockIdx.z, e = threadIdx.x;
+  int bi = 0, r = t;
+  while (r >= 8 - bi) { r -= 8 - bi; ++bi; }
+  const int bj = bi + r;
+  const int i = 16 * bi + e / 16, j = 16 * bj + e % 16;
   const int nwg = nwg_q + nwg_k;
   const int w0 = mat == 0 ? 0 : nwg_q, w1 = mat == 0 ? nwg_q : nwg;
-  const double* p = part + ((size_t)h * nwg) * CAL_TILES * 256 + (size_t)t * 256 + (i % 16) * 16 + (j % 16);
-  constexpr int RU = 8;                          // loads in flight; the sum stays in workgroup order
+  const double* p = part + ((size_t)h * nwg) * CAL_TILES * 256 + (size_t)t * 256 + e;
+  constexpr int RU = 32;                         // partials loaded at once
   double s = 0.0;
   for (int w = w0; w < w1; w += RU) {
     double x[RU];
 #pragma unroll
-    for (int u = 0; u < RU; ++u) x[u] = w + u < w1 ? p[(size_t)(w + u) * CAL_TILES * 256] : 0.0;
+    for (int u = 0; u < RU; ++u) x[u] = p[(size_t)min(w + u, w1 - 1) * CAL_TILES * 256];
 #pragma unroll
-    for (int u = 0; u < RU; ++u) s += x[u];
+    for (int u = 0; u < RU; ++u)
+      if (w + u < w1) s += x[u];
   }
-  double* dst = (mat == 0 ? SQ : SK) + (size_t)h * HEAD_DIM * HEAD_DIM + e;
-  *dst += s;
+  double* dst = (mat == 0 ? SQ : SK) + (size_t)h * HEAD_DIM * HEAD_DIM;
+  dst[i * HEAD_DIM + j] += s;
+  if (bi != bj) dst[j * HEAD_DIM + i] += s;
 }
 
 }  // namespace
@@ -416,7 +420,7 @@ hipError_t launch_calib(const sjsa_shape& s, const uint16_t* q, const uint16_t* 
 #undef SJSA_CAL
     default: return hipErrorInvalidValue;
   }
-  calib_reduce_kernel<<<dim3(HEAD_DIM * HEAD_DIM / 256, (unsigned)s.n_kv_heads, 2), dim3(256), 0, st>>>(
+  calib_reduce_kernel<<<dim3(CAL_TILES, (unsigned)s.n_kv_heads, 2), dim3(256), 0, st>>>(
       part, nwg_q, nwg_k, SQ, SK);
   return hipGetLastError();
 }
