@@ -579,7 +579,7 @@ def main():
                                                               True)}))
         return
     if only == "calib":
-        print(json.dumps({"calib_variant": calib_variant(sj, max(2, steps // 20), 1)}))
+        print(json.dumps({"calib_variant": calib_variant(sj, max(5, steps // 20), 2)}))
         return
     t_setup = time.time()
     wl = workloads.long_batched(device=dev, n_q_sets=8)
@@ -773,7 +773,7 @@ def main():
         line["block_variant"] = block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, False, cpu=cpu)
         line["block_int4_variant"] = block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, True, cpu=cpu)
     if not only and not args.no_calib_variant:
-        line["calib_variant"] = calib_variant(sj, max(2, steps // 20), 1, cpu=cpu)
+        line["calib_variant"] = calib_variant(sj, max(5, steps // 20), 2, cpu=cpu)
     if not only and not args.no_fp8_variant:
         line["kproj_fp8_variant"] = fp8_variant(sj, wl, K, V, M, seq_len, q_sets, k_new, v_new, pos_new, steps,
                                                 warmup, step_bytes, MI355X_HBM_PEAK_GBS, cpu=cpu)
