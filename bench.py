@@ -639,6 +639,21 @@ def main():
         return {nm: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1000.0, 2)
                 for j, nm in enumerate(names)}
 
+    def padded_slot(steps_, warmup_):
+        # sequence 0's query heads all zero (a padded batch slot): every score of its
+        # units is 0, every row a candidate, and those units take the exact path
+        qz = q_sets.clone()
+        qz[:, 0].zero_()
+        wsz = sj.alloc_workspace(shape, k, dev)
+        step_z = make_step(shape, wsz, K, V, Kp, qz)
+        us = back_to_back_us(step_z, steps_, warmup_)
+        res = {"us_per_step": round(us, 2), "stage_us": stage_us(step_z)}
+        step_z(0)
+        torch.cuda.synchronize()
+        res["first_positions"] = bool(torch.equal(idx[0].cpu(), torch.arange(k, dtype=torch.int32).expand(Hkv, k)))
+        del wsz, qz
+        return res
+
     step = make_step(shape, ws, K, V, Kp, q_sets)
     if only == "exact":
         # every unit on the exact path (no scan workgroup takes what its prep publishes)
@@ -646,6 +661,7 @@ def main():
         step_fb = make_step(shape_fb, sj.alloc_workspace(shape_fb, k, dev), K, V, Kp, q_sets)
         fb = back_to_back_us(step_fb, steps, warmup)
         print(json.dumps({"fallback_variant": {"us_per_step": round(fb, 2), "stage_us": stage_us(step_fb)}}))
+        print(json.dumps({"padded_slot_variant": padded_slot(steps, warmup)}))
         return
     # throughput: K whole steps back to back, bracketed by one pair of events (an event
     # between two kernels delays the second by several microseconds, so the steps
@@ -732,12 +748,19 @@ def main():
         same = bool(torch.equal(idx, ref_idx) and torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
         line["fallback_variant"] = {
             "what": "the headline step with sjsa_shape.fused_wait_us < 0: no scan workgroup takes what its prep "
-                    "publishes, so every unit takes the exact path (scores recomputed by two workgroups per unit, "
+                    "publishes, so every unit takes the exact path (scores recomputed by four workgroups per unit, "
                     "dense radix selection)",
             "us_per_step": round(fb, 2), "ratio_to_headline": round(fb / us_step, 3), "stage_us": fb_st,
             "results_equal_headline": same}
         del ws_fb
         say(f"fallback: {fb:.1f} us/step ({fb / us_step:.2f}x), stages {fb_st}, same results {same}")
+        pz = padded_slot(max(4, steps // 4), max(2, warmup // 4))
+        line["padded_slot_variant"] = {
+            "what": "the headline step with every query head of sequence 0 zero (a padded batch slot): its 8 units "
+                    "score every row 0, so every row is a candidate and they take the exact path; the result is "
+                    "their first k positions",
+            **pz, "ratio_to_headline": round(pz["us_per_step"] / us_step, 3)}
+        say(f"padded slot: {pz['us_per_step']:.1f} us/step ({pz['us_per_step'] / us_step:.2f}x)")
         # an input whose top-k the threshold sampler cannot see
         wb = workloads.long_batched_blind_spot(device=dev)
         Kb_, Vb_ = wb.K, wb.V

@@ -136,7 +136,9 @@ size_t sjsa_decode_workspace_size(const sjsa_shape* shape, int32_t k);
  * which is always so for k > 16384 and n_b > k; fewer than k; or a scan
  * workgroup that gave up waiting, see fused_wait_us) has its scores recomputed
  * and selected exactly: the same result, at about 1.4 times the step's time when
- * every unit of the 128K-token batch-16 step takes that path.
+ * every unit of the 128K-token batch-16 step takes that path, and 1.25 times when
+ * the 8 units of one sequence do (a padded slot whose queries are zero, say: all
+ * its scores tie, every row is a candidate).
  * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _K, _WORKSPACE, _ALIGN, _HIP.
  */
 int sjsa_decode_step(const sjsa_shape* shape, const void* q, const void* K, const void* V,
@@ -171,8 +173,8 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
  * on, held until the process ends; the call itself allocates and frees nothing.
  * A shape whose workspace (sjsa_decode_workspace_size(shape, k)) is larger is
  * rejected with SJSA_ERR_SCRATCH before anything is enqueued (with 131072 token
- * slots, r = 32 and k = 4096 that allows up to 60 (sequence, KV head) pairs; one
- * sequence of 32768 tokens with 8 KV heads and k = 2048 needs 2.8 MiB).
+ * slots, r = 32 and k = 4096 that allows up to 58 (sequence, KV head) pairs; one
+ * sequence of 32768 tokens with 8 KV heads and k = 2048 needs 3.0 MiB).
  * Every call on one GPU uses that GPU's one array, which keeps the previous call's
  * contents (the step, like a fresh workspace, needs nothing cleared): calls that
  * overlap on one GPU (on different streams, or from host threads without ordering)

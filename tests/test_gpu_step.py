@@ -200,6 +200,23 @@ def test_candidate_underflow_falls_back_exactly():
     _ties_check(wl, kp, k, "underflow")
 
 
+def test_constant_unit_with_spread_high_rows_falls_back_exactly():
+    # 1000 high rows spread over a unit whose other rows are all equal: every row is
+    # a candidate, and in the exact path the crowded boundary bin holds one key value
+    say("step constant unit with spread high rows -> exact fallback")
+    n, k = 40000, 1500
+    wl = workloads.gaussian(1, 1, 4, 128, 16, n, k, seed=28, device="cuda")
+    M = wl.M.cpu().numpy()
+    q = bits(wl.q)
+    qhat = jssa.project_query(jssa.mean_query(q[0, 0:4]), M[0]).astype(np.float64)
+    low = jssa.project_keys(bits(wl.K[0, 0, :1].contiguous()), M[0])[0]
+    from oracle.numerics import round_to_bf16
+    high = round_to_bf16(np.sign(qhat) * 4.0)
+    kp = np.tile(low, (1, 1, n, 1)).astype(np.uint16)
+    kp[0, 0, np.random.default_rng(28).choice(n, 1000, replace=False)] = high
+    _ties_check(wl, kp, k, "constant unit, high rows")
+
+
 def test_scan_stage_overflow_falls_back_exactly():
     # the first 4096 rows (one scan tile) all score high, the rest low: every wave of
     # that tile finds 1024 candidates, more than it can stage; the total (4096) would
@@ -295,7 +312,7 @@ def test_units_on_different_paths_in_one_launch():
     # one launch where unit (0,0) has every row identical (its 20001 candidates overflow
     # the lists), (1,0) has the first row of every sampled pair scoring high (1024
     # candidates, fewer than k) and (0,1), (1,1) are ordinary: the exact-path units are
-    # recomputed by two workgroups each (over lengths that split unevenly), the others
+    # recomputed by four workgroups each (over lengths that split unevenly), the others
     # select from their candidates
     say("step units on different paths")
     n, k = 20001, 1500

@@ -51,6 +51,35 @@ def test_all_equal_fallback_path():
     _run(s, [50000], 3000)
 
 
+def test_constant_row_takes_the_first_positions():
+    # more equal keys than the lists hold: the crowded-bin check finds one key value
+    say("topk constant row (crowded bin, one key)")
+    s = np.full((2, 2, 50000), -0.75, dtype=np.float32)
+    _run(s, [50000, 49999], 3000)
+    _run(s, [50000, 20000], 16000)
+
+
+def test_crowded_bin_of_one_key_below_other_keys():
+    # 300 keys above a crowded bin whose keys are all equal: the threshold is that key
+    say("topk crowded bin of one key, 300 keys above")
+    s = np.full((1, 2, 40000), 1.0, dtype=np.float32)
+    pos = _rng(6).choice(40000, 300, replace=False)
+    s[0, 0, pos] = 3.0
+    s[0, 1, pos] = _rng(7).uniform(2.0, 4.0, 300).astype(np.float32)
+    _run(s, [40000], 1000)
+
+
+def test_crowded_bin_of_distinct_keys():
+    # 50000 keys in [1, 1.125): one first-digit bin (sign, exponent and three mantissa
+    # bits), distinct low bits, with exact repeats: the two radix rounds resolve it
+    say("topk crowded bin of distinct keys")
+    rng = _rng(8)
+    s = (1.0 + rng.integers(0, 1 << 17, size=(2, 2, 50000)) * np.float32(2.0 ** -20)).astype(np.float32)
+    s[:, 1, ::2] = s[:, 1, 1::2]
+    _run(s, [50000, 50000], 3000)
+    _run(s, [50000, 45001], 20000)
+
+
 def test_large_budget_fallback_path():
     say("topk large k (fallback)")
     s = _rng(2).standard_normal((1, 2, 100000)).astype(np.float32)

@@ -59,6 +59,7 @@ struct SelShared {
   uint32_t scan[SEL_WAVES];
   uint32_t scan2[SEL_WAVES];
   int32_t misc[8];
+  uint32_t spare[64];                // hist_add's sink: one word per lane of a wave
 };
 
 // Block-wide inclusive scan of one u32 per thread; returns the inclusive value and
@@ -116,6 +117,24 @@ __device__ __forceinline__ f32x4 load4(const float* row, int64_t pos, int64_t la
   return *reinterpret_cast<const f32x4*>(row + min(pos, last4));
 }
 
+// Counts each lane with `on` into hist[bin] (LDS), one atomic per lane, with no
+// branch (a branch in a loop that keeps loads in flight makes the compiler wait on
+// them early). The counted lanes of the wave that share the bin of its first active
+// lane add their number through the first of them; the other lanes add 0 to their
+// own word of `spare`. Without this a run of equal keys (a constant score row,
+// duplicated cache rows) sends every lane of every wave to one LDS address, where
+// the atomics are done one at a time.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t* spare, uint32_t bin, bool on) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(bin);
+  const bool in_same = on && bin == b0;
+  const uint64_t same = __ballot(in_same);
+  const uint32_t lead = same != 0 ? (uint32_t)__builtin_ctzll(same) : 64u;
+  const bool counts = on && (!in_same || lane == lead);
+  const uint32_t v = !counts ? 0u : (in_same ? (uint32_t)__popcll(same) : 1u);
+  atomicAdd(counts ? &hist[bin] : &spare[lane], v);
+}
+
 // Ordered compaction helper: ranks of the flagged elements of one sub-chunk (each
 // thread holds NE consecutive positions; lanes, then waves, are in position order).
 // Returns this thread's first output slot relative to the sub-chunk start and the
@@ -157,7 +176,7 @@ __device__ uint32_t lds_threshold(const uint32_t* keys, int cnt, uint32_t prefix
     __syncthreads();
     for (int i = tid; i < cnt; i += SEL_THREADS) {
       const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 1023u], 1u);
+      hist_add(sh.hist, sh.spare, (key >> shift) & 1023u, (key & mask) == prefix);
     }
     __syncthreads();
     find_bucket(sh.hist, 1024, need, sh);
@@ -417,7 +436,7 @@ __device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk
       for (int u = 0; u < HU; ++u) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
-          if (c0 + (int64_t)u * SUB + e < n) atomicAdd(&sh.hist[score_key(v[u][e]) >> HIST_SHIFT], 1u);
+          hist_add(sh.hist, sh.spare, score_key(v[u][e]) >> HIST_SHIFT, c0 + (int64_t)u * SUB + e < n);
       }
     }
     __syncthreads();
@@ -533,18 +552,65 @@ __device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk
   }
 
   // the lists would not fit: resolve the lower 20 bits with passes over the row
+  // (HU float4 loads in flight per thread, as in the first digit's pass)
+  constexpr int HU = 8;
   uint32_t prefix = b1 << HIST_SHIFT;
   uint32_t mask = 0xfff00000u;
-  for (int round = 0; round < 2; ++round) {
+  int rounds = 2;
+  if (cntC > C_CAP) {
+    // a crowded boundary bin: first its least and greatest keys. When they are equal
+    // (a constant row, for one) that key is the threshold; when the bin is also the
+    // whole row, every score ties and the selection is the first kk positions.
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (int64_t c0 = (int64_t)tid * EPT; c0 < n; c0 += (int64_t)SUB * HU) {
+      f32x4 v[HU];
+#pragma unroll
+      for (int u = 0; u < HU; ++u) v[u] = load4(row, c0 + (int64_t)u * SUB, last4);
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          const uint32_t key = score_key(v[u][e]);
+          const bool in = c0 + (int64_t)u * SUB + e < n && (key & mask) == prefix;
+          kmin = in ? min(kmin, key) : kmin;
+          kmax = in ? max(kmax, key) : kmax;
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if ((tid & 63) == 0) { sh.scan[tid >> 6] = kmin; sh.scan2[tid >> 6] = kmax; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < SEL_WAVES; ++w) { kmin = min(kmin, sh.scan[w]); kmax = max(kmax, sh.scan2[w]); }
+    __syncthreads();
+    if (kmin == kmax) {
+      if (cntA == 0 && (int64_t)cntC == n) {
+        for (int i = tid; i < kk; i += SEL_THREADS) out[i] = i;
+        return;
+      }
+      prefix = kmin;
+      rounds = 0;
+    }
+  }
+  for (int round = 0; round < rounds; ++round) {
     const int shift = round == 0 ? 10 : 0;
     for (int i = tid; i < 1024; i += SEL_THREADS) sh.hist[i] = 0u;
     __syncthreads();
-    for (int64_t c = (int64_t)tid * EPT; c < n; c += SUB) {
-      const f32x4 v = load4(row, c, last4);
+    for (int64_t c0 = (int64_t)tid * EPT; c0 < n; c0 += (int64_t)SUB * HU) {
+      f32x4 v[HU];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const uint32_t key = score_key(v[e]);
-        if (c + e < n && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 1023u], 1u);
+      for (int u = 0; u < HU; ++u) v[u] = load4(row, c0 + (int64_t)u * SUB, last4);
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          const uint32_t key = score_key(v[u][e]);
+          hist_add(sh.hist, sh.spare, (key >> shift) & 1023u,
+                   c0 + (int64_t)u * SUB + e < n && (key & mask) == prefix);
+        }
       }
     }
     __syncthreads();
@@ -556,9 +622,15 @@ __device__ __forceinline__ void select_dense(const float* row, int64_t n, int kk
   const uint32_t T = prefix;
   const uint32_t needT = need;
   uint32_t baseS = 0, baseEq = 0;
+  // ordered selection, one sub-chunk per step; each step first issues the next
+  // sub-chunk's load, which is in flight while this one is ranked (a deeper queue
+  // gains nothing: the loop's global stores make the compiler wait on every load at
+  // its head)
+  f32x4 next = load4(row, (int64_t)tid * EPT, last4);
   for (int64_t c0 = 0; c0 < n; c0 += SUB) {
     const int64_t p0 = c0 + tid * EPT;
-    const f32x4 v = load4(row, p0, last4);
+    const f32x4 v = next;
+    next = load4(row, p0 + SUB, last4);
     bool eq[EPT], sel[EPT];
     uint32_t key[EPT];
 #pragma unroll
@@ -636,10 +708,8 @@ __device__ void recompute_scores(const unsigned char* kproj_unit, const float* q
         for (int i = 0; i < LPR; ++i) d[i] = dot_chunk<KB>(qh, w[u][i]);
         const float sc = transpose_reduce<LPR>(d, p);
         const int64_t j = g0 + u * 64 + p * RPL + rs;
-        if (j < s1) {
-          stage[j - s0] = sc;
-          atomicAdd(&sh.hist[score_key(sc) >> HIST_SHIFT], 1u);
-        }
+        if (j < s1) stage[j - s0] = sc;
+        hist_add(sh.hist, sh.spare, score_key(sc) >> HIST_SHIFT, j < s1);
       }
     }
     __syncthreads();

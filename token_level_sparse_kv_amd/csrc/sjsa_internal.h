@@ -55,7 +55,7 @@ constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
 // Workgroups of the selection launch per unit: the first selects from the candidates;
 // when the unit takes the exact path (scores recomputed from the projected cache), all
 // of them recompute one part of its rows and the last to finish selects.
-constexpr int EXACT_WGS = 2;
+constexpr int EXACT_WGS = 4;
 
 struct Layout {
   int64_t units = 0;          // B * H_kv
