@@ -136,7 +136,7 @@ size_t sjsa_decode_workspace_size(const sjsa_shape* shape, int32_t k);
  * which is always so for k > 16384 and n_b > k; fewer than k; or a scan
  * workgroup that gave up waiting, see fused_wait_us) has its scores recomputed
  * and selected exactly: the same result, at about 1.4 times the step's time when
- * every unit of the 128K-token batch-16 step takes that path, and 1.25 times when
+ * every unit of the 128K-token batch-16 step takes that path, and 1.25-1.3 times when
  * the 8 units of one sequence do (a padded slot whose queries are zero, say: all
  * its scores tie, every row is a candidate).
  * Errors: SJSA_ERR_NULL, _DIMS, _UNSUPPORTED, _K, _WORKSPACE, _ALIGN, _HIP.
