@@ -75,6 +75,18 @@ def test_sequence_past_one_gather_chunk(r):
     _run_and_check(wl, kp, 1024, tag=f"two gather chunks r{r}")
 
 
+@pytest.mark.parametrize("r,k", [(32, 12000), (32, 20000), (16, 30000)])
+def test_budgets_near_and_above_the_candidate_lists(r, k):
+    # k = 12000: the candidates (about 1.7 k) exceed the 16384 the selection keeps, so
+    # the exact path runs; k > 16384 always takes it. The attention splits the budget
+    # over many chunks; the second sequence is shorter than k
+    say(f"step large budget r={r} k={k}")
+    seq = [60000, 25001]
+    wl = workloads.gaussian(2, 2, 4, 128, r, 60000, k, seed=90 + r + k, device="cuda", seq_len=seq)
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    _run_and_check(wl, kp, k, tag=f"large budget r{r} k{k}")
+
+
 def test_budget_at_least_context_is_dense():
     say("step k >= n")
     wl = workloads.gaussian(2, 2, 4, 128, 32, 900, 1000, seed=21, device="cuda", seq_len=[900, 333])
