@@ -741,7 +741,7 @@ def main():
         shape_fb = sj.make_shape(B, Hkv, G, d, r, n, fused_wait_us=-1)
         ws_fb = sj.alloc_workspace(shape_fb, k, dev)
         step_fb = make_step(shape_fb, ws_fb, K, V, Kp, q_sets)
-        fb = back_to_back_us(step_fb, max(4, steps // 4), max(2, warmup // 4))
+        fb = back_to_back_us(step_fb, steps, warmup)
         fb_st = {kk: v for kk, v in stage_us(step_fb).items()}
         step_fb(0)
         torch.cuda.synchronize()
@@ -754,7 +754,7 @@ def main():
             "results_equal_headline": same}
         del ws_fb
         say(f"fallback: {fb:.1f} us/step ({fb / us_step:.2f}x), stages {fb_st}, same results {same}")
-        pz = padded_slot(max(4, steps // 4), max(2, warmup // 4))
+        pz = padded_slot(steps, warmup)
         line["padded_slot_variant"] = {
             "what": "the headline step with every query head of sequence 0 zero (a padded batch slot): its 8 units "
                     "score every row 0, so every row is a candidate and they take the exact path; the result is "
@@ -767,7 +767,7 @@ def main():
         Kpb = kproj_cache(Kb_, Vb_, M)
         wsb = sj.alloc_workspace(shape, k, dev)
         step_b = make_step(shape, wsb, Kb_, Vb_, Kpb, q_sets)
-        bl = back_to_back_us(step_b, max(4, steps // 4), max(2, warmup // 4))
+        bl = back_to_back_us(step_b, steps, warmup)
         bl_st = stage_us(step_b)
         line["blind_spot_variant"] = {
             "workload": "the headline workload with the keys at positions p % 128 < 2 scaled by 1/16: the rows an "
