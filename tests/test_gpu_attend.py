@@ -109,3 +109,32 @@ def test_attend_interleaved_invalid_entries_and_growing_logits(G):
     out = sj.attend(wl.q, wl.K, wl.V, idx_t, wl.seq_len, out_f32=True)
     torch.cuda.synchronize()
     assert np.max(np.abs(out.cpu().numpy() - ref)) <= OUT_TOL_F32
+
+
+@pytest.mark.parametrize("G,k", [(4, 4096), (2, 20000)])
+def test_split_attention_on_an_uninitialised_workspace(G, k):
+    # the workspace needs no initialisation: one of random bytes, used by several calls
+    # in a row, gives the oracle's output every time (the splits' partials and their
+    # merge go through it), and the calls agree bit for bit
+    say(f"attend on a random workspace G={G} k={k}")
+    B, H, n = 2, 2, 30000
+    wl = workloads.gaussian(B, H, G, 128, 16, n, k, seed=G + k, device="cuda", seq_len=[n, 25001])
+    rng = np.random.default_rng(G + k)
+    idx = np.stack([np.stack([np.sort(rng.choice(n, size=k, replace=False)) for _ in range(H)])
+                    for _ in range(B)]).astype(np.int32)
+    idx_t = torch.from_numpy(idx).cuda()
+    shape = sj.make_shape(B, H, G, 128, 16, n)
+    ws = sj.alloc_workspace(shape, k)
+    ws.copy_(torch.from_numpy(rng.integers(0, 256, ws.numel(), dtype=np.uint8)).cuda())
+    q, K, V = bits(wl.q), bits(wl.K), bits(wl.V)
+    ref = _ref(q, K, V, idx, wl.seq_len.cpu().numpy(), G, jssa.default_sm_scale(128))
+    first = None
+    for call in range(3):
+        out = sj.attend(wl.q, wl.K, wl.V, idx_t, wl.seq_len, out_f32=True, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got - ref)) <= OUT_TOL_F32, call
+        if first is None:
+            first = out.clone()
+        else:
+            assert torch.equal(out, first), call
