@@ -49,7 +49,7 @@ def test_long_batched_full_size():
     q, K, V, P, M = bits(wl.q), bits(wl.K), bits(wl.V), bits(Kp), wl.M.cpu().numpy()
     _check_all_units("full size", out, idx, q, K, V, P, M, wl.capacity, wl.k)
     # every unit through the exact path (no scan workgroup takes what its prep
-    # publishes): the two-workgroup recompute and dense selection give the same result
+    # publishes): the four-workgroup recompute and dense selection give the same result
     say("full size: every unit on the exact path")
     shape = sj.make_shape(16, 8, 4, 128, 32, wl.capacity, fused_wait_us=-1)
     ws = sj.alloc_workspace(shape, wl.k)
