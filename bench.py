@@ -106,7 +106,7 @@ def host_info():
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
-    # a GPU machine grants this process a share of 16 host threads whatever the OS reports
+    # the oracle's thread pool: at most 16 threads, whatever the OS reports as available
     pool = max(1, min(16, avail))
     return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": avail, "pool_threads": pool}
 
@@ -552,8 +552,8 @@ def main():
 
     only = args.only
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this build measures the "
-              f"single-GPU path)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the step is measured on "
+              f"one GPU's share of the batch)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(1 << 30, 5)
