@@ -45,7 +45,7 @@ constexpr int C_CAP = 12288;
 constexpr int CAND_CAP = LDS_WORDS / 2;         // candidate path: ckey | cpos
 static_assert(A_CAP + 2 * C_CAP == LDS_WORDS, "dense lists fill the list storage");
 
-constexpr int HIST2_BINS = 2048;                // second histogram (candidate path, round 1)
+constexpr int HIST2_BINS = 2048;                // second histogram (candidate path, second radix digit)
 constexpr int HIST1_BITS = 12;                  // candidate path: first digit of the relative keys
 static_assert(1 << HIST1_BITS <= HIST_BINS && HIST1_BITS < CAND_KEY_BITS, "first digit fits sh.hist");
 
