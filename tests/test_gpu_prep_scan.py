@@ -206,6 +206,25 @@ def test_zero_wait_limit_falls_back_exactly():
     _oracle(wl, got, wl.q, seq, 700, False, "zero wait", [(0, 0), (2, 1), (3, 0)])
 
 
+@pytest.mark.parametrize("r,G,fp8", [(16, 1, False), (16, 2, True), (32, 4, True), (64, 8, False), (64, 4, True)])
+def test_every_unit_exact_equals_candidate_path(r, G, fp8):
+    # every rank and cache format of the exact path (scores recomputed by several
+    # workgroups per unit, dense selection) against the candidate path: the same
+    # index lists and outputs bit for bit, over ragged lengths and a budget past the
+    # dense selection's lists (k > 8192) for one of them
+    k = 9000 if r == 64 and not fp8 else 700
+    seq = [30000, 17, 12345, 4096 + 3]
+    tag = f"exact path r={r} G={G} fp8={fp8} k={k}"
+    say(tag)
+    wl = workloads.gaussian(4, 2, G, 128, r, 30000, k, seed=95 + r + G, capacity=30000, device="cuda", seq_len=seq)
+    Kp = _cache(wl, fp8)
+    seq_len = torch.tensor(seq, dtype=torch.int32, device="cuda")
+    ref = _step(wl, Kp, wl.q, seq_len, k, "fused")
+    got = _step(wl, Kp, wl.q, seq_len, k, "fused", wait_us=-1)
+    _same(ref, got, tag)
+    _oracle(wl, got, wl.q, seq, k, fp8, tag, [(0, 1), (2, 0), (3, 1)])
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_fused_edge_lengths(fp8):
     # capacity not a multiple of the 4096-row tile, an empty sequence, a sequence no
