@@ -118,6 +118,21 @@ def test_zero_query_all_scores_tie():
     assert np.array_equal(ix[0, 0], np.arange(100))       # all scores are +-0: lowest positions
 
 
+def test_zero_query_sequence_in_a_batch_takes_the_first_positions():
+    # a padded slot: sequence 1's query heads are zero, so every score of its units is
+    # +-0 (one key), every row is a candidate and those units take the exact path,
+    # whose crowded first-digit bin holds the whole row: the first k positions; the
+    # other sequence is an ordinary one in the same launch
+    say("step zero-query sequence in a batch")
+    n, k = 40000, 1500
+    wl = workloads.gaussian(2, 2, 4, 128, 32, n, k, seed=29, device="cuda")
+    wl.q[1].zero_()
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    o, ix, _ = _run_and_check(wl, kp, k, tag="zero-query slot")
+    for h in range(2):
+        assert np.array_equal(ix[1, h], np.arange(k))
+
+
 def test_stage_calls_equal_fused_step_and_are_deterministic():
     say("stages vs fused step, determinism")
     wl = workloads.gaussian(3, 2, 4, 128, 32, 20000, 700, seed=24, device="cuda", seq_len=[20000, 15000, 9])
