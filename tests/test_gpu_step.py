@@ -96,6 +96,17 @@ def test_budget_at_least_context_is_dense():
     assert np.array_equal(ix[1, 1, :333], np.arange(333)) and np.all(ix[1, 1, 333:] == -1)
 
 
+@pytest.mark.parametrize("k", [4999, 4998])
+def test_budget_just_below_the_context(k):
+    # all but one or two positions selected: the candidate lists cannot hold them, so the
+    # exact path selects; the second sequence is shorter than k (every position taken)
+    say(f"step k = n - {5000 - k}")
+    wl = workloads.gaussian(2, 2, 4, 128, 32, 5000, k, seed=31 + k, device="cuda", seq_len=[5000, 4000])
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    o, ix, _ = _run_and_check(wl, kp, k, tag=f"k = {k}")
+    assert np.array_equal(ix[1, 0, :4000], np.arange(4000)) and np.all(ix[1, 0, 4000:] == -1)
+
+
 def test_duplicated_kproj_rows_tie_to_lower_position():
     say("step exact ties from duplicated rows")
     wl = workloads.gaussian(1, 1, 4, 128, 32, 8192, 512, seed=22, device="cuda")
