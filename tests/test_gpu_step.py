@@ -144,6 +144,27 @@ def test_zero_query_sequence_in_a_batch_takes_the_first_positions():
         assert np.array_equal(ix[1, h], np.arange(k))
 
 
+def test_nan_query_sequence_selects_its_first_positions():
+    # one sequence's queries are NaN: every score is NaN (ranked last, all equal), so its
+    # units select their first k positions through the exact path; the other sequence
+    # in the launch is unaffected
+    say("step NaN-query sequence")
+    n, k = 20000, 700
+    wl = workloads.gaussian(2, 2, 4, 128, 32, n, k, seed=33, device="cuda")
+    wl.q[1] = float("nan")
+    kp = kproj_oracle(bits(wl.K), wl.M.cpu().numpy())
+    Kp = from_bits(kp).cuda()
+    out, idx = sj.decode_step(wl.q, wl.K, wl.V, Kp, wl.M, wl.seq_len, k, out_f32=True)
+    torch.cuda.synchronize()
+    ix, o = idx.cpu().numpy(), out.cpu().numpy()
+    for h in range(2):
+        assert np.array_equal(ix[1, h], np.arange(k))
+    q, K, V, M = bits(wl.q), bits(wl.K), bits(wl.V), wl.M.cpu().numpy()
+    for h in range(2):
+        check_unit(o[0, 4 * h:4 * h + 4], ix[0, h], q, K, V, kp, M, 0, h, 4, n, k, jssa.default_sm_scale(128),
+                   OUT_TOL_F32, "NaN-query batch")
+
+
 def test_stage_calls_equal_fused_step_and_are_deterministic():
     say("stages vs fused step, determinism")
     wl = workloads.gaussian(3, 2, 4, 128, 32, 20000, 700, seed=24, device="cuda", seq_len=[20000, 15000, 9])
