@@ -188,6 +188,61 @@ def test_graph_replay_with_new_queries():
         assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), f"replay {rep}: out"
 
 
+@pytest.mark.parametrize("fp8,wait_us", [(False, 0), (False, -1), (True, 0), (True, -1)])
+def test_graph_replay_of_the_appending_stage_calls(fp8, wait_us):
+    # the appending step's stage calls (append + prep + scan in one launch, select,
+    # attend + merge) captured once and replayed with new queries and new tokens copied
+    # into the captured inputs. Each replay gives the caches, index lists and outputs of
+    # the same calls made eagerly on a copy of the caches. This holds on the candidate
+    # path and with every unit on the exact path (wait_us < 0), whose arrival counts
+    # each replay's prep clears again.
+    tag = f"prep_scan: graph replays of the appending step (fp8 {fp8}, wait {wait_us})"
+    say(tag)
+    k = 400
+    wl = workloads.gaussian(2, 2, 4, 128, 32, 9000, k, seed=87, capacity=9216, device="cuda",
+                            seq_len=[9000, 7001])
+    Kp = _cache(wl, fp8)
+    seq_len = wl.seq_len
+    pos = (seq_len - 1).to(torch.int32)
+    shape = sj.make_shape(2, 2, 4, 128, 32, 9216, kproj_fp8=fp8, fused_wait_us=wait_us)
+    ws = sj.alloc_workspace(shape, k)
+    K, V, P = wl.K.clone(), wl.V.clone(), Kp.clone()
+    q_in = wl.q.clone()
+    kn_in, vn_in = workloads.new_token(wl, seed=88)
+    idx = torch.empty(2, 2, k, dtype=torch.int32, device="cuda")
+    out = torch.empty(wl.q.shape, dtype=torch.float32, device="cuda")
+
+    def calls():
+        sj.prep_scan(shape, q_in, wl.M, P, seq_len, k, ws, k_new=kn_in, v_new=vn_in, pos=pos, K=K, V=V)
+        sj.select(shape, P, seq_len, k, ws, idx=idx)
+        sj.attend(q_in, K, V, idx, seq_len, out=out, workspace=ws, out_f32=True, rank=32)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm-up outside the capture
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(89)
+    for rep in range(4):
+        q = torch.randn(wl.q.shape, generator=g, device="cuda").to(torch.bfloat16)
+        kn = torch.randn(kn_in.shape, generator=g, device="cuda").to(torch.bfloat16)
+        vn = torch.randn(vn_in.shape, generator=g, device="cuda").to(torch.bfloat16)
+        q_in.copy_(q)
+        kn_in.copy_(kn)
+        vn_in.copy_(vn)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = _step(wl, Kp, q, seq_len, k, "fused", new=(kn, vn, pos), wait_us=wait_us)
+        _same((K, V, P, idx, out), ref, f"{tag}, replay {rep}")
+
+
 def test_zero_wait_limit_falls_back_exactly():
     # scan workgroups that do not wait (a negative limit in the shape) mark their tiles
     # unusable; the selection then recomputes those units exactly, so the results do
