@@ -281,6 +281,25 @@ def test_every_unit_exact_equals_candidate_path(r, G, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_exact_path_with_one_workgroup_per_unit(fp8):
+    # 256 units fill the GPU with their selectors, so the selection launch has no
+    # exact-path helpers and the exact path recomputes and selects each unit in one
+    # workgroup: the same index lists and outputs as the candidate path, bit for bit,
+    # over ragged lengths
+    seq = [3000 - 37 * b for b in range(32)]
+    k = 200
+    tag = f"exact path, one workgroup per unit, fp8={fp8}"
+    say(tag)
+    wl = workloads.gaussian(32, 8, 4, 128, 32, 3000, k, seed=141 + fp8, capacity=3000, device="cuda", seq_len=seq)
+    Kp = _cache(wl, fp8)
+    seq_len = torch.tensor(seq, dtype=torch.int32, device="cuda")
+    ref = _step(wl, Kp, wl.q, seq_len, k, "fused")
+    got = _step(wl, Kp, wl.q, seq_len, k, "fused", wait_us=-1)
+    _same(ref, got, tag)
+    _oracle(wl, got, wl.q, seq, k, fp8, tag, [(0, 0), (17, 5), (31, 7)])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_fused_edge_lengths(fp8):
     # capacity not a multiple of the 4096-row tile, an empty sequence, a sequence no
     # longer than the budget (every position taken), one exactly a tile long, one whose

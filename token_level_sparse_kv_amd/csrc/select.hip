@@ -725,9 +725,9 @@ __device__ void recompute_scores(const unsigned char* kproj_unit, const float* q
 }
 
 // grid = (B * H_kv, parts). scores != nullptr (parts = 1): dense selection over caller
-// scores (stride `stride`). Otherwise (parts = EXACT_WGS): take-all, the candidate path
-// (part 0 alone), or the exact path: every part recomputes its share of the unit's
-// scores and the last part to finish runs the dense selection.
+// scores (stride `stride`). Otherwise (1 <= parts <= EXACT_WGS, see select_parts):
+// take-all, the candidate path (part 0 alone), or the exact path: every part recomputes
+// its share of the unit's scores and the last part to finish runs the dense selection.
 template <int R, int KB>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ seq_len,
@@ -994,6 +994,24 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
   select_dense(row, n, kk, out, sh, true);
 }
 
+// Workgroups per unit of the selection launch: the selector, and exact-path helpers.
+// On the candidate path a helper only reads its unit's count words and exits: free
+// while the selectors (one per unit, each filling a CU's LDS) leave CUs idle, which run
+// the helpers in short rounds beside them, but extra rounds after the selectors once
+// these fill the GPU (512 units of the 128K decode step: 35 us with three helpers per
+// unit, 27 us with none). So a unit gets as many helpers as about three rounds on the
+// idle CUs hold: all EXACT_WGS - 1 up to half as many units as CUs, none from one unit
+// per CU on (the exact path then recomputes the unit in one workgroup).
+int select_parts(int64_t units) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return EXACT_WGS;                            // the error is reported after the launch
+  if (units >= cus) return 1;
+  const int64_t p = 1 + 3 * (cus - units) / units;
+  return (int)(p < EXACT_WGS ? p : EXACT_WGS);
+}
+
 }  // namespace
 
 hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scores, int64_t stride,
@@ -1007,7 +1025,7 @@ hipError_t launch_select(const sjsa_shape& s, const Layout& L, const float* scor
   uint32_t* epoch = reinterpret_cast<uint32_t*>(ws + L.off_epoch);
   uint32_t* arrive = reinterpret_cast<uint32_t*>(ws + L.off_arrive);
   uint32_t* parthist = reinterpret_cast<uint32_t*>(ws + L.off_parthist);
-  const dim3 grid((unsigned)L.units, scores ? 1u : (unsigned)EXACT_WGS), block(SEL_THREADS);
+  const dim3 grid((unsigned)L.units, scores ? 1u : (unsigned)select_parts(L.units)), block(SEL_THREADS);
   const unsigned char* kp = static_cast<const unsigned char*>(kproj);
   const bool fp8 = (s.flags & SJSA_FLAG_KPROJ_FP8) != 0;
 #define SJSA_SEL(RR, KB)                                                                                \

@@ -52,9 +52,10 @@ __host__ __device__ constexpr uint32_t cand_entry(uint32_t rel, int row) {
 constexpr int TLOW_SHIFT_POS = 8;
 constexpr int CAND_HEADROOM = 2;      // log2 of the relative keys' span over the sampled range
 constexpr int PART_STRIDE = HEAD_DIM + 2;   // acc[d], running max, running sum
-// Workgroups of the selection launch per unit: the first selects from the candidates;
-// when the unit takes the exact path (scores recomputed from the projected cache), all
-// of them recompute one part of its rows and the last to finish selects.
+// Most workgroups of the selection launch per unit (fewer when the units alone fill the
+// GPU): the first selects from the candidates; when the unit takes the exact path (scores
+// recomputed from the projected cache), all of them recompute one part of its rows and
+// the last to finish selects.
 constexpr int EXACT_WGS = 4;
 
 struct Layout {
