@@ -531,6 +531,66 @@ def recall_diagnostic(sj, workloads):
             "planted": len(planted), "kind": "diagnostic, not parity"}
 
 
+def batch_sweep(sj, workloads, batches, steps, warmup, peak_gbs):
+    """The 128K decode step (the headline's heads, rank and budget) at other batch sizes,
+    bf16 and FP8 scoring caches: steps back to back, and the mean time of each stage with
+    an event between stages. Shows how the stages' shares move with the batch."""
+    import numpy as np
+    import torch
+    from token_level_sparse_kv_amd.perfmodel import step_bytes
+    dev = torch.device("cuda:0")
+    rows = []
+    for B in batches:
+        for fp8 in (False, True):
+            say(f"sweep: batch {B}, {'FP8' if fp8 else 'bf16'} scoring cache")
+            wl = workloads.long_batched(device=dev, n_q_sets=8, batch=B)
+            Hkv, G, d, r, n, k = wl.n_kv_heads, wl.group, wl.head_dim, wl.rank, wl.capacity, wl.k
+            K, V, M, seq_len, q_sets = wl.K, wl.V, wl.M, wl.seq_len, wl.extra["q_sets"]
+            Kp = torch.empty(B, Hkv, n, r, dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+            for t0 in range(0, n, 8192):
+                pos = torch.full((B,), t0, dtype=torch.int32, device=dev)
+                sj.append_kv(K[:, :, t0:t0 + 8192].contiguous(), V[:, :, t0:t0 + 8192].contiguous(), M, pos, K, V,
+                             Kp)
+            k_new, v_new = workloads.new_token(wl, seed=99)
+            pos_new = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+            shape = sj.make_shape(B, Hkv, G, d, r, n, kproj_fp8=fp8)
+            ws = sj.alloc_workspace(shape, k, dev)
+            idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+            out = torch.empty(B, Hkv * G, d, dtype=torch.bfloat16, device=dev)
+
+            def step(i, ev=None):
+                q = q_sets[i % q_sets.shape[0]]
+                if ev is not None:
+                    ev[0].record()
+                sj.prep_scan(shape, q, M, Kp, seq_len, k, ws, k_new=k_new, v_new=v_new, pos=pos_new, K=K, V=V)
+                if ev is not None:
+                    ev[1].record()
+                sj.select(shape, Kp, seq_len, k, ws, idx=idx)
+                if ev is not None:
+                    ev[2].record()
+                sj.attend(q, K, V, idx, seq_len, out=out, workspace=ws, rank=r)
+                if ev is not None:
+                    ev[3].record()
+
+            us = back_to_back_us(step, steps, warmup)
+            evs = [[_ev() for _ in range(4)] for _ in range(steps)]
+            torch.cuda.synchronize()
+            for i in range(steps):
+                step(i, evs[i])
+            torch.cuda.synchronize()
+            stages = {nm: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1000.0, 2)
+                      for j, nm in enumerate(["append+prep+scan", "select", "attend+merge"])}
+            tb = step_bytes(B, Hkv, G, d, r, n, k, kb=1 if fp8 else 2)
+            rows.append({"batch": B, "kproj_dtype": "fp8_e4m3" if fp8 else "bf16", "us_per_step": round(us, 2),
+                         "algorithmic_bytes_per_step": tb["total"],
+                         "hbm_frac_of_peak": round(tb["total"] / (us * 1e-6) / 1e9 / peak_gbs, 4),
+                         "stage_us": stages})
+            say(json.dumps(rows[-1]))
+            del wl, K, V, M, Kp, ws, q_sets, idx, out
+            torch.cuda.empty_cache()
+    return rows
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -539,9 +599,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["headline", "fp8", "exact", "gated", "block", "calib"],
+    ap.add_argument("--only", choices=["headline", "fp8", "exact", "gated", "block", "calib", "sweep"],
                     help="run one measurement only, for profiling: the headline step's passes (one JSON line, no "
-                         "variants), or one variant (its JSON object alone)")
+                         "variants), or one variant (its JSON object alone); sweep: the step at batch 1 to 64 "
+                         "(not part of the default run)")
     ap.add_argument("--no-fp8-variant", action="store_true", help="skip the FP8 scoring-cache measurement")
     ap.add_argument("--no-gated-variant", action="store_true", help="skip the gated-logit step measurement")
     ap.add_argument("--no-block-variant", action="store_true", help="skip the block-sparse step measurements")
@@ -577,6 +638,10 @@ def main():
         print(json.dumps({"block_variant": block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS, False),
                           "block_int4_variant": block_variant(sj, workloads, steps, warmup, MI355X_HBM_PEAK_GBS,
                                                               True)}))
+        return
+    if only == "sweep":
+        print(json.dumps({"batch_sweep": batch_sweep(sj, workloads, [1, 2, 4, 8, 16, 32, 64], min(steps, 100),
+                                                     warmup, MI355X_HBM_PEAK_GBS)}))
         return
     if only == "calib":
         print(json.dumps({"calib_variant": calib_variant(sj, max(5, steps // 20), 2)}))
