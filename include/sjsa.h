@@ -174,7 +174,7 @@ int sjsa_decode_step_append(const sjsa_shape* shape, const void* k_new, const vo
  * A shape whose workspace (sjsa_decode_workspace_size(shape, k)) is larger is
  * rejected with SJSA_ERR_SCRATCH before anything is enqueued (with 131072 token
  * slots, r = 32 and k = 4096 that allows up to 58 (sequence, KV head) pairs; one
- * sequence of 32768 tokens with 8 KV heads and k = 2048 needs 3.0 MiB).
+ * sequence of 32768 tokens with 8 KV heads and k = 2048 needs 2.8 MiB).
  * Every call on one GPU uses that GPU's one array, which keeps the previous call's
  * contents (the step, like a fresh workspace, needs nothing cleared): calls that
  * overlap on one GPU (on different streams, or from host threads without ordering)

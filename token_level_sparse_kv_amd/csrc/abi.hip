@@ -12,7 +12,14 @@ namespace {
 
 constexpr size_t WS_ALIGN = 256;
 constexpr int ATT_TARGET_WGS = 1024;   // attention workgroups to aim for (4 per CU)
-constexpr int ATT_MIN_CHUNK = 64;
+constexpr int ATT_ALIGN = 64;          // attention splits hold a multiple of 64 entries
+// Shortest attention split of the token-level step: a split of 64 rows is one pass of
+// its slots, and costs more to start and to merge than it saves (at 8 units, 32 splits
+// of 128 rows took the step from 51.5 to 48.2 us; at 16 units from 64.1 to 59.7 us).
+constexpr int ATT_MIN_CHUNK = 128;
+// The gated step's splits: each repeats its unit's gated selection, and 64-entry splits
+// measured faster there (16.2 against 17.2 us graph-replayed at 8 units)
+constexpr int GATE_ATT_MIN_CHUNK = 64;
 constexpr int ATT_MAX_CHUNK = 1024;    // the attention kernel stages one chunk of indices in LDS
 constexpr int BLOCK_ATT_MIN_CHUNK = 128;
 
@@ -43,15 +50,17 @@ int status_of(hipError_t e) { return e == hipSuccess ? SJSA_OK : SJSA_ERR_HIP; }
 
 }  // namespace
 
-Layout make_layout(const sjsa_shape& s, int k) {
+namespace {
+
+Layout make_layout_split(const sjsa_shape& s, int k, int min_chunk) {
   Layout L;
   L.units = (int64_t)s.batch * s.n_kv_heads;
   L.score_stride = (int64_t)align_up((size_t)s.capacity, 64);
-  const int64_t max_split = (k + ATT_MIN_CHUNK - 1) / ATT_MIN_CHUNK;
+  const int64_t max_split = (k + min_chunk - 1) / min_chunk;
   int64_t want = (ATT_TARGET_WGS + L.units - 1) / L.units;
   want = want < 1 ? 1 : (want > max_split ? max_split : want);
   int64_t chunk = (k + want - 1) / want;
-  chunk = (int64_t)align_up((size_t)chunk, ATT_MIN_CHUNK);
+  chunk = (int64_t)align_up((size_t)chunk, ATT_ALIGN);
   if (chunk > ATT_MAX_CHUNK) chunk = ATT_MAX_CHUNK;
   L.chunk = (int)chunk;
   L.nsplit = (int)((k + chunk - 1) / chunk);
@@ -87,8 +96,12 @@ Layout make_layout(const sjsa_shape& s, int k) {
   return L;
 }
 
+}  // namespace
+
+Layout make_layout(const sjsa_shape& s, int k) { return make_layout_split(s, k, ATT_MIN_CHUNK); }
+
 Layout make_gated_layout(const sjsa_shape& s, int ktok) {
-  const Layout A = make_layout(s, ktok);      // attention split of a ktok-entry index list
+  const Layout A = make_layout_split(s, ktok, GATE_ATT_MIN_CHUNK);   // attention split of a ktok-entry index list
   Layout L;
   L.units = A.units;
   L.nsplit = A.nsplit;
