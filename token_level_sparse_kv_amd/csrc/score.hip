@@ -38,7 +38,13 @@ constexpr int STASH = TILE_ROWS_MAX / SCORE_WAVES;    // keys of one wave's rows
 // threshold (fewer candidates) but cost the prep about as much time as the later
 // stages save (measured with 4096 at the 128K batch-16 shape)
 constexpr int PREP_SAMPLES = 2048;
-constexpr int PREP_PASS = 1;         // sample batches per load pass (bounds the registers)
+// Sample batches per load pass: one for bf16 rows (two make the fused kernel spill at 8
+// waves per SIMD) and for FP8 rows of rank 64 (spills at 6 waves); two for FP8 rows of
+// rank 16 or 32, whose fused kernel runs at 7 waves with registers to spare, which at
+// small batch, where the prep's chain of sample loads decides the launch, took the step
+// from 45-47 to 43 us at batch 1 and from 51 to 49 us at batch 2.
+template <int R, int KB>
+constexpr int prep_pass() { return KB == 1 && R <= 32 ? 2 : 1; }
 constexpr int PREP_BINS = 4096;      // linear score bins of the threshold histogram
 constexpr uint32_t TAG_MULT = 0x9E3779B1u;
 constexpr uint32_t TAG_ADD = 0x7F4A7C15u;
@@ -200,6 +206,7 @@ __device__ __forceinline__ void prep_body(PrepShared& sh, int unit, const PrepAr
   constexpr int BATCHES = NS / SCORE_THREADS;         // 64-sample batches per wave (= samples per lane)
   constexpr int OUTS = R * 16 / SCORE_THREADS;        // q_hat outputs per thread
   constexpr int RW = R * KB / 4;                      // 32-bit words of a projected row
+  constexpr int PREP_PASS = prep_pass<R, KB>();
   static_assert(BATCHES % PREP_PASS == 0 && R * 16 % SCORE_THREADS == 0, "prep work divides evenly");
   const int b = unit / a.n_kv_heads;
   const int h = unit - b * a.n_kv_heads;
